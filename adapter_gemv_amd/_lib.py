@@ -1,0 +1,80 @@
+"""ctypes declarations of libsgmv's C ABI (include/sgmv.h).  Loading fails loudly when
+the library has not been built: there is no fallback implementation."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB_PATH
+
+F16 = 0
+BF16 = 1
+
+OK = 0
+ERR_NULL = 1
+ERR_SHAPE = 2
+ERR_ALIGNMENT = 3
+ERR_ADAPTER_ID = 4
+ERR_UNSUPPORTED = 5
+ERR_WORKSPACE = 6
+ERR_ALIAS = 7
+ERR_HIP = 8
+
+STATUS_NAMES = {
+    OK: "SGMV_OK", ERR_NULL: "SGMV_ERR_NULL", ERR_SHAPE: "SGMV_ERR_SHAPE",
+    ERR_ALIGNMENT: "SGMV_ERR_ALIGNMENT", ERR_ADAPTER_ID: "SGMV_ERR_ADAPTER_ID",
+    ERR_UNSUPPORTED: "SGMV_ERR_UNSUPPORTED", ERR_WORKSPACE: "SGMV_ERR_WORKSPACE",
+    ERR_ALIAS: "SGMV_ERR_ALIAS", ERR_HIP: "SGMV_ERR_HIP",
+}
+
+# every function the header declares, with its ctypes signature
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+SIGNATURES = {
+    "sgmv_abi_version": (ctypes.c_int, []),
+    "sgmv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "sgmv_build_segments": (ctypes.c_int, [_p, _i32, _i32, _p, _p, _p, _p, _p, _p]),
+    "sgmv_build_ptr_table": (ctypes.c_int, [_p, _i32, _p, _i32, _p]),
+    "sgmv_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "sgmv_shrink": (ctypes.c_int, [_p, _i32, _p, _p, _i64, _p, _p, _p, _i32, _i32, _i32, _i32,
+                                   _i32, _i32, _p, _sz]),
+    "sgmv_expand": (ctypes.c_int, [_p, _i32, _p, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
+                                   _i32, _i32, ctypes.c_float]),
+    "sgmv_lora_add": (ctypes.c_int, [_p, _i32, _p, _i64, _p, _i64, _p, _p, _p, _p, _i32, _i32,
+                                     _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _p, _sz]),
+}
+
+_LIB = None
+
+
+class SgmvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({status_string(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libsgmv.so (raises if it was not built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                               "`python -m adapter_gemv_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return lib().sgmv_status_string(int(status)).decode()
+
+
+def check(status: int, where: str) -> None:
+    if status != OK:
+        raise SgmvError(status, where)

@@ -1,0 +1,80 @@
+// Host side of libsgmv that needs no GPU: status strings and the segment-metadata
+// builder.  The builder is the "sort the batch by adapter" step of the Punica paper
+// summary (research.elamur.ai, "Interesting ideas", I2): a stable counting sort of
+// the caller's rows by adapter id, so that every adapter's rows form one contiguous
+// segment, followed by the per-segment adapter pointer table that lets one launch
+// gather each segment's own A and B.
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "../../include/sgmv.h"
+
+extern "C" int sgmv_abi_version(void) { return SGMV_ABI_VERSION; }
+
+extern "C" const char* sgmv_status_string(int status) {
+  switch (status) {
+    case SGMV_OK: return "ok";
+    case SGMV_ERR_NULL: return "a required pointer is NULL";
+    case SGMV_ERR_SHAPE: return "inconsistent size, stride or segment bound";
+    case SGMV_ERR_ALIGNMENT: return "pointer not 16-byte aligned or dimension not a multiple of 8";
+    case SGMV_ERR_ADAPTER_ID: return "adapter id out of range";
+    case SGMV_ERR_UNSUPPORTED: return "unsupported dtype or rank";
+    case SGMV_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case SGMV_ERR_ALIAS: return "output overlaps an input";
+    case SGMV_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int sgmv_build_segments(const int32_t* adapter_ids, int32_t n, int32_t n_adapters,
+                                   int32_t* perm, int32_t* seg_starts, int32_t* seg_adapter,
+                                   int32_t* n_segments, int32_t* min_seg_len,
+                                   int32_t* max_seg_len) {
+  if (n < 0 || n_adapters <= 0) return SGMV_ERR_SHAPE;
+  if (!seg_starts || !n_segments || (n > 0 && (!adapter_ids || !perm || !seg_adapter)))
+    return SGMV_ERR_NULL;
+  for (int32_t t = 0; t < n; ++t)
+    if (adapter_ids[t] < 0 || adapter_ids[t] >= n_adapters) return SGMV_ERR_ADAPTER_ID;
+
+  // counts per adapter, then an exclusive prefix sum gives each adapter's first slot
+  std::vector<int32_t> slot(static_cast<size_t>(n_adapters) + 1, 0);
+  for (int32_t t = 0; t < n; ++t) ++slot[adapter_ids[t] + 1];
+  int32_t S = 0, lo = n, hi = 0;
+  for (int32_t a = 0; a < n_adapters; ++a) {
+    const int32_t cnt = slot[a + 1];
+    if (cnt > 0) {
+      seg_starts[S] = slot[a];
+      seg_adapter[S] = a;
+      ++S;
+      if (cnt < lo) lo = cnt;
+      if (cnt > hi) hi = cnt;
+    }
+    slot[a + 1] += slot[a];
+  }
+  seg_starts[S] = n;
+  // scatter in caller order: rows of one adapter keep their relative order (stable)
+  for (int32_t t = 0; t < n; ++t) perm[slot[adapter_ids[t]]++] = t;
+
+  *n_segments = S;
+  if (min_seg_len) *min_seg_len = (n > 0) ? lo : 0;
+  if (max_seg_len) *max_seg_len = hi;
+  return SGMV_OK;
+}
+
+extern "C" int sgmv_build_ptr_table(const uint64_t* adapter_base, int32_t n_adapters,
+                                    const int32_t* seg_adapter, int32_t n_segments,
+                                    uint64_t* seg_ptrs) {
+  if (n_adapters <= 0 || n_segments < 0) return SGMV_ERR_SHAPE;
+  if (n_segments == 0) return SGMV_OK;
+  if (!adapter_base || !seg_adapter || !seg_ptrs) return SGMV_ERR_NULL;
+  for (int32_t s = 0; s < n_segments; ++s) {
+    const int32_t a = seg_adapter[s];
+    if (a < 0 || a >= n_adapters) return SGMV_ERR_ADAPTER_ID;
+    const uint64_t p = adapter_base[a];
+    if (p == 0) return SGMV_ERR_NULL;
+    if (p % 16 != 0) return SGMV_ERR_ALIGNMENT;
+    seg_ptrs[s] = p;
+  }
+  return SGMV_OK;
+}

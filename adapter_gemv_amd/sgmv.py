@@ -1,0 +1,278 @@
+"""Python binding of libsgmv (SGMV: segmented gather matrix-vector multiplication).
+
+Two layers, both argument marshalling only -- every step of the computation runs in
+libsgmv's HIP kernels or its C++ segment builder:
+
+* ``sgmv_*`` functions mirror the C ABI one to one (raw device addresses as ints,
+  host arrays as numpy);
+* ``Batch`` / ``lora_add`` / ``shrink`` / ``expand`` take torch tensors: PyTorch only
+  provides device memory and the current HIP stream.
+
+Layouts (see include/sgmv.h): x [n, h_in], y [n, h_out] row-major; an adapter pool
+``A_pool`` [P, r, h_in] (row j of A[a] is column j of the h_in x r matrix) and
+``B_pool`` [P, h_out, r] (row c is column c of the r x h_out matrix).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Sequence, Union
+
+import numpy as np
+
+from . import _lib
+from ._lib import BF16, F16, SgmvError, check  # noqa: F401
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+# --------------------------------------------------------------------------------------
+# C ABI mirror
+# --------------------------------------------------------------------------------------
+def sgmv_abi_version() -> int:
+    return int(_lib.lib().sgmv_abi_version())
+
+
+def sgmv_status_string(status: int) -> str:
+    return _lib.status_string(status)
+
+
+@dataclasses.dataclass
+class SegmentTable:
+    """Host segment metadata of one batch (see sgmv_build_segments)."""
+    perm: np.ndarray          # int32 [n]
+    seg_starts: np.ndarray    # int32 [S+1]
+    seg_adapter: np.ndarray   # int32 [S]
+    n_segments: int
+    min_seg_len: int
+    max_seg_len: int
+
+    @property
+    def n(self) -> int:
+        return int(self.perm.shape[0])
+
+
+def sgmv_build_segments(adapter_ids, n_adapters: int) -> SegmentTable:
+    ids = np.ascontiguousarray(np.asarray(adapter_ids), dtype=np.int32)
+    n = int(ids.shape[0])
+    perm = np.zeros(n, np.int32)
+    starts = np.zeros(n + 1, np.int32)
+    seg_ad = np.zeros(max(n, 1), np.int32)
+    S, lo, hi = (np.zeros(1, np.int32) for _ in range(3))
+    st = _lib.lib().sgmv_build_segments(_ptr(ids), n, int(n_adapters), _ptr(perm), _ptr(starts),
+                                        _ptr(seg_ad), _ptr(S), _ptr(lo), _ptr(hi))
+    check(st, "sgmv_build_segments")
+    s = int(S[0])
+    return SegmentTable(perm, starts[: s + 1].copy(), seg_ad[:s].copy(), s, int(lo[0]), int(hi[0]))
+
+
+def sgmv_build_ptr_table(adapter_base, seg_adapter) -> np.ndarray:
+    base = np.ascontiguousarray(np.asarray(adapter_base), dtype=np.uint64)
+    seg_ad = np.ascontiguousarray(np.asarray(seg_adapter), dtype=np.int32)
+    out = np.zeros(max(seg_ad.shape[0], 1), np.uint64)
+    st = _lib.lib().sgmv_build_ptr_table(_ptr(base), int(base.shape[0]), _ptr(seg_ad),
+                                         int(seg_ad.shape[0]), _ptr(out))
+    check(st, "sgmv_build_ptr_table")
+    return out[: seg_ad.shape[0]]
+
+
+def sgmv_workspace_bytes(n: int, h_in: int, r: int) -> int:
+    return int(_lib.lib().sgmv_workspace_bytes(int(n), int(h_in), int(r)))
+
+
+def sgmv_shrink(stream, dtype, v, x, ld_x, A_ptrs, seg_starts, perm, n, n_segments,
+                min_seg_len, max_seg_len, h_in, r, workspace, workspace_bytes) -> int:
+    return _lib.lib().sgmv_shrink(stream, dtype, v, x, ld_x, A_ptrs, seg_starts, perm, n,
+                                  n_segments, min_seg_len, max_seg_len, h_in, r, workspace,
+                                  workspace_bytes)
+
+
+def sgmv_expand(stream, dtype, y, ld_y, v, B_ptrs, seg_starts, perm, n, n_segments,
+                min_seg_len, max_seg_len, r, h_out, scale) -> int:
+    return _lib.lib().sgmv_expand(stream, dtype, y, ld_y, v, B_ptrs, seg_starts, perm, n,
+                                  n_segments, min_seg_len, max_seg_len, r, h_out, float(scale))
+
+
+def sgmv_lora_add(stream, dtype, y, ld_y, x, ld_x, A_ptrs, B_ptrs, seg_starts, perm, n,
+                  n_segments, min_seg_len, max_seg_len, h_in, h_out, r, scale, workspace,
+                  workspace_bytes) -> int:
+    return _lib.lib().sgmv_lora_add(stream, dtype, y, ld_y, x, ld_x, A_ptrs, B_ptrs, seg_starts,
+                                    perm, n, n_segments, min_seg_len, max_seg_len, h_in, h_out, r,
+                                    float(scale), workspace, workspace_bytes)
+
+
+# --------------------------------------------------------------------------------------
+# torch layer
+# --------------------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float16 or bfloat16)")
+
+
+def as_tensor(arr: np.ndarray, dtype: str, device=None):
+    """Storage array of the input generator ("f16": float16, "bf16": uint16 bits) as a
+    torch tensor of the matching dtype (no value conversion)."""
+    torch = _torch()
+    a = np.ascontiguousarray(arr)
+    if dtype == "f16":
+        t = torch.from_numpy(a.view(np.float16))
+    elif dtype == "bf16":
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    else:
+        raise ValueError(dtype)
+    return t.to(device) if device is not None else t
+
+
+def adapter_bases(pool) -> np.ndarray:
+    """Device address of each adapter in a pool tensor [P, ...] or a list of tensors."""
+    if isinstance(pool, (list, tuple)):
+        return np.array([int(t.data_ptr()) for t in pool], dtype=np.uint64)
+    stride = pool.stride(0) * pool.element_size()
+    return np.uint64(pool.data_ptr()) + np.arange(pool.shape[0], dtype=np.uint64) * np.uint64(stride)
+
+
+def _stream_handle(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+@dataclasses.dataclass
+class Batch:
+    """Segment metadata of one batch, resident on the device (one H2D copy).
+
+    ``table`` is the host SegmentTable; ``dev`` holds [A_ptrs | B_ptrs | seg_starts |
+    perm] in one device buffer, and the ``*_addr`` fields are device addresses into it.
+    """
+    table: SegmentTable
+    n_adapters: int
+    rank: int
+    dev: object
+    A_ptrs_addr: int
+    B_ptrs_addr: int
+    seg_starts_addr: int
+    perm_addr: int
+
+    @property
+    def n(self) -> int:
+        return self.table.n
+
+    @classmethod
+    def build(cls, adapter_ids, A_pool, B_pool, device=None, identity_perm: bool = False):
+        """Sort ``adapter_ids`` (host) into segments and upload the tables.
+
+        ``A_pool`` / ``B_pool`` are pool tensors [P, ...] or lists of per-adapter tensors
+        on the device.  ``identity_perm`` passes perm = NULL (rows already sorted)."""
+        torch = _torch()
+        if isinstance(A_pool, (list, tuple)):
+            n_adapters, rank = len(A_pool), int(A_pool[0].shape[0])
+        else:
+            n_adapters, rank = int(A_pool.shape[0]), int(A_pool.shape[1])
+        tab = sgmv_build_segments(adapter_ids, n_adapters)
+        if identity_perm and not np.array_equal(tab.perm, np.arange(tab.n, dtype=np.int32)):
+            raise ValueError("identity_perm requires adapter_ids to be sorted")
+        a_ptr = sgmv_build_ptr_table(adapter_bases(A_pool), tab.seg_adapter)
+        b_ptr = sgmv_build_ptr_table(adapter_bases(B_pool), tab.seg_adapter)
+        buf = cls.pack(tab, a_ptr, b_ptr)
+        if device is None:
+            device = A_pool[0].device if isinstance(A_pool, (list, tuple)) else A_pool.device
+        dev = torch.from_numpy(buf).to(device)
+        base = int(dev.data_ptr())
+        S, n = tab.n_segments, tab.n
+        off_b = 8 * S
+        off_s = 16 * S
+        off_p = off_s + 4 * (S + 1)
+        return cls(tab, n_adapters, rank, dev, base, base + off_b, base + off_s,
+                   0 if identity_perm else base + off_p)
+
+    @staticmethod
+    def pack(tab: SegmentTable, a_ptr: np.ndarray, b_ptr: np.ndarray) -> np.ndarray:
+        S, n = tab.n_segments, tab.n
+        nbytes = 16 * S + 4 * (S + 1) + 4 * n
+        buf = np.zeros(max(nbytes, 16), np.uint8)
+        buf[: 8 * S] = a_ptr.view(np.uint8)
+        buf[8 * S: 16 * S] = b_ptr.view(np.uint8)
+        buf[16 * S: 16 * S + 4 * (S + 1)] = tab.seg_starts.view(np.uint8)
+        buf[16 * S + 4 * (S + 1): nbytes] = tab.perm.view(np.uint8)
+        return buf
+
+
+def make_workspace(n: int, h_in: int, r: int, device):
+    """Zero-filled, 256-byte aligned workspace for shrink / lora_add."""
+    torch = _torch()
+    nbytes = sgmv_workspace_bytes(n, h_in, r)
+    if nbytes == 0:
+        raise ValueError("invalid sizes for sgmv_workspace_bytes")
+    ws = torch.zeros(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-int(ws.data_ptr())) % 256
+    return ws[off: off + nbytes]
+
+
+def _check_rows(t, n: int, name: str):
+    if t.dim() != 2 or t.shape[0] != n or t.stride(1) != 1:
+        raise ValueError(f"{name} must be [n, h] with unit column stride")
+
+
+def lora_add(y, x, batch: Batch, scale: float, workspace=None, stream=None):
+    """y[t] += scale * (x[t] @ A[a_t]) @ B[a_t] in place (fused shrink + expand)."""
+    n = batch.n
+    _check_rows(x, n, "x")
+    _check_rows(y, n, "y")
+    if x.dtype != y.dtype:
+        raise TypeError("x and y must share a dtype")
+    r = _infer_rank(batch)
+    if workspace is None:
+        workspace = make_workspace(n, x.shape[1], r, x.device)
+    t = batch.table
+    st = sgmv_lora_add(_stream_handle(stream), dtype_code(y), y.data_ptr(), y.stride(0),
+                       x.data_ptr(), x.stride(0), batch.A_ptrs_addr, batch.B_ptrs_addr,
+                       batch.seg_starts_addr, batch.perm_addr or None, n, t.n_segments,
+                       t.min_seg_len, t.max_seg_len, x.shape[1], y.shape[1], r, scale,
+                       workspace.data_ptr(), workspace.numel())
+    check(st, "sgmv_lora_add")
+    return y
+
+
+def shrink(x, batch: Batch, r: Optional[int] = None, workspace=None, stream=None):
+    """v[i] = x[perm[i]] @ A[segment of i] as float32 [n, r] in sorted order."""
+    torch = _torch()
+    n = batch.n
+    _check_rows(x, n, "x")
+    r = r or _infer_rank(batch)
+    v = torch.empty((n, r), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = make_workspace(n, x.shape[1], r, x.device)
+    t = batch.table
+    st = sgmv_shrink(_stream_handle(stream), dtype_code(x), v.data_ptr(), x.data_ptr(),
+                     x.stride(0), batch.A_ptrs_addr, batch.seg_starts_addr,
+                     batch.perm_addr or None, n, t.n_segments, t.min_seg_len, t.max_seg_len,
+                     x.shape[1], r, workspace.data_ptr(), workspace.numel())
+    check(st, "sgmv_shrink")
+    return v
+
+
+def expand(y, v, batch: Batch, scale: float, stream=None):
+    """y[perm[i]] += scale * v[i] @ B[segment of i] in place."""
+    n = batch.n
+    _check_rows(y, n, "y")
+    t = batch.table
+    st = sgmv_expand(_stream_handle(stream), dtype_code(y), y.data_ptr(), y.stride(0),
+                     v.data_ptr(), batch.B_ptrs_addr, batch.seg_starts_addr,
+                     batch.perm_addr or None, n, t.n_segments, t.min_seg_len, t.max_seg_len,
+                     v.shape[1], y.shape[1], scale)
+    check(st, "sgmv_expand")
+    return y
+
+
+def _infer_rank(batch: Batch) -> int:
+    return int(batch.rank)

@@ -1,0 +1,162 @@
+/*
+ * libsgmv -- Segmented Gather Matrix-Vector multiplication (SGMV) on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * What it computes.  Punica serves many LoRA fine-tunes of one base model in one
+ * batch.  The Punica project overview ("How It Works") describes a LoRA model as the
+ * pretrained weight W plus two smaller matrices A and B, applied through SGMV; the
+ * Punica paper summary on research.elamur.ai ("Summary", and idea I2 under
+ * "Interesting ideas") says the backbone runs as one ordinary GEMM over the whole
+ * batch while the per-adapter low-rank additions are computed together, with the
+ * batch sorted so that requests for the same adapter are contiguous.  For every
+ * token (row) t of the batch, with a = adapter_ids[t]:
+ *
+ *     v[t, :] = x[t, :] @ A[a]                       (shrink, h_in -> r)
+ *     y[t, :] = y[t, :] + scale * v[t, :] @ B[a]     (expand, r -> h_out)
+ *
+ * y already holds the backbone output and is updated in place.  The backbone GEMM
+ * is not part of this library.
+ *
+ * Conventions shared by every call:
+ *   - Element type: x, y, A and B are all SGMV_F16 (IEEE binary16) or all
+ *     SGMV_BF16 (bfloat16).  v and every intermediate are float32; products and
+ *     sums are formed in float32 and y is rounded once, to nearest even.
+ *   - x is row-major [n, h_in] with row stride ld_x elements; y is row-major
+ *     [n, h_out] with row stride ld_y elements.
+ *   - A[a] (h_in x r) is stored as a row-major [r, h_in] array: row j holds column
+ *     j of A.  B[a] (r x h_out) is stored as a row-major [h_out, r] array: row c
+ *     holds column c of B.  (This is the nn.Linear weight layout of a LoRA pair;
+ *     the contracted dimension is contiguous in both.)
+ *   - Segments: the batch is viewed in *sorted order*.  Sorted position i is
+ *     caller row perm[i] (perm == NULL means the identity: the caller's rows are
+ *     already sorted).  Segment s covers sorted positions seg_starts[s] ..
+ *     seg_starts[s+1]-1 and uses adapter s of the per-segment pointer tables
+ *     A_ptrs[s] / B_ptrs[s].  sgmv_build_segments / sgmv_build_ptr_table produce
+ *     these tables from per-token adapter ids.
+ *   - min_seg_len / max_seg_len are host-side bounds on the number of rows of any
+ *     segment (sgmv_build_segments returns the exact values; 0 and n are always
+ *     valid).  They only choose which kernels are launched: segments shorter than
+ *     16 rows use wavefront-reduction (GEMV) kernels, longer ones MFMA tiles.
+ *
+ * Memory ownership: every pointer passed to a device call is device memory owned by
+ * the caller, except where a comment says "host".  The library allocates nothing,
+ * keeps no per-call state and never synchronises: device calls are enqueued on
+ * `stream` and return.  Calls that share a workspace must be ordered (same stream).
+ *
+ * Errors: every argument check is done on the host before any HIP call, so a
+ * rejected call has no effect.  The contents of device tables (seg_starts, perm,
+ * A_ptrs, B_ptrs) are preconditions that are not checked.  n == 0 returns SGMV_OK
+ * without launching anything.
+ */
+#ifndef SGMV_H_
+#define SGMV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SGMV_ABI_VERSION 1
+
+/* element types of x, y, A, B */
+#define SGMV_F16 0
+#define SGMV_BF16 1
+
+/* status codes */
+#define SGMV_OK 0
+#define SGMV_ERR_NULL 1        /* a required pointer is NULL */
+#define SGMV_ERR_SHAPE 2       /* a size, stride or segment bound is inconsistent */
+#define SGMV_ERR_ALIGNMENT 3   /* x, y, v or an adapter base is not 16-byte aligned, or h % 8 != 0 */
+#define SGMV_ERR_ADAPTER_ID 4  /* an adapter id lies outside [0, n_adapters) */
+#define SGMV_ERR_UNSUPPORTED 5 /* unknown dtype, or r not in {16, 32, 64} */
+#define SGMV_ERR_WORKSPACE 6   /* workspace missing, too small or not 256-byte aligned */
+#define SGMV_ERR_ALIAS 7       /* an output overlaps an input */
+#define SGMV_ERR_HIP 8         /* a HIP runtime call or kernel launch failed (e.g. no device) */
+
+/* Version of this interface (SGMV_ABI_VERSION of the library that was built). */
+int sgmv_abi_version(void);
+
+/* Static English text for a status code; never NULL. */
+const char* sgmv_status_string(int status);
+
+/*
+ * Segment metadata (host).  Stable counting sort of the caller's rows by adapter id
+ * (the paper summary's idea I2: sort the batch by adapter so that each adapter's
+ * requests form one dense segment).
+ *   adapter_ids  host int32[n]: adapter of caller row t, in [0, n_adapters)
+ *   perm         host int32[n] out: caller row at sorted position i; rows of one
+ *                adapter keep their caller order
+ *   seg_starts   host int32[n+1] out: first n_segments+1 entries written;
+ *                seg_starts[0] = 0, seg_starts[n_segments] = n
+ *   seg_adapter  host int32[n] out: adapter of segment s; segments come in
+ *                ascending adapter id and adapters without rows have no segment
+ *   n_segments   host out: number of distinct adapter ids present
+ *   min_seg_len, max_seg_len  host out (each may be NULL): shortest and longest
+ *                segment (0 when n == 0)
+ * Returns SGMV_ERR_ADAPTER_ID (outputs unspecified) for an id out of range,
+ * SGMV_ERR_NULL / SGMV_ERR_SHAPE for bad arguments.  n == 0 gives n_segments = 0.
+ */
+int sgmv_build_segments(const int32_t* adapter_ids, int32_t n, int32_t n_adapters,
+                        int32_t* perm, int32_t* seg_starts, int32_t* seg_adapter,
+                        int32_t* n_segments, int32_t* min_seg_len, int32_t* max_seg_len);
+
+/*
+ * Per-segment pointer table (host): seg_ptrs[s] = adapter_base[seg_adapter[s]].
+ *   adapter_base  host uint64[n_adapters]: device address of each adapter's A (or B)
+ *   seg_ptrs      host uint64[n_segments] out
+ * Returns SGMV_ERR_ADAPTER_ID for an entry of seg_adapter out of range and
+ * SGMV_ERR_ALIGNMENT if a referenced base is not 16-byte aligned.
+ */
+int sgmv_build_ptr_table(const uint64_t* adapter_base, int32_t n_adapters,
+                         const int32_t* seg_adapter, int32_t n_segments, uint64_t* seg_ptrs);
+
+/*
+ * Bytes of device workspace that sgmv_shrink and sgmv_lora_add need for a batch of
+ * n rows (fp32 split-K partial sums plus a few counters).  The workspace must be
+ * 256-byte aligned and zero-filled once before its first use; every call leaves it
+ * ready for the next one.  Returns 0 for invalid sizes.
+ */
+size_t sgmv_workspace_bytes(int32_t n, int32_t h_in, int32_t r);
+
+/*
+ * Shrink only: v[i, :] = x[perm[i], :] @ A[segment of i]   (float32, sorted order).
+ *   v  device float32 [n, r] out, row i = sorted position i, overwritten
+ * Other arguments as described above.  v must not overlap x.
+ */
+int sgmv_shrink(hipStream_t stream, int32_t dtype, float* v,
+                const void* x, int64_t ld_x, const void* const* A_ptrs,
+                const int32_t* seg_starts, const int32_t* perm,
+                int32_t n, int32_t n_segments, int32_t min_seg_len, int32_t max_seg_len,
+                int32_t h_in, int32_t r, void* workspace, size_t workspace_bytes);
+
+/*
+ * Expand only: y[perm[i], :] += scale * v[i, :] @ B[segment of i], rounded once.
+ *   v  device float32 [n, r], row i = sorted position i (as written by sgmv_shrink)
+ * y must not overlap v.
+ */
+int sgmv_expand(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y, const float* v,
+                const void* const* B_ptrs, const int32_t* seg_starts, const int32_t* perm,
+                int32_t n, int32_t n_segments, int32_t min_seg_len, int32_t max_seg_len,
+                int32_t r, int32_t h_out, float scale);
+
+/*
+ * Fused LoRA add-on: shrink then expand, y[t] += scale * (x[t] @ A[a_t]) @ B[a_t]
+ * for every row, with v kept in float32 in the workspace.  x and y must not overlap.
+ */
+int sgmv_lora_add(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
+                  const void* x, int64_t ld_x,
+                  const void* const* A_ptrs, const void* const* B_ptrs,
+                  const int32_t* seg_starts, const int32_t* perm,
+                  int32_t n, int32_t n_segments, int32_t min_seg_len, int32_t max_seg_len,
+                  int32_t h_in, int32_t h_out, int32_t r, float scale,
+                  void* workspace, size_t workspace_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGMV_H_ */

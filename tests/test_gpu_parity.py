@@ -1,0 +1,292 @@
+"""GPU parity of libsgmv against the fp64 oracle, through the C ABI.
+
+Tolerance (fp16/bf16 I/O, float32 accumulation): |y_gpu - y_ref| <= 1e-2 + 1e-2 |y_ref|
+elementwise, y_ref being the unrounded fp64 oracle.  Segment gathering and exact-grid
+inputs are checked bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 1e-2
+RTOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _upload(p, **kw):
+    from adapter_gemv_amd.device_problem import DeviceProblem
+    return DeviceProblem.upload(p, **kw)
+
+
+def _y_f64(y, dtype):
+    from adapter_gemv_amd.device_problem import to_numpy_storage
+    return oracle.decode(to_numpy_storage(y, dtype), dtype)
+
+
+def _assert_close(got, ref, what):
+    err = np.abs(got - ref)
+    tol = ATOL + RTOL * np.abs(ref)
+    bad = err > tol
+    _say(f"{what}: max|err| {err.max():.3e}, worst err/tol {np.max(err / tol):.3f}")
+    assert not bad.any(), f"{what}: {int(bad.sum())} of {bad.size} outside tolerance"
+
+
+def _run_lora(p, **kw):
+    import torch
+    dp = _upload(p, **kw)
+    y = dp.lora_add()
+    torch.cuda.synchronize()
+    return dp, y
+
+
+# --------------------------------------------------------------------------------------
+# the workloads at full size
+# --------------------------------------------------------------------------------------
+SMALL = ["tiny", "decode7b", "sweep_a", "sweep_b", "sweep_c",
+         "prefill13b_qo", "prefill13b_gateup", "prefill13b_down"]
+FACT = dict(synth.all_workloads())
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_workload_full_compare(torch_cuda, name):
+    _say(f"[parity] {name}")
+    p = FACT[name]()
+    _, y = _run_lora(p)
+    _assert_close(_y_f64(y, p.dtype), oracle.lora_add_problem(p), name)
+
+
+MIXED = [f"mixed70b_r{r}_{proj}" for r in (16, 64) for proj in synth.MIXED70B_SHAPES]
+
+
+@pytest.mark.parametrize("name", MIXED)
+def test_mixed70b_sampled_rows(torch_cuda, name):
+    """Full-size mixed batch in the benchmark's launch configuration; the oracle is
+    evaluated on every decode row and 96 sampled prefill rows (rows are independent)."""
+    _say(f"[parity] {name}")
+    p = FACT[name]()
+    _, y = _run_lora(p)
+    rng = np.random.default_rng(77)
+    rows = np.concatenate([np.arange(64), 64 + rng.choice(p.n - 64, 96, replace=False)])
+    rows.sort()
+    ref = oracle.lora_add(p.y[rows], p.x[rows], p.ids[rows], p.A, p.B, p.scale, p.dtype)
+    got = _y_f64(y[torch_cuda.as_tensor(rows, device=y.device)], p.dtype)
+    _assert_close(got, ref, name)
+
+
+# --------------------------------------------------------------------------------------
+# bit-exact: power-of-two grids and gather probes
+# --------------------------------------------------------------------------------------
+EXACT_CASES = [
+    # name, n, h_in, h_out, r, P, ids-kind
+    ("decode", 40, 4096, 4096, 16, 40, "perm"),
+    ("short_mixed", 61, 1032, 520, 16, 9, "uniform"),
+    ("long_only", 96, 2048, 1024, 16, 3, "blocks"),
+    ("mixed_long_short", 150, 520, 1048, 32, 6, "mixed"),
+    ("r64_mixed", 90, 1024, 776, 64, 5, "mixed"),
+    ("r64_decode", 12, 8192, 1024, 64, 12, "perm"),
+    ("deep_k", 40, 28672, 264, 16, 3, "mixed"),
+]
+
+
+def _ids(kind, n, P, rng):
+    if kind == "perm":
+        return rng.permutation(n).astype(np.int32) % P
+    if kind == "uniform":
+        return rng.integers(0, P, n).astype(np.int32)
+    if kind == "blocks":
+        return np.repeat(rng.permutation(P), -(-n // P))[:n].astype(np.int32)
+    # a few long segments plus scattered short ones
+    ids = rng.integers(2, P, n).astype(np.int32)
+    ids[rng.choice(n, n // 3, replace=False)] = 0
+    ids[rng.choice(n, n // 4, replace=False)] = 1
+    return ids
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("case", EXACT_CASES, ids=[c[0] for c in EXACT_CASES])
+def test_exact_grid_bit_exact(torch_cuda, case, dtype):
+    name, n, h_in, h_out, r, P, kind = case
+    _say(f"[exact] {name} {dtype}")
+    rng = np.random.default_rng(sum(map(ord, name)))
+    p = synth.exact_problem((31, len(name)), n=n, h_in=h_in, h_out=h_out, r=r, n_adapters=P,
+                            dtype=dtype, ids=_ids(kind, n, P, rng))
+    _, y = _run_lora(p)
+    from adapter_gemv_amd.device_problem import to_numpy_storage
+    got = to_numpy_storage(y, dtype).view(np.uint16)
+    want = oracle.round_io(oracle.lora_add_problem(p), dtype).view(np.uint16)
+    mism = got != want
+    assert not mism.any(), f"{int(mism.sum())} elements differ"
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("r,kind,n", [(16, "perm", 24), (16, "mixed", 120), (64, "mixed", 100),
+                                      (32, "uniform", 57)])
+def test_gather_probe_bit_exact(torch_cuda, dtype, r, kind, n):
+    _say(f"[gather] r={r} {kind} n={n} {dtype}")
+    P = 6
+    rng = np.random.default_rng(r + n)
+    p = synth.gather_probe((41, r, n), n=n, h_in=512, h_out=384, r=r, n_adapters=P, dtype=dtype,
+                           ids=_ids(kind, n, P, rng))
+    _, y = _run_lora(p)
+    from adapter_gemv_amd.device_problem import to_numpy_storage
+    got = to_numpy_storage(y, dtype).view(np.uint16)
+    want = oracle.round_io(oracle.lora_add_problem(p), dtype).view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+# --------------------------------------------------------------------------------------
+# ragged sizes, strides, edge cases
+# --------------------------------------------------------------------------------------
+RAGGED = [
+    # n, h_in, h_out, r, P, ids-kind, ld_pad, identity_perm
+    (1, 8, 8, 16, 1, "uniform", 0, False),
+    (37, 200, 136, 16, 5, "uniform", 8, False),
+    (15, 4104, 2056, 16, 1, "blocks", 0, True),     # longest short segment
+    (16, 4104, 2056, 16, 1, "blocks", 0, True),     # shortest long segment
+    (17, 1000, 3000, 32, 2, "blocks", 16, False),
+    (333, 776, 1304, 64, 7, "mixed", 0, False),
+    (257, 5128, 520, 16, 3, "mixed", 24, False),
+    (64, 24, 4104, 64, 64, "perm", 0, False),
+    (2048, 264, 264, 16, 1, "blocks", 0, True),     # one very long segment
+]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("case", RAGGED, ids=[f"n{c[0]}_{c[1]}x{c[2]}_r{c[3]}" for c in RAGGED])
+def test_ragged_and_strided(torch_cuda, case, dtype):
+    n, h_in, h_out, r, P, kind, ld_pad, ident = case
+    _say(f"[ragged] {case} {dtype}")
+    rng = np.random.default_rng(n * 7 + h_in)
+    ids = _ids(kind, n, P, rng)
+    if ident:
+        ids = np.sort(ids)
+    p = synth.random_problem((51, n, h_in, h_out, r), n=n, h_in=h_in, h_out=h_out, r=r,
+                             n_adapters=P, dtype=dtype, ids=ids, scale=0.75)
+    _, y = _run_lora(p, ld_pad=ld_pad, identity_perm=ident)
+    _assert_close(_y_f64(y, dtype), oracle.lora_add_problem(p), f"ragged {case} {dtype}")
+
+
+# --------------------------------------------------------------------------------------
+# shrink and expand on their own
+# --------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("r,kind,n", [(16, "mixed", 200), (64, "mixed", 150), (32, "perm", 32)])
+def test_shrink_and_expand(torch_cuda, dtype, r, kind, n):
+    torch = torch_cuda
+    _say(f"[shrink/expand] r={r} {kind} n={n} {dtype}")
+    P = 8 if kind != "perm" else n
+    rng = np.random.default_rng(3 * n + r)
+    p = synth.random_problem((61, r, n), n=n, h_in=1544, h_out=1032, r=r, n_adapters=P,
+                             dtype=dtype, ids=_ids(kind, n, P, rng))
+    dp = _upload(p)
+    v = dp.shrink()
+    torch.cuda.synchronize()
+    perm = dp.batch.table.perm
+    v_ref = oracle.shrink(p.x, p.ids, p.A, dtype)[perm]          # sorted order
+    _assert_close(v.double().cpu().numpy(), v_ref, "shrink v")
+    # expand from the oracle's v (rounded to float32), in sorted order
+    v_in = torch.as_tensor(v_ref.astype(np.float32), device=dp.x.device)
+    y = dp.expand(v_in)
+    torch.cuda.synchronize()
+    y_ref = oracle.expand(p.y[perm], v_ref.astype(np.float32).astype(np.float64), p.ids[perm],
+                          p.B, p.scale, dtype)
+    _assert_close(_y_f64(y, dtype)[perm], y_ref, "expand y")
+
+
+# --------------------------------------------------------------------------------------
+# invariants on the GPU results
+# --------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_zero_B_and_zero_scale_leave_y_unchanged(torch_cuda, dtype):
+    _say(f"[invariant] zero B / zero scale {dtype}")
+    rng = np.random.default_rng(5)
+    p = synth.random_problem((71,), n=120, h_in=1032, h_out=776, r=16, n_adapters=5,
+                             dtype=dtype, ids=_ids("mixed", 120, 5, rng))
+    y0 = oracle.decode(p.y, dtype)
+    dp = _upload(p)
+    y = dp.lora_add(scale=0.0)
+    torch_cuda.cuda.synchronize()
+    assert np.array_equal(_y_f64(y, dtype), y0)
+    p.B = np.zeros_like(p.B)
+    dp = _upload(p)
+    y = dp.lora_add()
+    torch_cuda.cuda.synchronize()
+    assert np.array_equal(_y_f64(y, dtype), y0)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_shrink_linear_in_x_exactly(torch_cuda, dtype):
+    _say(f"[invariant] v(2x) == 2 v(x) {dtype}")
+    rng = np.random.default_rng(6)
+    p = synth.random_problem((72,), n=140, h_in=2056, h_out=264, r=16, n_adapters=4,
+                             dtype=dtype, ids=_ids("mixed", 140, 4, rng))
+    v1 = _upload(p).shrink()
+    p.x = synth.quantize(oracle.decode(p.x, dtype) * 2, dtype)
+    v2 = _upload(p).shrink()
+    torch_cuda.cuda.synchronize()
+    assert torch_cuda.equal(v2, 2 * v1)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_row_order_independence(torch_cuda, dtype):
+    """Permuting the caller's rows permutes the output (bit for bit: each row's sums do
+    not depend on its position)."""
+    _say(f"[invariant] row order {dtype}")
+    rng = np.random.default_rng(8)
+    p = synth.random_problem((73,), n=180, h_in=1032, h_out=520, r=16, n_adapters=6,
+                             dtype=dtype, ids=_ids("mixed", 180, 6, rng))
+    _, y1 = _run_lora(p)
+    q = rng.permutation(p.n)
+    p2 = synth.Problem("perm", dtype, p.ids[q], p.x[q], p.y[q], p.A, p.B, p.scale)
+    _, y2 = _run_lora(p2)
+    assert torch_cuda.equal(y2, y1[torch_cuda.as_tensor(q, device=y1.device)])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_identical_adapter_equals_any_split(torch_cuda, dtype):
+    _say(f"[invariant] split adapter {dtype}")
+    n = 64
+    p = synth.random_problem((74,), n=n, h_in=2056, h_out=1032, r=16, n_adapters=1,
+                             dtype=dtype, ids=np.zeros(n, np.int32))
+    _, y1 = _run_lora(p)
+    rng = np.random.default_rng(9)
+    ids = rng.integers(0, 5, n).astype(np.int32)
+    p2 = synth.Problem("split", dtype, ids, p.x, p.y, np.repeat(p.A, 5, 0), np.repeat(p.B, 5, 0),
+                       p.scale)
+    _, y2 = _run_lora(p2)
+    a, b = _y_f64(y1, dtype), _y_f64(y2, dtype)
+    _assert_close(b, a, "split vs identical")
+    _assert_close(a, oracle.lora_add_problem(p), "identical vs oracle")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_deterministic_and_workspace_reuse(torch_cuda, dtype):
+    torch = torch_cuda
+    _say(f"[determinism] {dtype}")
+    from adapter_gemv_amd import sgmv
+    rng = np.random.default_rng(10)
+    p = synth.random_problem((75,), n=300, h_in=4096, h_out=2048, r=16, n_adapters=9,
+                             dtype=dtype, ids=_ids("mixed", 300, 9, rng))
+    dp = _upload(p)
+    ws = sgmv.make_workspace(p.n, p.h_in, 16, dp.x.device)
+    outs = [dp.lora_add(workspace=ws) for _ in range(3)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])

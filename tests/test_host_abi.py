@@ -1,0 +1,188 @@
+"""CPU tests of libsgmv's host side: the library loads and exports every function that
+include/sgmv.h declares, the C++ segment builder equals the oracle's stable sort bit for
+bit, and argument validation rejects bad calls before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from adapter_gemv_amd import _lib, sgmv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgmv.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sgmv_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_abi():
+    assert header_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in header_functions():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_abi_version_and_status_strings():
+    assert sgmv.sgmv_abi_version() == 1
+    for code in range(9):
+        assert sgmv.sgmv_status_string(code) and sgmv.sgmv_status_string(code) != "unknown status"
+    assert sgmv.sgmv_status_string(99) == "unknown status"
+
+
+# --------------------------------------------------------------------------------------
+# segment builder vs the oracle
+# --------------------------------------------------------------------------------------
+def _ids_cases():
+    rng = np.random.default_rng(42)
+    cases = [
+        ("empty", np.zeros(0, np.int32), 3),
+        ("one", np.array([2], np.int32), 3),
+        ("same", np.full(33, 5, np.int32), 8),
+        ("distinct", rng.permutation(32).astype(np.int32), 32),
+        ("sorted", np.repeat(np.arange(4), 512).astype(np.int32), 4),
+        ("empty_adapters", rng.choice([0, 7, 63], 100).astype(np.int32), 64),
+    ]
+    for k in range(20):
+        P = int(rng.integers(1, 70))
+        n = int(rng.integers(1, 3000))
+        cases.append((f"random{k}", rng.integers(0, P, n).astype(np.int32), P))
+    return cases
+
+
+@pytest.mark.parametrize("name,ids,P", _ids_cases(), ids=[c[0] for c in _ids_cases()])
+def test_build_segments_matches_oracle(name, ids, P):
+    tab = sgmv.sgmv_build_segments(ids, P)
+    perm, starts, seg_ad = oracle.segments(ids, P)
+    assert np.array_equal(tab.perm, perm)
+    assert np.array_equal(tab.seg_starts, starts)
+    assert np.array_equal(tab.seg_adapter, seg_ad)
+    assert tab.n_segments == len(seg_ad)
+    lens = np.diff(starts)
+    assert tab.min_seg_len == (int(lens.min()) if lens.size else 0)
+    assert tab.max_seg_len == (int(lens.max()) if lens.size else 0)
+
+
+def test_build_segments_rejects_bad_ids():
+    for bad in ([0, 3], [-1, 0]):
+        with pytest.raises(sgmv.SgmvError) as e:
+            sgmv.sgmv_build_segments(np.array(bad, np.int32), 3)
+        assert e.value.status == _lib.ERR_ADAPTER_ID
+    L = _lib.lib()
+    assert L.sgmv_build_segments(None, 4, 3, None, None, None, None, None, None) == _lib.ERR_NULL
+    out = np.zeros(4, np.int32)
+    assert L.sgmv_build_segments(None, -1, 3, None, out.ctypes.data, None, out.ctypes.data,
+                                 None, None) == _lib.ERR_SHAPE
+
+
+def test_build_ptr_table():
+    base = np.array([4096, 8192, 12288, 16384], np.uint64)
+    seg_ad = np.array([0, 2, 3], np.int32)
+    assert np.array_equal(sgmv.sgmv_build_ptr_table(base, seg_ad), oracle.ptr_table(base, seg_ad))
+    with pytest.raises(sgmv.SgmvError) as e:
+        sgmv.sgmv_build_ptr_table(base, np.array([4], np.int32))
+    assert e.value.status == _lib.ERR_ADAPTER_ID
+    with pytest.raises(sgmv.SgmvError) as e:
+        sgmv.sgmv_build_ptr_table(np.array([4100], np.uint64), np.array([0], np.int32))
+    assert e.value.status == _lib.ERR_ALIGNMENT
+
+
+def test_workspace_bytes():
+    assert sgmv.sgmv_workspace_bytes(32, 4096, 16) >= 8 * 32 * 16 * 4
+    assert sgmv.sgmv_workspace_bytes(32, 4096, 7) == 0
+    assert sgmv.sgmv_workspace_bytes(-1, 4096, 16) == 0
+    a = sgmv.sgmv_workspace_bytes(2112, 28672, 64)
+    assert a >= 2112 * 64 * 4 and a < 64 * 2 ** 20
+
+
+# --------------------------------------------------------------------------------------
+# validation: every one of these returns before any HIP call
+# --------------------------------------------------------------------------------------
+# Fake, 256-aligned "device" addresses: never dereferenced because every call below is
+# rejected by the host-side checks.
+X, Y, V, WS, TAB = 1 << 40, 2 << 40, 3 << 40, 4 << 40, 5 << 40
+
+
+def _lora(**kw):
+    a = dict(stream=None, dtype=0, y=Y, ld_y=4096, x=X, ld_x=4096, A_ptrs=TAB, B_ptrs=TAB + 256,
+             seg_starts=TAB + 512, perm=None, n=32, n_segments=32, min_seg_len=1, max_seg_len=1,
+             h_in=4096, h_out=4096, r=16, scale=2.0, workspace=WS, workspace_bytes=1 << 30)
+    a.update(kw)
+    return sgmv.sgmv_lora_add(**a)
+
+
+REJECTS = [
+    ("dtype", dict(dtype=2), _lib.ERR_UNSUPPORTED),
+    ("rank", dict(r=8), _lib.ERR_UNSUPPORTED),
+    ("rank128", dict(r=128), _lib.ERR_UNSUPPORTED),
+    ("n<0", dict(n=-1), _lib.ERR_SHAPE),
+    ("S>n", dict(n_segments=33), _lib.ERR_SHAPE),
+    ("S=0", dict(n_segments=0), _lib.ERR_SHAPE),
+    ("min>max", dict(min_seg_len=2, max_seg_len=1), _lib.ERR_SHAPE),
+    ("max<ceil(n/S)", dict(n_segments=16, max_seg_len=1), _lib.ERR_SHAPE),
+    ("min>n/S", dict(n_segments=16, min_seg_len=3, max_seg_len=3), _lib.ERR_SHAPE),
+    ("max>n", dict(max_seg_len=33), _lib.ERR_SHAPE),
+    ("h_in%8", dict(h_in=4092, ld_x=4092), _lib.ERR_ALIGNMENT),
+    ("ld_x<h_in", dict(ld_x=4088), _lib.ERR_SHAPE),
+    ("ld_y%8", dict(ld_y=4100), _lib.ERR_ALIGNMENT),
+    ("h_out tiny", dict(h_out=0), _lib.ERR_SHAPE),
+    ("x null", dict(x=None), _lib.ERR_NULL),
+    ("A null", dict(A_ptrs=None), _lib.ERR_NULL),
+    ("seg null", dict(seg_starts=None), _lib.ERR_NULL),
+    ("x misaligned", dict(x=X + 8), _lib.ERR_ALIGNMENT),
+    ("y misaligned", dict(y=Y + 2), _lib.ERR_ALIGNMENT),
+    ("alias", dict(y=X + 4096 * 2), _lib.ERR_ALIAS),
+    ("ws null", dict(workspace=None), _lib.ERR_WORKSPACE),
+    ("ws small", dict(workspace_bytes=100), _lib.ERR_WORKSPACE),
+    ("ws misaligned", dict(workspace=WS + 16), _lib.ERR_WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", REJECTS, ids=[r[0] for r in REJECTS])
+def test_lora_add_rejects(name, kw, code):
+    assert _lora(**kw) == code
+
+
+def test_n_zero_is_ok_without_launch():
+    assert _lora(n=0, n_segments=0, min_seg_len=0, max_seg_len=0, x=None, y=None) == _lib.OK
+
+
+def test_shrink_and_expand_reject():
+    L = _lib.lib()
+    ok = dict(n=32, S=32, lo=1, hi=1)
+    # shrink: v overlapping x
+    assert L.sgmv_shrink(None, 0, X + 64, X, 4096, TAB, TAB + 512, None, 32, 32, 1, 1, 4096,
+                         16, WS, 1 << 30) == _lib.ERR_ALIAS
+    assert L.sgmv_shrink(None, 0, V, X, 4096, TAB, TAB + 512, None, 32, 32, 1, 1, 4096,
+                         12, WS, 1 << 30) == _lib.ERR_UNSUPPORTED
+    assert L.sgmv_shrink(None, 0, V, X, 4096, TAB, TAB + 512, None, 32, 32, 1, 1, 4096,
+                         16, WS, 16) == _lib.ERR_WORKSPACE
+    # expand: y overlapping v, null B
+    assert L.sgmv_expand(None, 1, Y, 4096, Y + 256, TAB, TAB + 512, None, 32, 32, 1, 1, 16,
+                         4096, 1.0) == _lib.ERR_ALIAS
+    assert L.sgmv_expand(None, 1, Y, 4096, V, None, TAB + 512, None, 32, 32, 1, 1, 16,
+                         4096, 1.0) == _lib.ERR_NULL
+    assert ok
+
+
+def _no_gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+@pytest.mark.skipif(not _no_gpu_visible(), reason="needs a machine without a GPU: the fake "
+                    "addresses would reach a kernel")
+def test_valid_call_without_device_is_hip_error():
+    assert _lora() == _lib.ERR_HIP
