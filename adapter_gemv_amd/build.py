@@ -23,7 +23,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libsgmv.so")
 ARCH = "gfx950"
 
-SOURCES = ["sgmv_segments.cpp", "sgmv_kernels.hip"]
+SOURCES = ["sgmv_segments.cpp", "sgmv_kernels.hip", "sgmv_decode.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}",
           "-Wall", "-Wno-unused-function",
@@ -57,9 +57,10 @@ def build(asm: bool = False, verbose: bool = False) -> str:
         objs.append(obj)
         jobs.append([hipcc, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
     if asm:
-        jobs.append([hipcc, *COMMON, "--cuda-device-only", "-S",
-                     os.path.join(CSRC, "sgmv_kernels.hip"),
-                     "-o", os.path.join(BUILD_DIR, "sgmv_kernels.gfx950.s")])
+        for src in SOURCES:
+            if src.endswith(".hip"):
+                jobs.append([hipcc, *COMMON, "--cuda-device-only", "-S", os.path.join(CSRC, src),
+                             "-o", os.path.join(BUILD_DIR, src.replace(".hip", ".gfx950.s"))])
     with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         outs = list(ex.map(_run, jobs))
     if verbose:

@@ -1,0 +1,463 @@
+// libsgmv decode path for gfx950: one launch per SGMV call for batches of up to 64
+// tokens whose adapters live in pools (A_pool[a], B_pool[a] at fixed strides) and
+// whose adapter ids are already on the device.
+//
+// Everything the Punica pages put in one SGMV call happens inside this one kernel
+// (paper summary on research.elamur.ai, "Summary" and "Interesting ideas" I1/I2):
+//   * the batch is sorted by adapter id into segments (every workgroup sorts the <= 64
+//     (id, row) keys of the batch in registers with a wavefront bitonic network --
+//     cheaper than a separate launch or a host round trip);
+//   * shrink items (segment, K chunk) compute float32 partial sums of v = x @ A[a] on
+//     MFMA 16x16x32 tiles and publish them with a release fence and a per-segment
+//     counter;
+//   * expand items (segment, column chunk) load their slice of B[a] and of y while
+//     the shrink runs, wait for the segment's counter, add the partial sums in a fixed
+//     order and write y = y + scale * v @ B[a] with one rounding.
+// Items are ordered shrink-first in the grid.  Workgroups are dispatched in index
+// order within each XCD, so every shrink item a waiting expand item depends on has
+// already been placed on a CU; shrink items never wait, hence the waits always end.
+// The last expand item of a segment resets its counter, leaving the workspace ready
+// for the next call without a memset (safe under HIP graph capture).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/sgmv.h"
+#include "sgmv_checks.h"
+#include "sgmv_device.h"
+
+namespace {
+
+using namespace sgmv_dev;
+using namespace sgmv_host;
+
+constexpr int kPoolMaxN = 64;            // tokens per call on this path (one wavefront)
+constexpr int kWsCounters = 256;         // byte offset of the per-leader counters
+constexpr int kCounterStride = 64;       // ints: one counter per 256-byte line (no sharing)
+constexpr int kWsPartials = 32768;       // byte offset of the split-K partial sums
+constexpr int kSpinLimit = 1 << 22;      // bounded wait (about 0.1 s), then flag and exit
+constexpr uint32_t kNoKey = 0xffffffffu;
+
+// ------------------------------------------------------------------------------------
+// segment plan of one batch, computed by a single wavefront
+// ------------------------------------------------------------------------------------
+// Lane p ends up holding the p-th smallest key (id << 6 | caller row): a stable sort by
+// adapter id, since the caller row breaks ties.  Rows with an id outside
+// [0, n_adapters) get no key and are skipped.
+struct WavePlan {
+  uint32_t key;     // per lane: sorted key at position lane, kNoKey past the valid rows
+  uint64_t starts;  // bit p set: sorted position p starts a segment
+  int S;            // number of segments
+  int n_valid;      // rows with a valid id
+  bool bad_id;      // some id was out of range
+};
+
+__device__ inline WavePlan wave_plan(const int32_t* __restrict__ ids, int n, int n_adapters) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key = kNoKey;
+  bool bad = false;
+  if (lane < n) {
+    const int id = ids[lane];
+    if (id >= 0 && id < n_adapters)
+      key = (static_cast<uint32_t>(id) << 6) | static_cast<uint32_t>(lane);
+    else
+      bad = true;
+  }
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(key), j));
+      const bool ascending = (lane & k) == 0;
+      const bool lower = (lane & j) == 0;
+      const uint32_t lo = key < other ? key : other, hi = key < other ? other : key;
+      key = (lower == ascending) ? lo : hi;
+    }
+  }
+  const uint32_t prev = static_cast<uint32_t>(__shfl_up(static_cast<int>(key), 1));
+  const bool valid = key != kNoKey;
+  const bool start = valid && (lane == 0 || (key >> 6) != (prev >> 6));
+  WavePlan P;
+  P.key = key;
+  P.starts = __ballot(start);
+  P.S = __popcll(P.starts);
+  P.n_valid = __popcll(__ballot(valid));
+  P.bad_id = __ballot(bad) != 0;
+  return P;
+}
+
+// sorted position where segment s starts (s < popcount(mask))
+__device__ inline int nth_set_bit(uint64_t mask, int s) {
+  for (int t = 0; t < s; ++t) mask &= mask - 1;
+  return __ffsll(static_cast<long long>(mask)) - 1;
+}
+
+struct SegInfo {
+  int a;     // adapter
+  int seg0;  // first sorted position
+  int m;     // rows
+};
+
+__device__ inline SegInfo segment_of(const WavePlan& P, int s) {
+  SegInfo g;
+  g.seg0 = nth_set_bit(P.starts, s);
+  const uint64_t later = (g.seg0 >= 63) ? 0ull : (P.starts & ~((2ull << g.seg0) - 1ull));
+  const int end = later ? (__ffsll(static_cast<long long>(later)) - 1) : P.n_valid;
+  g.m = end - g.seg0;
+  g.a = static_cast<int>(static_cast<uint32_t>(__shfl(static_cast<int>(P.key), g.seg0)) >> 6);
+  return g;
+}
+
+// caller row of sorted position q (q may differ per lane; every lane must call)
+__device__ inline int caller_row(const WavePlan& P, int q) {
+  return static_cast<int>(static_cast<uint32_t>(__shfl(static_cast<int>(P.key), q & 63)) & 63u);
+}
+
+// ------------------------------------------------------------------------------------
+// a1 on the device: write the segment tables (for callers that want them, and tests)
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void segments_from_ids_kernel(
+    const int32_t* __restrict__ ids, int32_t n, int32_t n_adapters, int32_t* __restrict__ perm,
+    int32_t* __restrict__ seg_starts, int32_t* __restrict__ seg_adapter,
+    int32_t* __restrict__ n_segments) {
+  const int lane = threadIdx.x;
+  const WavePlan P = wave_plan(ids, n, n_adapters);
+  if (lane < P.n_valid) perm[lane] = static_cast<int32_t>(P.key & 63u);
+  if ((P.starts >> lane) & 1ull) {
+    const int s = __popcll(P.starts & ((1ull << lane) - 1ull));
+    seg_starts[s] = lane;
+    seg_adapter[s] = static_cast<int32_t>(P.key >> 6);
+  }
+  if (lane == 0) {
+    seg_starts[P.S] = P.n_valid;
+    n_segments[0] = P.bad_id ? -1 : P.S;
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// fused shrink + expand
+// ------------------------------------------------------------------------------------
+// Work items are keyed by a *leader* row: the first caller row of each adapter.  One
+// coalesced load of the ids and one ballot give every workgroup its adapter and the
+// set of rows that share it (the same rows, in the same caller order, as the stable
+// sort's segment; the order of segments does not change the result).  Split-K partial
+// sums are indexed by caller row.  They are published with agent-scope atomic stores
+// that are complete before the segment counter is bumped, and read back with
+// agent-scope atomic loads, so no L2 write-back or invalidate is needed between XCDs.
+struct PoolArgs {
+  uint16_t* y;
+  const uint16_t* x;
+  const int32_t* ids;
+  const uint16_t* A;
+  const uint16_t* B;
+  int64_t ld_y, ld_x, A_stride, B_stride;
+  int32_t n, n_adapters, h_in, h_out;
+  int32_t KS, NS;
+  float scale;
+  int32_t* ws_flag;
+  int32_t* counters;
+  float* part;
+};
+
+struct Leader {
+  int a;          // adapter
+  uint64_t rows;  // caller rows that use it
+};
+
+// The item's leader row i: returns false when row i is not the first row of a valid
+// adapter (the workgroup then has nothing to do).
+__device__ inline bool leader_of(const PoolArgs& p, int id_lane, int i, Leader* L) {
+  const int lane = threadIdx.x & 63;
+  const int a = __builtin_amdgcn_readlane(id_lane, i);
+  if (a < 0 || a >= p.n_adapters) return false;
+  const uint64_t rows = __ballot(lane < p.n && id_lane == a);
+  if (rows & ((1ull << i) - 1ull)) return false;  // an earlier row has the same adapter
+  L->a = a;
+  L->rows = rows;
+  return true;
+}
+
+__device__ inline void store_partial(float* q, float v) {
+  __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline float load_partial(const float* q) {
+  return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// partial-sum rows are padded to whole 128-byte lines so items of different adapters
+// never write into one line
+template <int R>
+constexpr int part_row() { return R < 32 ? 32 : R; }
+
+// shrink item: partial v over k in [kc*KC, (kc+1)*KC) for every row of the adapter.
+// MFMA 16x16x32 over blocks of 16 caller rows; lane l supplies MFMA row/column l%16
+// and the k group l/16, reading its own contiguous 8*U-element run of k for both
+// operands.  Row blocks without rows of this adapter are skipped.
+template <int DT, int R>
+__device__ inline void shrink_item(const PoolArgs& p, const Leader& L, int i, int kc) {
+  using E = Elem<DT>;
+  constexpr int U = 256 / R;
+  constexpr int NB = R / 16;
+  constexpr int KC = 32 * U;
+  const int lane = threadIdx.x & 63;
+  const int mrow = lane & 15, kq = lane >> 4;
+  const uint16_t* A = p.A + static_cast<int64_t>(L.a) * p.A_stride;
+  const int kbase = kc * KC + kq * 8 * U;
+  uint4 av[NB][U];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = kbase + 8 * u;
+      av[nb][u] = (kk < p.h_in) ? ld16(A + static_cast<int64_t>(nb * 16 + mrow) * p.h_in + kk)
+                                : zero4();
+    }
+  const int64_t slice = static_cast<int64_t>(p.n) * part_row<R>();
+  for (int blk = 0; blk < 4; ++blk) {
+    const uint32_t bm = static_cast<uint32_t>(L.rows >> (16 * blk)) & 0xffffu;
+    if (bm == 0) continue;  // uniform
+    const int row = 16 * blk + mrow;
+    const uint16_t* xr = ((bm >> mrow) & 1u) ? p.x + static_cast<int64_t>(row) * p.ld_x : nullptr;
+    uint4 xv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = kbase + 8 * u;
+      xv[u] = (xr && kk < p.h_in) ? ld16(xr + kk) : zero4();
+    }
+    f32x4_t acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = E::mfma(xv[u], av[nb][u], acc[nb]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * (lane >> 4) + e;
+      if ((bm >> r) & 1u) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          store_partial(p.part + kc * slice + static_cast<int64_t>(16 * blk + r) * part_row<R>() + nb * 16 + mrow,
+                        acc[nb][e]);
+      }
+    }
+  }
+  // every partial store has completed (and is visible device-wide) before the count
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  if (lane == 0)
+    __hip_atomic_fetch_add(&p.counters[i * kCounterStride], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// expand item: one caller row r and columns [nc*64*CPL, (nc+1)*64*CPL); lane owns
+// CPL = 128/R consecutive columns, i.e. 256 contiguous bytes of the stored [h_out, r]
+// B[a].  Keying expand items by row spreads an adapter with many rows over as many
+// wavefronts.  B and y are loaded (and B widened to float32) while the shrink runs.
+template <int DT, int R>
+__device__ inline void expand_item(const PoolArgs& p, const Leader& L, int i, int r, int nc) {
+  using E = Elem<DT>;
+  constexpr int CPL = 128 / R;
+  constexpr int YW = CPL / 2;
+  constexpr int G = 64 / R;  // lanes per column j when reading the partial slices
+  const int lane = threadIdx.x & 63;
+  const int c0 = (nc * 64 + lane) * CPL;
+  const bool cin = c0 < p.h_out;
+
+  uint4 b[16];
+  const uint16_t* Bblk = p.B + static_cast<int64_t>(L.a) * p.B_stride + static_cast<int64_t>(c0) * R;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) b[v] = cin ? ld16(Bblk + 8 * v) : zero4();
+  uint32_t yv[YW];
+#pragma unroll
+  for (int q = 0; q < YW; ++q) yv[q] = 0u;
+  uint16_t* yrow = p.y + static_cast<int64_t>(r) * p.ld_y + c0;
+  if (cin) load_words<YW>(yrow, yv);
+  float bf[CPL * R];
+#pragma unroll
+  for (int e = 0; e < CPL * R; ++e) bf[e] = elem<DT>(b[e >> 3], e & 7);
+
+  if (lane == 0) {
+    int spins = 0;
+    while (__hip_atomic_load(&p.counters[i * kCounterStride], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT) < p.KS) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit) {
+        __hip_atomic_store(p.ws_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+
+  // v[r, j]: lane (j = lane % R, g = lane / R) adds slices g, g+G, ... in order, then
+  // the G groups are combined by a fixed butterfly; every lane ends with the same sum
+  const int64_t slice = static_cast<int64_t>(p.n) * part_row<R>();
+  const float* src = p.part + static_cast<int64_t>(r) * part_row<R>() + (lane % R);
+  const int g = lane / R;
+  float acc = 0.f;
+  for (int k0 = g; k0 < p.KS; k0 += 8 * G) {
+    float part8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + u * G;
+      part8[u] = (k < p.KS) ? load_partial(src + k * slice) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += part8[u];
+  }
+#pragma unroll
+  for (int msk = R; msk < 64; msk <<= 1) acc += __shfl_xor(acc, msk);
+  // broadcast v[r, :] to scalar registers while every lane is active
+  float vj[R];
+#pragma unroll
+  for (int jj = 0; jj < R; ++jj)
+    vj[jj] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), jj));
+
+  if (cin) {
+    float out[CPL];
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) out[cc] = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < R; ++jj)
+#pragma unroll
+      for (int cc = 0; cc < CPL; ++cc) out[cc] = fmaf(vj[jj], bf[cc * R + jj], out[cc]);
+    uint32_t packed[YW];
+#pragma unroll
+    for (int q = 0; q < YW; ++q) {
+      const float y0 = E::lo(yv[q]), y1 = E::hi(yv[q]);
+      packed[q] = E::pack(fmaf(p.scale, out[2 * q], y0), fmaf(p.scale, out[2 * q + 1], y1));
+    }
+    store_words<YW>(yrow, packed);
+  }
+
+  // the last of the adapter's KS + m * NS items leaves its counter at zero for the next call
+  if (lane == 0) {
+    int* c = &p.counters[i * kCounterStride];
+    const int m = __popcll(L.rows);
+    const int old = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == p.KS + m * p.NS - 1) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Grid: n * KS shrink items (leader row i = b % n, chunk b / n), then n * NS expand
+// items (caller row r = e % n, column chunk e / n).  Every shrink item an expand item
+// waits for has a lower index.
+template <int DT, int R>
+__global__ __launch_bounds__(64) void lora_add_pool_kernel(PoolArgs p) {
+  const int lane = threadIdx.x;
+  const int id = lane < p.n ? p.ids[lane] : -1;
+  const int b = blockIdx.x;
+  const int n_shrink = p.n * p.KS;
+  if (b == 0) {
+    const bool bad = __ballot(lane < p.n && (id < 0 || id >= p.n_adapters)) != 0;
+    if (bad && lane == 0) __hip_atomic_store(p.ws_flag, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  Leader L;
+  if (b < n_shrink) {
+    const int i = b % p.n, kc = b / p.n;
+    if (leader_of(p, id, i, &L)) shrink_item<DT, R>(p, L, i, kc);
+  } else {
+    const int e = b - n_shrink;
+    const int r = e % p.n, nc = e / p.n;
+    const int a = __builtin_amdgcn_readlane(id, r);
+    if (a < 0 || a >= p.n_adapters) return;
+    L.a = a;
+    L.rows = __ballot(lane < p.n && id == a);
+    const int i = __ffsll(static_cast<long long>(L.rows)) - 1;  // the adapter's leader row
+    expand_item<DT, R>(p, L, i, r, nc);
+  }
+}
+
+inline int pool_kc(int r) { return 8192 / r; }
+
+template <int DT, int R>
+hipError_t launch_pool(hipStream_t st, const PoolArgs& p) {
+  const int grid = p.n * (p.KS + p.NS);
+  hipLaunchKernelGGL((lora_add_pool_kernel<DT, R>), dim3(grid), dim3(64), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// bytes the decode path needs in the workspace (the table path's own need is larger or
+// equal for r <= 32; sgmv_workspace_bytes returns the maximum of both)
+extern "C" size_t sgmv_pool_workspace_bytes_internal(int32_t n, int32_t h_in, int32_t r) {
+  const int ks = (h_in + pool_kc(r) - 1) / pool_kc(r);
+  const int pr = r < 32 ? 32 : r;
+  return kWsPartials + sizeof(float) * static_cast<size_t>(ks) * n * pr;
+}
+
+extern "C" int sgmv_build_segments_device(hipStream_t stream, const int32_t* adapter_ids,
+                                          int32_t n, int32_t n_adapters, int32_t* perm,
+                                          int32_t* seg_starts, int32_t* seg_adapter,
+                                          int32_t* n_segments) {
+  if (n < 0 || n > kPoolMaxN || n_adapters <= 0 || n_adapters > (1 << 24)) return SGMV_ERR_SHAPE;
+  if (!seg_starts || !n_segments || (n > 0 && (!adapter_ids || !perm || !seg_adapter)))
+    return SGMV_ERR_NULL;
+  int st = check_device();
+  if (st) return st;
+  hipLaunchKernelGGL(segments_from_ids_kernel, dim3(1), dim3(64), 0, stream, adapter_ids, n,
+                     n_adapters, perm, seg_starts, seg_adapter, n_segments);
+  return hip_status(hipGetLastError());
+}
+
+extern "C" int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
+                                  const void* x, int64_t ld_x, const int32_t* adapter_ids,
+                                  int32_t n, const void* A_pool, int64_t A_stride,
+                                  const void* B_pool, int64_t B_stride, int32_t n_adapters,
+                                  int32_t h_in, int32_t h_out, int32_t r, float scale,
+                                  void* workspace, size_t workspace_bytes) {
+  if (dtype != SGMV_F16 && dtype != SGMV_BF16) return SGMV_ERR_UNSUPPORTED;
+  if (!rank_ok(r)) return SGMV_ERR_UNSUPPORTED;
+  if (n < 0 || n > kPoolMaxN || n_adapters <= 0 || n_adapters > (1 << 24)) return SGMV_ERR_SHAPE;
+  int st = check_dim(h_in, ld_x);
+  if (st) return st;
+  if ((st = check_dim(h_out, ld_y))) return st;
+  if (A_stride < static_cast<int64_t>(r) * h_in || B_stride < static_cast<int64_t>(h_out) * r)
+    return SGMV_ERR_SHAPE;
+  if (A_stride % 8 != 0 || B_stride % 8 != 0) return SGMV_ERR_ALIGNMENT;
+  if (n == 0) return SGMV_OK;
+  if (!y || !x || !adapter_ids || !A_pool || !B_pool) return SGMV_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(A_pool) || !aligned16(B_pool))
+    return SGMV_ERR_ALIGNMENT;
+  if (ranges_overlap(x, matrix_bytes(n, ld_x, h_in), y, matrix_bytes(n, ld_y, h_out)))
+    return SGMV_ERR_ALIAS;
+  if (!workspace || workspace_bytes < sgmv_workspace_bytes(n, h_in, r) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return SGMV_ERR_WORKSPACE;
+  if ((st = check_device())) return st;
+
+  PoolArgs p;
+  p.y = static_cast<uint16_t*>(y);
+  p.x = static_cast<const uint16_t*>(x);
+  p.ids = adapter_ids;
+  p.A = static_cast<const uint16_t*>(A_pool);
+  p.B = static_cast<const uint16_t*>(B_pool);
+  p.ld_y = ld_y;
+  p.ld_x = ld_x;
+  p.A_stride = A_stride;
+  p.B_stride = B_stride;
+  p.n = n;
+  p.n_adapters = n_adapters;
+  p.h_in = h_in;
+  p.h_out = h_out;
+  p.KS = (h_in + pool_kc(r) - 1) / pool_kc(r);
+  p.NS = (h_out + pool_kc(r) - 1) / pool_kc(r);  // 64 lanes x 128/r columns per item
+  p.scale = scale;
+  char* ws = static_cast<char*>(workspace);
+  p.ws_flag = reinterpret_cast<int32_t*>(ws);
+  p.counters = reinterpret_cast<int32_t*>(ws + kWsCounters);
+  p.part = reinterpret_cast<float*>(ws + kWsPartials);
+
+  hipError_t e;
+  if (dtype == SGMV_F16) {
+    e = (r == 16) ? launch_pool<SGMV_F16, 16>(stream, p)
+        : (r == 32) ? launch_pool<SGMV_F16, 32>(stream, p) : launch_pool<SGMV_F16, 64>(stream, p);
+  } else {
+    e = (r == 16) ? launch_pool<SGMV_BF16, 16>(stream, p)
+        : (r == 32) ? launch_pool<SGMV_BF16, 32>(stream, p) : launch_pool<SGMV_BF16, 64>(stream, p);
+  }
+  return hip_status(e);
+}

@@ -1,0 +1,124 @@
+// Device-side helpers shared by libsgmv's kernels (gfx950): packed 16-bit element
+// access, 16-byte vector loads and the MFMA 16x16x32 wrappers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/sgmv.h"
+
+namespace sgmv_dev {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+// ------------------------------------------------------------------------------------
+// element helpers: 16-bit values travel packed two per 32-bit word
+// ------------------------------------------------------------------------------------
+template <int DT>
+struct Elem;
+
+template <>
+struct Elem<SGMV_F16> {
+  static __device__ inline float lo(uint32_t u) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(u & 0xffffu)));
+  }
+  static __device__ inline float hi(uint32_t u) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(u >> 16)));
+  }
+  static __device__ inline uint32_t pack(float a, float b) {
+    const uint32_t ua = __builtin_bit_cast(uint16_t, static_cast<_Float16>(a));
+    const uint32_t ub = __builtin_bit_cast(uint16_t, static_cast<_Float16>(b));
+    return ua | (ub << 16);
+  }
+  static __device__ inline f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Elem<SGMV_BF16> {
+  static __device__ inline float lo(uint32_t u) { return __uint_as_float(u << 16); }
+  static __device__ inline float hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+  static __device__ inline uint32_t pack(float a, float b) {
+    const uint32_t ua = __builtin_bit_cast(uint16_t, static_cast<__bf16>(a));
+    const uint32_t ub = __builtin_bit_cast(uint16_t, static_cast<__bf16>(b));
+    return ua | (ub << 16);
+  }
+  static __device__ inline f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+};
+
+__device__ inline uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ inline uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+// NW consecutive 32-bit words at p (p aligned to 4*NW bytes), as one vector access
+template <int NW>
+__device__ inline void load_words(const uint16_t* p, uint32_t* out) {
+  if constexpr (NW == 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+  } else if constexpr (NW == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    out[0] = v.x; out[1] = v.y;
+  } else {
+    out[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+}
+
+template <int NW>
+__device__ inline void store_words(uint16_t* p, const uint32_t* in) {
+  if constexpr (NW == 4) {
+    *reinterpret_cast<uint4*>(p) = make_uint4(in[0], in[1], in[2], in[3]);
+  } else if constexpr (NW == 2) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(in[0], in[1]);
+  } else {
+    *reinterpret_cast<uint32_t*>(p) = in[0];
+  }
+}
+
+__device__ inline uint32_t word(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// element e (0..7) of a 16-byte vector of 16-bit values, as float
+template <int DT>
+__device__ inline float elem(const uint4& v, int e) {
+  const uint32_t w = word(v, e >> 1);
+  return (e & 1) ? Elem<DT>::hi(w) : Elem<DT>::lo(w);
+}
+
+// sum of the 8 products of two 16-byte vectors, in a fixed order, added to acc
+template <int DT>
+__device__ inline float dot8(const uint4& a, const uint4& b, float acc) {
+  using E = Elem<DT>;
+  acc = fmaf(E::lo(a.x), E::lo(b.x), acc);
+  acc = fmaf(E::hi(a.x), E::hi(b.x), acc);
+  acc = fmaf(E::lo(a.y), E::lo(b.y), acc);
+  acc = fmaf(E::hi(a.y), E::hi(b.y), acc);
+  acc = fmaf(E::lo(a.z), E::lo(b.z), acc);
+  acc = fmaf(E::hi(a.z), E::hi(b.z), acc);
+  acc = fmaf(E::lo(a.w), E::lo(b.w), acc);
+  acc = fmaf(E::hi(a.w), E::hi(b.w), acc);
+  return acc;
+}
+
+// sum of ks float slices src[0], src[stride], ... in slice order, 8 loads in flight
+__device__ inline float sum_slices(const float* __restrict__ src, int64_t stride, int ks) {
+  float acc = 0.f;
+  for (int k0 = 0; k0 < ks; k0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = (k0 + u < ks) ? src[(k0 + u) * stride] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  return acc;
+}
+
+}  // namespace sgmv_dev

@@ -20,111 +20,17 @@
 #include <cstdint>
 
 #include "../../include/sgmv.h"
+#include "sgmv_checks.h"
+#include "sgmv_device.h"
 
 namespace {
+
+using namespace sgmv_dev;
+using namespace sgmv_host;
 
 constexpr int kLongMin = 16;   // segments with at least this many rows use MFMA tiles
 constexpr int kTileRows = 16;  // sorted rows per tile on the long-segment path
 constexpr int kShortMax = kLongMin - 1;
-constexpr int64_t kMaxDim = int64_t(1) << 22;
-
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-
-// ------------------------------------------------------------------------------------
-// element helpers: 16-bit values travel packed two per 32-bit word
-// ------------------------------------------------------------------------------------
-template <int DT>
-struct Elem;
-
-template <>
-struct Elem<SGMV_F16> {
-  static __device__ inline float lo(uint32_t u) {
-    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(u & 0xffffu)));
-  }
-  static __device__ inline float hi(uint32_t u) {
-    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(u >> 16)));
-  }
-  static __device__ inline uint32_t pack(float a, float b) {
-    const uint32_t ua = __builtin_bit_cast(uint16_t, static_cast<_Float16>(a));
-    const uint32_t ub = __builtin_bit_cast(uint16_t, static_cast<_Float16>(b));
-    return ua | (ub << 16);
-  }
-  static __device__ inline f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
-                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-  }
-};
-
-template <>
-struct Elem<SGMV_BF16> {
-  static __device__ inline float lo(uint32_t u) { return __uint_as_float(u << 16); }
-  static __device__ inline float hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-  static __device__ inline uint32_t pack(float a, float b) {
-    const uint32_t ua = __builtin_bit_cast(uint16_t, static_cast<__bf16>(a));
-    const uint32_t ub = __builtin_bit_cast(uint16_t, static_cast<__bf16>(b));
-    return ua | (ub << 16);
-  }
-  static __device__ inline f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-  }
-};
-
-__device__ inline uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ inline uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
-
-// NW consecutive 32-bit words at p (p aligned to 4*NW bytes), as one vector access
-template <int NW>
-__device__ inline void load_words(const uint16_t* p, uint32_t* out) {
-  if constexpr (NW == 4) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
-  } else if constexpr (NW == 2) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    out[0] = v.x; out[1] = v.y;
-  } else {
-    out[0] = *reinterpret_cast<const uint32_t*>(p);
-  }
-}
-
-template <int NW>
-__device__ inline void store_words(uint16_t* p, const uint32_t* in) {
-  if constexpr (NW == 4) {
-    *reinterpret_cast<uint4*>(p) = make_uint4(in[0], in[1], in[2], in[3]);
-  } else if constexpr (NW == 2) {
-    *reinterpret_cast<uint2*>(p) = make_uint2(in[0], in[1]);
-  } else {
-    *reinterpret_cast<uint32_t*>(p) = in[0];
-  }
-}
-
-__device__ inline uint32_t word(const uint4& v, int i) {
-  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
-}
-
-// element e (0..7) of a 16-byte vector of 16-bit values, as float
-template <int DT>
-__device__ inline float elem(const uint4& v, int e) {
-  const uint32_t w = word(v, e >> 1);
-  return (e & 1) ? Elem<DT>::hi(w) : Elem<DT>::lo(w);
-}
-
-// sum of the 8 products of two 16-byte vectors, in a fixed order, added to acc
-template <int DT>
-__device__ inline float dot8(const uint4& a, const uint4& b, float acc) {
-  using E = Elem<DT>;
-  acc = fmaf(E::lo(a.x), E::lo(b.x), acc);
-  acc = fmaf(E::hi(a.x), E::hi(b.x), acc);
-  acc = fmaf(E::lo(a.y), E::lo(b.y), acc);
-  acc = fmaf(E::hi(a.y), E::hi(b.y), acc);
-  acc = fmaf(E::lo(a.z), E::lo(b.z), acc);
-  acc = fmaf(E::hi(a.z), E::hi(b.z), acc);
-  acc = fmaf(E::lo(a.w), E::lo(b.w), acc);
-  acc = fmaf(E::hi(a.w), E::hi(b.w), acc);
-  return acc;
-}
 
 // Segment that holds sorted row `row` (0 <= row < n): the number of s in [1, S] with
 // seg_starts[s] <= row, since seg_starts is non-decreasing with seg_starts[0] = 0.
@@ -248,10 +154,7 @@ __global__ __launch_bounds__(64) void expand_gemv_kernel(
 
   for (int idx = lane; idx < m * R; idx += 64) {
     const int i = idx / R, jj = idx % R;
-    const float* p = vsrc + static_cast<int64_t>(seg0 + i) * R + jj;
-    float acc = 0.f;
-    for (int k = 0; k < ks; ++k) acc += p[k * slice];
-    vs[i][jj] = acc;
+    vs[i][jj] = sum_slices(vsrc + static_cast<int64_t>(seg0 + i) * R + jj, slice, ks);
   }
   __syncthreads();
   if (!cin) return;
@@ -377,10 +280,7 @@ __global__ __launch_bounds__(256) void expand_long_kernel(
 
   for (int idx = threadIdx.x; idx < (r1 - r0) * R; idx += 256) {
     const int i = idx / R, jj = idx % R;
-    const float* p = vsrc + static_cast<int64_t>(r0 + i) * R + jj;
-    float acc = 0.f;
-    for (int k = 0; k < ks; ++k) acc += p[k * slice];
-    vs[i][jj] = acc;
+    vs[i][jj] = sum_slices(vsrc + static_cast<int64_t>(r0 + i) * R + jj, slice, ks);
   }
   __syncthreads();
   if (!cin) return;
@@ -441,16 +341,13 @@ __global__ __launch_bounds__(256) void reduce_v_kernel(float* __restrict__ v,
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= static_cast<int64_t>(n) * R) return;
   const int row = static_cast<int>(idx / R);
-  const int ks = min(rowks[row], ks_max);
-  float acc = 0.f;
-  for (int k = 0; k < ks; ++k) acc += part[k * slice + idx];
-  v[idx] = acc;
+  v[idx] = sum_slices(part + idx, slice, min(rowks[row], ks_max));
 }
 
 // ------------------------------------------------------------------------------------
 // host side: sizes, validation, launches
 // ------------------------------------------------------------------------------------
-constexpr size_t kWsHeader = 256;
+constexpr size_t kWsHeader = 32768;  // error flag and the decode path's counters
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -494,40 +391,6 @@ inline int mfma_kcm(int32_t n, int32_t h_in, int32_t r) {
   const int steps_per_chunk = (steps_total + chunks - 1) / chunks;
   return steps_per_chunk * step;
 }
-
-bool rank_ok(int32_t r) { return r == 16 || r == 32 || r == 64; }
-
-bool ranges_overlap(const void* a, size_t abytes, const void* b, size_t bbytes) {
-  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
-  return a0 < b0 + bbytes && b0 < a0 + abytes;
-}
-
-size_t matrix_bytes(int32_t rows, int64_t ld, int32_t cols) {
-  if (rows <= 0) return 0;
-  return (static_cast<size_t>(rows - 1) * static_cast<size_t>(ld) + static_cast<size_t>(cols)) * 2;
-}
-
-// checks shared by every device entry point; 0 when fine
-int check_segments(int32_t n, int32_t S, int32_t min_len, int32_t max_len) {
-  if (n < 0) return SGMV_ERR_SHAPE;
-  if (n == 0) return SGMV_OK;
-  if (S < 1 || S > n) return SGMV_ERR_SHAPE;
-  if (min_len < 0 || max_len < 1 || min_len > max_len || max_len > n) return SGMV_ERR_SHAPE;
-  // pigeonhole: the longest segment holds at least ceil(n/S) rows, the shortest at most n/S
-  if (static_cast<int64_t>(max_len) * S < n) return SGMV_ERR_SHAPE;
-  if (static_cast<int64_t>(min_len) * S > n) return SGMV_ERR_SHAPE;
-  return SGMV_OK;
-}
-
-int check_dim(int32_t h, int64_t ld) {
-  if (h < 8 || h > kMaxDim || ld < h) return SGMV_ERR_SHAPE;
-  if (h % 8 != 0 || ld % 8 != 0) return SGMV_ERR_ALIGNMENT;
-  return SGMV_OK;
-}
-
-inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-int hip_status(hipError_t e) { return e == hipSuccess ? SGMV_OK : SGMV_ERR_HIP; }
 
 struct Tables {
   const uint16_t* const* ptrs;
@@ -633,17 +496,17 @@ struct LoraOp {
   static hipError_t run(A... a) { return run_lora_add<DT, R>(a...); }
 };
 
-int check_device() {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return SGMV_ERR_HIP;
-  return SGMV_OK;
-}
 
 }  // namespace
 
+extern "C" size_t sgmv_pool_workspace_bytes_internal(int32_t n, int32_t h_in, int32_t r);
+
 extern "C" size_t sgmv_workspace_bytes(int32_t n, int32_t h_in, int32_t r) {
   if (n < 0 || h_in < 8 || h_in > kMaxDim || !rank_ok(r)) return 0;
-  return ws_layout(n, h_in, r).total;
+  const size_t a = ws_layout(n, h_in, r).total;
+  // the one-launch decode path takes at most 64 rows
+  const size_t b = n <= 64 ? sgmv_pool_workspace_bytes_internal(n, h_in, r) : 0;
+  return a > b ? a : b;
 }
 
 extern "C" int sgmv_shrink(hipStream_t stream, int32_t dtype, float* v, const void* x, int64_t ld_x,

@@ -58,6 +58,16 @@ class DeviceProblem:
         sgmv.lora_add(y, self.x, self.batch, self.scale if scale is None else scale, workspace)
         return y
 
+    def lora_add_pool(self, y=None, workspace=None, scale=None, ids=None):
+        """The one-launch decode path (n <= 64) with device-resident ids."""
+        import torch
+        y = self.fresh_y() if y is None else y
+        if ids is None:
+            ids = torch.as_tensor(self.ids, dtype=torch.int32, device=self.x.device)
+        sgmv.lora_add_pool(y, self.x, ids, self.A, self.B,
+                           self.scale if scale is None else scale, workspace)
+        return y
+
     def shrink(self, workspace=None):
         return sgmv.shrink(self.x, self.batch, workspace=workspace)
 

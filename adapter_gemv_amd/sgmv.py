@@ -276,3 +276,65 @@ def expand(y, v, batch: Batch, scale: float, stream=None):
 
 def _infer_rank(batch: Batch) -> int:
     return int(batch.rank)
+
+
+# --------------------------------------------------------------------------------------
+# decode path: device-resident adapter ids, adapters in pools, one launch per call
+# --------------------------------------------------------------------------------------
+def sgmv_build_segments_device(stream, adapter_ids, n, n_adapters, perm, seg_starts,
+                               seg_adapter, n_segments) -> int:
+    return _lib.lib().sgmv_build_segments_device(stream, adapter_ids, n, n_adapters, perm,
+                                                 seg_starts, seg_adapter, n_segments)
+
+
+def sgmv_lora_add_pool(stream, dtype, y, ld_y, x, ld_x, adapter_ids, n, A_pool, A_stride,
+                       B_pool, B_stride, n_adapters, h_in, h_out, r, scale, workspace,
+                       workspace_bytes) -> int:
+    return _lib.lib().sgmv_lora_add_pool(stream, dtype, y, ld_y, x, ld_x, adapter_ids, n, A_pool,
+                                         A_stride, B_pool, B_stride, n_adapters, h_in, h_out, r,
+                                         float(scale), workspace, workspace_bytes)
+
+
+POOL_MAX_TOKENS = 64
+
+
+def build_segments_device(ids, n_adapters: int, stream=None):
+    """Device segment tables for device int32 ids (n <= 64): (perm, seg_starts,
+    seg_adapter, n_segments) as int32 tensors; n_segments[0] is -1 if an id is out of
+    range."""
+    torch = _torch()
+    n = int(ids.shape[0])
+    dev = ids.device
+    perm = torch.full((max(n, 1),), -1, dtype=torch.int32, device=dev)
+    starts = torch.full((n + 1,), -1, dtype=torch.int32, device=dev)
+    seg_ad = torch.full((max(n, 1),), -1, dtype=torch.int32, device=dev)
+    S = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = sgmv_build_segments_device(_stream_handle(stream), ids.data_ptr(), n, int(n_adapters),
+                                    perm.data_ptr(), starts.data_ptr(), seg_ad.data_ptr(),
+                                    S.data_ptr())
+    check(st, "sgmv_build_segments_device")
+    return perm, starts, seg_ad, S
+
+
+def lora_add_pool(y, x, ids, A_pool, B_pool, scale: float, workspace=None, stream=None):
+    """y[t] += scale * (x[t] @ A_pool[ids[t]]) @ B_pool[ids[t]] in one launch (n <= 64).
+
+    ``ids`` is a device int32 tensor [n]; ``A_pool`` [P, r, h_in] and ``B_pool``
+    [P, h_out, r] are device tensors with contiguous adapters."""
+    n = int(x.shape[0])
+    _check_rows(x, n, "x")
+    _check_rows(y, n, "y")
+    r = int(A_pool.shape[1])
+    if A_pool.stride(1) != A_pool.shape[2] or A_pool.stride(2) != 1:
+        raise ValueError("each A_pool[a] must be a dense [r, h_in] array")
+    if B_pool.stride(1) != B_pool.shape[2] or B_pool.stride(2) != 1:
+        raise ValueError("each B_pool[a] must be a dense [h_out, r] array")
+    if workspace is None:
+        workspace = make_workspace(n, x.shape[1], r, x.device)
+    st = sgmv_lora_add_pool(_stream_handle(stream), dtype_code(y), y.data_ptr(), y.stride(0),
+                            x.data_ptr(), x.stride(0), ids.data_ptr(), n, A_pool.data_ptr(),
+                            A_pool.stride(0), B_pool.data_ptr(), B_pool.stride(0),
+                            int(A_pool.shape[0]), x.shape[1], y.shape[1], r, scale,
+                            workspace.data_ptr(), workspace.numel())
+    check(st, "sgmv_lora_add_pool")
+    return y

@@ -1,0 +1,402 @@
+#!/usr/bin/env python3
+"""SGMV benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode7b]
+
+One step is one batch through the whole SGMV path, with every input resident in HBM:
+  * batches of <= 64 tokens (the decode workloads) take the one-launch path,
+    sgmv_lora_add_pool: the segment metadata (stable sort of the batch's adapter ids),
+    the shrink and the expand all run in one kernel; the K timed steps are captured in
+    one HIP graph and replayed once, as a serving loop runs its decode steps;
+  * larger batches (prefill, mixed) build the segment metadata with libsgmv's host
+    builder, upload it with one host-to-device copy from pinned memory and call
+    sgmv_lora_add (MFMA tiles for segments of 16+ rows).
+Every step uses a different slot of x / y buffers, adapter ids and adapters, the slots
+together spanning more than 1 GiB, so each step reads its operands from HBM and not from
+the 256 MB Infinity Cache (cache-cold by construction).
+
+Printed: one JSON line with the whole-step throughput (algorithmic bytes per step over
+the wall time of K steps), the per-call duration of sgmv_lora_add from HIP events
+recorded on its stream during the timed steps (the roofline figure), and the fp64 CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from workloads import synth  # noqa: E402
+
+METRIC = "SGMV shrink+expand us/call and HBM GB/s, h=4096 r=16 bs=32 distinct adapters"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16/fp16 MFMA, AMD published figure
+ROTATION_BYTES = 1 << 30       # operand slots cycled per pass (> 2x the 256 MB MALL)
+KERNEL_SRCS = [os.path.join(ROOT, "adapter_gemv_amd", "csrc", f)
+               for f in ("sgmv_device.h", "sgmv_kernels.hip", "sgmv_decode.hip")]
+
+
+def workload_problem(name: str):
+    table = dict(synth.all_workloads())
+    if name not in table:
+        raise SystemExit(f"unknown workload {name!r}; choose from {sorted(table)}")
+    return table[name]()
+
+
+def algorithmic_bytes(p) -> int:
+    """x read once, y read and written once, each distinct adapter's A and B read once."""
+    e = 2
+    D = p.distinct_adapters()
+    return e * (p.n * p.h_in + 2 * p.n * p.h_out + D * p.r * (p.h_in + p.h_out))
+
+
+def algorithmic_flops(p) -> int:
+    return 2 * p.n * p.r * (p.h_in + p.h_out)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# --------------------------------------------------------------------------------------
+# CPU oracle baseline
+# --------------------------------------------------------------------------------------
+def cpu_baseline(p, budget_s: float = 12.0):
+    import oracle
+    from threadpoolctl import threadpool_info
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.lora_add_problem(p)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per_call = el / reps
+    threads = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+    cores = int(threads[0]) if threads else 1
+    return {
+        "value": round(algorithmic_bytes(p) / per_call / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{reps} full calls of the same workload ({p.name}) in {el:.1f} s; "
+                  f"{per_call * 1e3:.2f} ms/call; numpy fp64, BLAS threads {cores}, "
+                  f"os.cpu_count() {os.cpu_count()}",
+    }
+
+
+# --------------------------------------------------------------------------------------
+# GPU setup
+# --------------------------------------------------------------------------------------
+class Rig:
+    """Rotation slots of x, y, adapter ids and adapters on the device."""
+
+    def __init__(self, p, device, seed=1234):
+        import torch
+        from adapter_gemv_amd import sgmv
+        self.p = p
+        self.device = device
+        per_slot = algorithmic_bytes(p)
+        self.slots = max(2, min(256, -(-ROTATION_BYTES // per_slot)))
+        S_, P = self.slots, p.n_adapters
+        tdt = torch.float16 if p.dtype == "f16" else torch.bfloat16
+        g = torch.Generator(device=device)
+        g.manual_seed(seed)
+
+        def randn(shape, std):
+            t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+            return (t * std).to(tdt)
+
+        self.x = randn((S_, p.n, p.h_in), 1.0)
+        self.y = randn((S_, p.n, p.h_out), 1.0)
+        self.A = randn((S_ * P, p.r, p.h_in), 1.0 / np.sqrt(p.h_in))
+        self.B = randn((S_ * P, p.h_out, p.r), 1.0 / np.sqrt(p.r))
+        # slot 0 holds the seeded problem itself (checked against the oracle)
+        self.x[0].copy_(sgmv.as_tensor(p.x, p.dtype, device))
+        self.y[0].copy_(sgmv.as_tensor(p.y, p.dtype, device))
+        self.A[:P].copy_(sgmv.as_tensor(p.A, p.dtype, device))
+        self.B[:P].copy_(sgmv.as_tensor(p.B, p.dtype, device))
+        self.y0 = self.y[0].clone()
+        self.n_pool = S_ * P
+        # slot k's batch uses adapters [k*P, (k+1)*P) of the big pool
+        self.ids = [np.ascontiguousarray(p.ids + k * P, dtype=np.int32) for k in range(S_)]
+        self.ids_dev = torch.as_tensor(np.stack(self.ids), device=device)
+        self.ws = sgmv.make_workspace(p.n, p.h_in, p.r, device)
+        self.dtype_code = sgmv.dtype_code(self.x)
+        self.ld_x, self.ld_y = p.h_in, p.h_out
+        self.pool_path = p.n <= sgmv.POOL_MAX_TOKENS
+        # table path: metadata staging ring (pinned host -> device)
+        self.A_bases = sgmv.adapter_bases(self.A)
+        self.B_bases = sgmv.adapter_bases(self.B)
+        self.ring = 64
+        S_max = min(p.n, self.n_pool)
+        self.meta_bytes = 16 * S_max + 4 * (S_max + 1) + 4 * p.n + 64
+        self.pinned = torch.empty((self.ring, self.meta_bytes), dtype=torch.uint8, pin_memory=True)
+        self.pinned_np = self.pinned.numpy()
+        self.dev_meta = torch.empty((self.ring, self.meta_bytes), dtype=torch.uint8, device=device)
+        self.ring_evt = [None] * self.ring
+
+    def step(self, k: int, ev=None):
+        """One step on slot k.  ``ev`` = (start, end) events bracket the SGMV call."""
+        return self.step_pool(k, ev) if self.pool_path else self.step_table(k, ev)
+
+    def step_pool(self, k: int, ev=None):
+        """Segment metadata, shrink and expand in one launch (device-resident ids)."""
+        import torch
+        from adapter_gemv_amd import sgmv
+        p = self.p
+        slot = k % self.slots
+        stream = torch.cuda.current_stream()
+        if ev is not None:
+            ev[0].record(stream)
+        st = sgmv.sgmv_lora_add_pool(
+            stream.cuda_stream, self.dtype_code, self.y[slot].data_ptr(), self.ld_y,
+            self.x[slot].data_ptr(), self.ld_x, self.ids_dev[slot].data_ptr(), p.n,
+            self.A.data_ptr(), self.A.stride(0), self.B.data_ptr(), self.B.stride(0),
+            self.n_pool, p.h_in, p.h_out, p.r, p.scale, self.ws.data_ptr(), self.ws.numel())
+        if ev is not None:
+            ev[1].record(stream)
+        if st != 0:
+            raise RuntimeError(f"sgmv_lora_add_pool failed: {sgmv.sgmv_status_string(st)}")
+
+    def step_table(self, k: int, ev=None):
+        """Segment metadata for slot k's batch (host build + one pinned H2D copy) and the
+        fused LoRA add-on through the table interface."""
+        import torch
+        from adapter_gemv_amd import sgmv
+        p = self.p
+        slot = k % self.slots
+        i = k % self.ring
+        if self.ring_evt[i] is not None:
+            self.ring_evt[i].synchronize()
+        tab = sgmv.sgmv_build_segments(self.ids[slot], self.n_pool)
+        a_ptr = sgmv.sgmv_build_ptr_table(self.A_bases, tab.seg_adapter)
+        b_ptr = sgmv.sgmv_build_ptr_table(self.B_bases, tab.seg_adapter)
+        S, n = tab.n_segments, tab.n
+        buf = self.pinned_np[i]
+        buf[: 8 * S] = a_ptr.view(np.uint8)
+        buf[8 * S: 16 * S] = b_ptr.view(np.uint8)
+        o_s = 16 * S
+        buf[o_s: o_s + 4 * (S + 1)] = tab.seg_starts.view(np.uint8)
+        o_p = o_s + 4 * (S + 1)
+        buf[o_p: o_p + 4 * n] = tab.perm.view(np.uint8)
+        dev = self.dev_meta[i]
+        dev[: o_p + 4 * n].copy_(self.pinned[i, : o_p + 4 * n], non_blocking=True)
+        base = dev.data_ptr()
+        stream = torch.cuda.current_stream()
+        if ev is not None:
+            ev[0].record(stream)
+        st = sgmv.sgmv_lora_add(
+            stream.cuda_stream, self.dtype_code, self.y[slot].data_ptr(), self.ld_y,
+            self.x[slot].data_ptr(), self.ld_x, base, base + 8 * S, base + o_s, base + o_p,
+            n, S, tab.min_seg_len, tab.max_seg_len, p.h_in, p.h_out, p.r, p.scale,
+            self.ws.data_ptr(), self.ws.numel())
+        if ev is not None:
+            ev[1].record(stream)
+        if st != 0:
+            raise RuntimeError(f"sgmv_lora_add failed: {sgmv.sgmv_status_string(st)}")
+        e = torch.cuda.Event()
+        e.record(stream)
+        self.ring_evt[i] = e
+
+
+def parity_check(rig):
+    """Run slot 0 (the seeded problem) once from its initial y and compare to the oracle."""
+    import torch
+    import oracle
+    from adapter_gemv_amd.device_problem import to_numpy_storage
+    p = rig.p
+    rig.y[0].copy_(rig.y0)
+    rig.step(0)
+    torch.cuda.synchronize()
+    got = oracle.decode(to_numpy_storage(rig.y[0], p.dtype), p.dtype)
+    ref = oracle.lora_add_problem(p)
+    err = np.abs(got - ref)
+    tol = 1e-2 + 1e-2 * np.abs(ref)
+    rig.y[0].copy_(rig.y0)
+    flag = int(rig.ws[:4].view(torch.int32).item())
+    return {"max_abs_err": float(err.max()), "worst_err_over_tol": float((err / tol).max()),
+            "ok": bool(np.all(err <= tol)) and flag == 0, "workspace_flag": flag}
+
+
+def load_traffic(workload: str):
+    """HBM bytes per call from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"sgmv_lora_add_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_call")
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="decode7b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=["auto", "table"], default="auto",
+                    help="auto: one-launch path for batches of <= 64 tokens")
+    ap.add_argument("--eager", action="store_true", help="no HIP graph on the one-launch path")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter scaling)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; multi-GPU runs are not supported "
+              "(--gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 2
+        a = torch.ones(n, dtype=torch.float16, device=device)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": 2 * n}))
+        return 0
+
+    p = workload_problem(args.workload)
+    rig = Rig(p, device)
+    if args.path == "table":
+        rig.pool_path = False
+    parity = parity_check(rig)
+    print(f"# {p.name}: slots={rig.slots} pool_path={rig.pool_path} parity={parity}",
+          file=sys.stderr, flush=True)
+    use_graph = rig.pool_path and not args.eager
+
+    for k in range(args.warmup):
+        rig.step(1 + k)
+    torch.cuda.synchronize()
+    base = 1 + args.warmup
+    stream = torch.cuda.current_stream()
+    t_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    if use_graph:
+        # capture the K timed steps (each on its own slot) into one graph
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            rig.step(base)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for k in range(args.steps):
+                rig.step(base + k)
+        graph.replay()                     # untimed: uploads the graph, K warm steps
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        t_ev[0].record(stream)
+        graph.replay()
+        t_ev[1].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        call_ev = None
+    else:
+        call_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        t_ev[0].record(stream)
+        for k in range(args.steps):
+            rig.step(base + k, call_ev[k])
+        t_ev[1].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    wall = (t1 - t0) / args.steps
+    gpu_step = t_ev[0].elapsed_time(t_ev[1]) * 1e-3 / args.steps
+    if call_ev is None:
+        # per-call kernel time: eager calls, each bracketed by events (untimed pass)
+        n_iso = min(args.steps, 500)
+        call_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n_iso)]
+        for k in range(n_iso):
+            rig.step(base + args.steps + k, call_ev[k])
+        torch.cuda.synchronize()
+    call_ms = np.array([a.elapsed_time(b) for a, b in call_ev])
+    call_s = float(call_ms.mean()) * 1e-3
+    flag = int(rig.ws[:4].view(torch.int32).item())
+
+    nbytes = algorithmic_bytes(p)
+    flops = algorithmic_flops(p)
+    traffic = load_traffic(args.workload)
+    kernel = ("lora_add_pool_kernel (one launch per call)" if rig.pool_path else
+              "sgmv_lora_add table path (all kernels of one call)")
+    out = {
+        "metric": METRIC,
+        "value": round(nbytes / wall / 1e9, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": p.name, "n_tokens": p.n, "h_in": p.h_in, "h_out": p.h_out, "r": p.r,
+            "distinct_adapters": p.distinct_adapters(), "adapter_pool": p.n_adapters,
+            "scale": p.scale, "rotation_slots": rig.slots,
+            "rotation_bytes": rig.slots * nbytes, "cache": "cold (rotating slots)",
+            "step": ("sgmv_lora_add_pool: device segment sort + shrink + expand, one launch" +
+                     (", K steps replayed from one HIP graph" if use_graph else ", eager"))
+                    if rig.pool_path else
+                    "host segment build + pinned H2D tables + sgmv_lora_add, eager",
+        },
+        "us_per_step_gpu": round(gpu_step * 1e6, 3),
+        "us_per_call": round(call_s * 1e6, 3),
+        "us_per_call_p10_p50_p90": [round(float(np.percentile(call_ms, q)) * 1e3, 3)
+                                    for q in (10, 50, 90)],
+        "algorithmic_bytes_per_call": nbytes,
+        "gflops_per_s": round(flops / call_s / 1e9, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(nbytes / call_s / 1e9, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(nbytes / call_s / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": kernel,
+            "mfma_frac": round(flops / call_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
+        },
+        "parity": parity,
+        "workspace_flag_after": flag,
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(p, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0 if parity["ok"] else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

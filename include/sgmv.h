@@ -155,6 +155,41 @@ int sgmv_lora_add(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
                   int32_t h_in, int32_t h_out, int32_t r, float scale,
                   void* workspace, size_t workspace_bytes);
 
+/*
+ * Segment metadata on the device, for a batch of at most 64 tokens whose adapter ids
+ * are already in device memory: the same stable sort as sgmv_build_segments, done by
+ * one wavefront (paper summary, idea I2).  All pointers are device memory.
+ *   adapter_ids  int32[n] in; n <= 64
+ *   perm         int32[n] out (first n_valid entries written)
+ *   seg_starts   int32[n+1] out, seg_adapter int32[n] out
+ *   n_segments   int32[1] out: S, or -1 if some id lies outside [0, n_adapters)
+ *                (rows with such ids are left out of the tables)
+ * Returns SGMV_ERR_SHAPE for n > 64.  Asynchronous on `stream`.
+ */
+int sgmv_build_segments_device(hipStream_t stream, const int32_t* adapter_ids, int32_t n,
+                               int32_t n_adapters, int32_t* perm, int32_t* seg_starts,
+                               int32_t* seg_adapter, int32_t* n_segments);
+
+/*
+ * Decode-sized fused LoRA add-on, one kernel launch: segment metadata, shrink and
+ * expand for a batch of at most 64 tokens, y[t] += scale * (x[t] @ A[a_t]) @ B[a_t].
+ *   adapter_ids  device int32[n]: adapter of caller row t (device memory, so a HIP
+ *                graph can capture the call and replay it with new ids)
+ *   A_pool       device: adapter a's A ([r, h_in] row-major) starts at
+ *                A_pool + a * A_stride elements; A_stride >= r * h_in, multiple of 8
+ *   B_pool       device: adapter a's B ([h_out, r] row-major) at B_pool + a * B_stride
+ *   workspace    as for sgmv_lora_add (sgmv_workspace_bytes(n, h_in, r) bytes,
+ *                zero-filled once); calls sharing a workspace must be stream-ordered
+ * Rows whose id lies outside [0, n_adapters) are left unchanged and set the int32 at
+ * the start of the workspace to 2 (a device-side wait that timed out sets it to 1;
+ * it is never cleared by the library).  Returns SGMV_ERR_SHAPE for n > 64.
+ */
+int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
+                       const void* x, int64_t ld_x, const int32_t* adapter_ids, int32_t n,
+                       const void* A_pool, int64_t A_stride, const void* B_pool,
+                       int64_t B_stride, int32_t n_adapters, int32_t h_in, int32_t h_out,
+                       int32_t r, float scale, void* workspace, size_t workspace_bytes);
+
 #ifdef __cplusplus
 }
 #endif

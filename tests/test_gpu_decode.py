@@ -1,0 +1,215 @@
+"""GPU tests of the one-launch decode path (sgmv_lora_add_pool, sgmv_build_segments_device):
+device segment metadata bit-exact against the oracle's stable sort, parity of y against
+the fp64 oracle, bit-exact grids and gather probes, invalid ids, counter self-reset and
+HIP graph replay."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _upload(p):
+    from adapter_gemv_amd.device_problem import DeviceProblem
+    return DeviceProblem.upload(p)
+
+
+def _storage(y, dtype):
+    from adapter_gemv_amd.device_problem import to_numpy_storage
+    return to_numpy_storage(y, dtype)
+
+
+def _assert_close(got, ref, what):
+    err = np.abs(got - ref)
+    tol = 1e-2 + 1e-2 * np.abs(ref)
+    _say(f"{what}: max|err| {err.max():.3e}, worst err/tol {np.max(err / tol):.3f}")
+    assert np.all(err <= tol), f"{what}: {int((err > tol).sum())} outside tolerance"
+
+
+ID_CASES = [
+    ("n1", np.array([3], np.int32), 5),
+    ("distinct32", np.random.default_rng(0).permutation(32).astype(np.int32), 32),
+    ("same64", np.full(64, 7, np.int32), 9),
+    ("uniform64", np.random.default_rng(1).integers(0, 64, 64).astype(np.int32), 64),
+    ("zipf40", synth.truncated_zipf_ids(np.random.default_rng(2), 40, 4096, 1.2), 4096),
+    ("sparse_pool", np.random.default_rng(3).choice([5, 900, 4000], 33).astype(np.int32), 4096),
+]
+
+
+@pytest.mark.parametrize("name,ids,P", ID_CASES, ids=[c[0] for c in ID_CASES])
+def test_device_segments_match_oracle(torch_cuda, name, ids, P):
+    torch = torch_cuda
+    from adapter_gemv_amd import sgmv
+    _say(f"[segments] {name}")
+    d = torch.as_tensor(ids, device="cuda")
+    perm, starts, seg_ad, S = sgmv.build_segments_device(d, P)
+    torch.cuda.synchronize()
+    rp, rs, ra = oracle.segments(ids, P)
+    s = int(S.item())
+    assert s == len(ra)
+    assert np.array_equal(perm.cpu().numpy()[: len(ids)], rp)
+    assert np.array_equal(starts.cpu().numpy()[: s + 1], rs)
+    assert np.array_equal(seg_ad.cpu().numpy()[:s], ra)
+
+
+def test_device_segments_flag_bad_ids(torch_cuda):
+    torch = torch_cuda
+    from adapter_gemv_amd import sgmv
+    d = torch.as_tensor(np.array([0, 5, 1], np.int32), device="cuda")
+    _, _, _, S = sgmv.build_segments_device(d, 3)
+    assert int(S.item()) == -1
+
+
+DECODE = ["tiny", "decode7b", "sweep_a", "sweep_b", "sweep_c"]
+FACT = dict(synth.all_workloads())
+
+
+@pytest.mark.parametrize("name", DECODE)
+def test_decode_workloads(torch_cuda, name):
+    _say(f"[pool parity] {name}")
+    p = FACT[name]()
+    dp = _upload(p)
+    y = dp.lora_add_pool()
+    torch_cuda.cuda.synchronize()
+    _assert_close(oracle.decode(_storage(y, p.dtype), p.dtype), oracle.lora_add_problem(p), name)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("r", [16, 32, 64])
+@pytest.mark.parametrize("n,P,kind", [(1, 3, "u"), (32, 32, "perm"), (64, 5, "u"), (47, 40, "zipf")])
+def test_pool_exact_bit_exact(torch_cuda, dtype, r, n, P, kind):
+    _say(f"[pool exact] n={n} P={P} r={r} {dtype}")
+    rng = np.random.default_rng(n * 100 + r)
+    ids = {"u": rng.integers(0, P, n), "perm": rng.permutation(n) % P,
+           "zipf": synth.truncated_zipf_ids(rng, n, P, 1.2)}[kind].astype(np.int32)
+    p = synth.exact_problem((81, n, r), n=n, h_in=2056, h_out=1544, r=r, n_adapters=P,
+                            dtype=dtype, ids=ids)
+    y = _upload(p).lora_add_pool()
+    torch_cuda.cuda.synchronize()
+    got = _storage(y, dtype).view(np.uint16)
+    want = oracle.round_io(oracle.lora_add_problem(p), dtype).view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("r", [16, 64])
+def test_pool_gather_probe(torch_cuda, dtype, r):
+    _say(f"[pool gather] r={r} {dtype}")
+    rng = np.random.default_rng(r)
+    ids = rng.integers(0, 6, 50).astype(np.int32)
+    p = synth.gather_probe((82, r), n=50, h_in=512, h_out=384, r=r, n_adapters=6, dtype=dtype,
+                           ids=ids)
+    y = _upload(p).lora_add_pool()
+    torch_cuda.cuda.synchronize()
+    want = oracle.round_io(oracle.lora_add_problem(p), dtype).view(np.uint16)
+    assert np.array_equal(_storage(y, dtype).view(np.uint16), want)
+
+
+RAGGED = [(5, 8, 8, 16), (33, 200, 136, 16), (64, 4104, 1032, 32), (17, 24, 4104, 64),
+          (60, 28672, 8192, 16), (12, 8192, 1024, 64)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("n,h_in,h_out,r", RAGGED)
+def test_pool_ragged(torch_cuda, dtype, n, h_in, h_out, r):
+    _say(f"[pool ragged] n={n} {h_in}x{h_out} r={r} {dtype}")
+    p = synth.random_problem((83, n, h_in, h_out), n=n, h_in=h_in, h_out=h_out, r=r,
+                             n_adapters=7, dtype=dtype, id_dist="zipf", zipf_s=1.1, scale=1.25)
+    y = _upload(p).lora_add_pool()
+    torch_cuda.cuda.synchronize()
+    _assert_close(oracle.decode(_storage(y, dtype), dtype), oracle.lora_add_problem(p),
+                  f"ragged n={n} {h_in}x{h_out} r={r}")
+
+
+def test_pool_invalid_ids_skip_rows_and_flag(torch_cuda):
+    torch = torch_cuda
+    from adapter_gemv_amd import sgmv
+    p = synth.random_problem((84,), n=20, h_in=256, h_out=128, r=16, n_adapters=4, dtype="f16")
+    dp = _upload(p)
+    ids = p.ids.copy()
+    ids[[3, 11]] = [4, -1]
+    ws = sgmv.make_workspace(p.n, p.h_in, 16, dp.x.device)
+    y = dp.lora_add_pool(ids=torch.as_tensor(ids, device="cuda"), workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32).item()) == 2
+    got = oracle.decode(_storage(y, "f16"), "f16")
+    keep = np.ones(p.n, bool)
+    keep[[3, 11]] = False
+    ref = oracle.lora_add(p.y[keep], p.x[keep], p.ids[keep], p.A, p.B, p.scale, "f16")
+    _assert_close(got[keep], ref, "valid rows")
+    assert np.array_equal(got[~keep], oracle.decode(p.y[~keep], "f16"))
+
+
+def test_pool_repeat_calls_reset_counters(torch_cuda):
+    torch = torch_cuda
+    from adapter_gemv_amd import sgmv
+    p = FACT["decode7b"]()
+    dp = _upload(p)
+    ws = sgmv.make_workspace(p.n, p.h_in, 16, dp.x.device)
+    outs = [dp.lora_add_pool(workspace=ws) for _ in range(5)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    assert int(ws[:32768].view(torch.int32).abs().sum().item()) == 0  # flag and counters at zero
+    # the table path on the same workspace agrees within tolerance
+    y2 = dp.lora_add(workspace=ws)
+    torch.cuda.synchronize()
+    _assert_close(oracle.decode(_storage(y2, "f16"), "f16"),
+                  oracle.decode(_storage(outs[0], "f16"), "f16"), "pool vs table path")
+
+
+def test_pool_hip_graph_replay(torch_cuda):
+    """Capture several calls (different ids and y buffers) in one HIP graph and replay it
+    a few times, with eager work between replays; every replay must match eager."""
+    torch = torch_cuda
+    from adapter_gemv_amd import sgmv
+    p = FACT["decode7b"]()
+    dp = _upload(p)
+    ws = sgmv.make_workspace(p.n, p.h_in, 16, dp.x.device)
+    rng = np.random.default_rng(5)
+    id_sets = [torch.as_tensor(rng.permutation(32).astype(np.int32), device="cuda") for _ in range(3)]
+    ys = [dp.fresh_y() for _ in range(3)]
+    # eager reference of one pass over the three calls
+    ref = [dp.fresh_y() for _ in range(3)]
+    for k in range(3):
+        sgmv.lora_add_pool(ref[k], dp.x, id_sets[k], dp.A, dp.B, p.scale, ws)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                       # warm the capture stream
+        for k in range(3):
+            sgmv.lora_add_pool(dp.fresh_y(), dp.x, id_sets[k], dp.A, dp.B, p.scale, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k in range(3):
+            sgmv.lora_add_pool(ys[k], dp.x, id_sets[k], dp.A, dp.B, p.scale, ws)
+    for rep in range(3):
+        for k in range(3):
+            ys[k].copy_(dp.y0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in range(3):
+            assert torch.equal(ys[k], ref[k]), f"replay {rep} call {k}"
+        _ = (dp.x.float() * 2).sum()                 # eager work between replays
+        torch.cuda.synchronize()
+    assert int(ws[:32768].view(torch.int32).abs().sum().item()) == 0

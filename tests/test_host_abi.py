@@ -186,3 +186,37 @@ def _no_gpu_visible():
                     "addresses would reach a kernel")
 def test_valid_call_without_device_is_hip_error():
     assert _lora() == _lib.ERR_HIP
+
+
+def _pool(**kw):
+    a = dict(stream=None, dtype=0, y=Y, ld_y=4096, x=X, ld_x=4096, adapter_ids=TAB, n=32,
+             A_pool=V, A_stride=16 * 4096, B_pool=V + (1 << 30), B_stride=16 * 4096,
+             n_adapters=4096, h_in=4096, h_out=4096, r=16, scale=2.0, workspace=WS,
+             workspace_bytes=1 << 30)
+    a.update(kw)
+    return sgmv.sgmv_lora_add_pool(**a)
+
+
+POOL_REJECTS = [
+    ("n>64", dict(n=65), _lib.ERR_SHAPE),
+    ("rank", dict(r=8), _lib.ERR_UNSUPPORTED),
+    ("dtype", dict(dtype=7), _lib.ERR_UNSUPPORTED),
+    ("A_stride small", dict(A_stride=16 * 4096 - 8), _lib.ERR_SHAPE),
+    ("B_stride odd", dict(B_stride=16 * 4096 + 4), _lib.ERR_ALIGNMENT),
+    ("ids null", dict(adapter_ids=None), _lib.ERR_NULL),
+    ("pool misaligned", dict(A_pool=V + 8), _lib.ERR_ALIGNMENT),
+    ("no adapters", dict(n_adapters=0), _lib.ERR_SHAPE),
+    ("ws small", dict(workspace_bytes=1024), _lib.ERR_WORKSPACE),
+    ("alias", dict(y=X + 64), _lib.ERR_ALIAS),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", POOL_REJECTS, ids=[r[0] for r in POOL_REJECTS])
+def test_lora_add_pool_rejects(name, kw, code):
+    assert _pool(**kw) == code
+
+
+def test_build_segments_device_rejects():
+    L = _lib.lib()
+    assert L.sgmv_build_segments_device(None, TAB, 65, 4, V, V, V, V) == _lib.ERR_SHAPE
+    assert L.sgmv_build_segments_device(None, None, 3, 4, V, V, V, V) == _lib.ERR_NULL
