@@ -4,20 +4,23 @@
 //
 // Everything the Punica pages put in one SGMV call happens inside this one kernel
 // (paper summary on research.elamur.ai, "Summary" and "Interesting ideas" I1/I2):
-//   * the batch is sorted by adapter id into segments (every workgroup sorts the <= 64
-//     (id, row) keys of the batch in registers with a wavefront bitonic network --
-//     cheaper than a separate launch or a host round trip);
-//   * shrink items (segment, K chunk) compute float32 partial sums of v = x @ A[a] on
-//     MFMA 16x16x32 tiles and publish them with a release fence and a per-segment
-//     counter;
-//   * expand items (segment, column chunk) load their slice of B[a] and of y while
-//     the shrink runs, wait for the segment's counter, add the partial sums in a fixed
-//     order and write y = y + scale * v @ B[a] with one rounding.
+//   * grouping by adapter: every workgroup loads the batch's ids (one coalesced load)
+//     and finds the rows that share its adapter with one wavefront ballot -- the same
+//     row sets, in the same caller order, as the stable sort's segments;
+//   * shrink items (adapter rows within a block of 16 caller rows, K chunk) compute
+//     float32 partial sums of v = x @ A[a] on MFMA 16x16x32 tiles, publish them with
+//     agent-scope atomic stores and then bump a counter per produced row;
+//   * expand items (caller row, column chunk) load their slice of B[a] and of y while
+//     the shrink runs, wait for the row's counter, add the partial sums in a fixed order and
+//     write y = y + scale * v @ B[a] with one rounding.
 // Items are ordered shrink-first in the grid.  Workgroups are dispatched in index
 // order within each XCD, so every shrink item a waiting expand item depends on has
-// already been placed on a CU; shrink items never wait, hence the waits always end.
-// The last expand item of a segment resets its counter, leaving the workspace ready
-// for the next call without a memset (safe under HIP graph capture).
+// already been placed on a CU; shrink items never wait, hence the waits end (they are
+// also bounded, and flag the workspace if the bound is hit).  The last item of a row
+// resets its counter, leaving the workspace ready for the next call without a
+// memset (safe under HIP graph capture).  Counters live one per 256-byte line, so items
+// of different rows never contend for a cache line.  The device-side stable sort itself is
+// available as sgmv_build_segments_device.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -164,19 +167,6 @@ struct Leader {
   uint64_t rows;  // caller rows that use it
 };
 
-// The item's leader row i: returns false when row i is not the first row of a valid
-// adapter (the workgroup then has nothing to do).
-__device__ inline bool leader_of(const PoolArgs& p, int id_lane, int i, Leader* L) {
-  const int lane = threadIdx.x & 63;
-  const int a = __builtin_amdgcn_readlane(id_lane, i);
-  if (a < 0 || a >= p.n_adapters) return false;
-  const uint64_t rows = __ballot(lane < p.n && id_lane == a);
-  if (rows & ((1ull << i) - 1ull)) return false;  // an earlier row has the same adapter
-  L->a = a;
-  L->rows = rows;
-  return true;
-}
-
 __device__ inline void store_partial(float* q, float v) {
   __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -190,12 +180,12 @@ __device__ inline float load_partial(const float* q) {
 template <int R>
 constexpr int part_row() { return R < 32 ? 32 : R; }
 
-// shrink item: partial v over k in [kc*KC, (kc+1)*KC) for every row of the adapter.
-// MFMA 16x16x32 over blocks of 16 caller rows; lane l supplies MFMA row/column l%16
-// and the k group l/16, reading its own contiguous 8*U-element run of k for both
-// operands.  Row blocks without rows of this adapter are skipped.
+// shrink item: partial v over k in [kc*KC, (kc+1)*KC) for the adapter's rows within
+// one block of 16 caller rows (blk).  MFMA 16x16x32; lane l supplies MFMA row/column
+// l%16 and the k group l/16, reading its own contiguous 8*U-element run of k for both
+// operands.  Each produced row's counter is bumped once the partials are visible.
 template <int DT, int R>
-__device__ inline void shrink_item(const PoolArgs& p, const Leader& L, int i, int kc) {
+__device__ inline void shrink_item(const PoolArgs& p, const Leader& L, int blk, int kc) {
   using E = Elem<DT>;
   constexpr int U = 256 / R;
   constexpr int NB = R / 16;
@@ -214,9 +204,8 @@ __device__ inline void shrink_item(const PoolArgs& p, const Leader& L, int i, in
                                 : zero4();
     }
   const int64_t slice = static_cast<int64_t>(p.n) * part_row<R>();
-  for (int blk = 0; blk < 4; ++blk) {
+  {
     const uint32_t bm = static_cast<uint32_t>(L.rows >> (16 * blk)) & 0xffffu;
-    if (bm == 0) continue;  // uniform
     const int row = 16 * blk + mrow;
     const uint16_t* xr = ((bm >> mrow) & 1u) ? p.x + static_cast<int64_t>(row) * p.ld_x : nullptr;
     uint4 xv[U];
@@ -243,11 +232,14 @@ __device__ inline void shrink_item(const PoolArgs& p, const Leader& L, int i, in
       }
     }
   }
-  // every partial store has completed (and is visible device-wide) before the count
+  // every partial store has completed (and is visible device-wide) before the counts;
+  // lane l < 16 counts row 16*blk + l
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(0);
-  if (lane == 0)
-    __hip_atomic_fetch_add(&p.counters[i * kCounterStride], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t bm = static_cast<uint32_t>(L.rows >> (16 * blk)) & 0xffffu;
+  if (lane < 16 && ((bm >> lane) & 1u))
+    __hip_atomic_fetch_add(&p.counters[(16 * blk + lane) * kCounterStride], 1, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // expand item: one caller row r and columns [nc*64*CPL, (nc+1)*64*CPL); lane owns
@@ -255,7 +247,7 @@ __device__ inline void shrink_item(const PoolArgs& p, const Leader& L, int i, in
 // B[a].  Keying expand items by row spreads an adapter with many rows over as many
 // wavefronts.  B and y are loaded (and B widened to float32) while the shrink runs.
 template <int DT, int R>
-__device__ inline void expand_item(const PoolArgs& p, const Leader& L, int i, int r, int nc) {
+__device__ inline void expand_item(const PoolArgs& p, const Leader& L, int r, int nc) {
   using E = Elem<DT>;
   constexpr int CPL = 128 / R;
   constexpr int YW = CPL / 2;
@@ -279,7 +271,7 @@ __device__ inline void expand_item(const PoolArgs& p, const Leader& L, int i, in
 
   if (lane == 0) {
     int spins = 0;
-    while (__hip_atomic_load(&p.counters[i * kCounterStride], __ATOMIC_RELAXED,
+    while (__hip_atomic_load(&p.counters[r * kCounterStride], __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT) < p.KS) {
       __builtin_amdgcn_s_sleep(1);
       if (++spins > kSpinLimit) {
@@ -332,17 +324,18 @@ __device__ inline void expand_item(const PoolArgs& p, const Leader& L, int i, in
     store_words<YW>(yrow, packed);
   }
 
-  // the last of the adapter's KS + m * NS items leaves its counter at zero for the next call
+  // row r's counter sees KS shrink counts and NS expand counts; the last one leaves it
+  // at zero for the next call
   if (lane == 0) {
-    int* c = &p.counters[i * kCounterStride];
-    const int m = __popcll(L.rows);
+    int* c = &p.counters[r * kCounterStride];
     const int old = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == p.KS + m * p.NS - 1) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == p.KS + p.NS - 1) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// Grid: n * KS shrink items (leader row i = b % n, chunk b / n), then n * NS expand
-// items (caller row r = e % n, column chunk e / n).  Every shrink item an expand item
+// Grid: n * KS shrink items (caller row r = b % n, chunk b / n; active when r is the
+// first row of its adapter within its block of 16 rows), then n * NS expand items
+// (caller row r = e % n, column chunk e / n).  Every shrink item an expand item
 // waits for has a lower index.
 template <int DT, int R>
 __global__ __launch_bounds__(64) void lora_add_pool_kernel(PoolArgs p) {
@@ -356,8 +349,16 @@ __global__ __launch_bounds__(64) void lora_add_pool_kernel(PoolArgs p) {
   }
   Leader L;
   if (b < n_shrink) {
-    const int i = b % p.n, kc = b / p.n;
-    if (leader_of(p, id, i, &L)) shrink_item<DT, R>(p, L, i, kc);
+    // item (row r, chunk kc) works iff r is its adapter's first row within r's block
+    const int r = b % p.n, kc = b / p.n;
+    const int a = __builtin_amdgcn_readlane(id, r);
+    if (a < 0 || a >= p.n_adapters) return;
+    L.a = a;
+    L.rows = __ballot(lane < p.n && id == a);
+    const int blk = r >> 4;
+    const uint32_t bm = static_cast<uint32_t>(L.rows >> (16 * blk)) & 0xffffu;
+    if (bm & ((1u << (r & 15)) - 1u)) return;
+    shrink_item<DT, R>(p, L, blk, kc);
   } else {
     const int e = b - n_shrink;
     const int r = e % p.n, nc = e / p.n;
@@ -365,8 +366,7 @@ __global__ __launch_bounds__(64) void lora_add_pool_kernel(PoolArgs p) {
     if (a < 0 || a >= p.n_adapters) return;
     L.a = a;
     L.rows = __ballot(lane < p.n && id == a);
-    const int i = __ffsll(static_cast<long long>(L.rows)) - 1;  // the adapter's leader row
-    expand_item<DT, R>(p, L, i, r, nc);
+    expand_item<DT, R>(p, L, r, nc);
   }
 }
 

@@ -16,8 +16,9 @@ together spanning more than 1 GiB, so each step reads its operands from HBM and 
 the 256 MB Infinity Cache (cache-cold by construction).
 
 Printed: one JSON line with the whole-step throughput (algorithmic bytes per step over
-the wall time of K steps), the per-call duration of sgmv_lora_add from HIP events
-recorded on its stream during the timed steps (the roofline figure), and the fp64 CPU
+the wall time of K steps), the average duration of the SGMV kernel(s) of one call from
+HIP events on their stream (the roofline figure: over the timed graph replay on the
+one-launch path, over a graph of the same calls on the table path), and the fp64 CPU
 oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -214,6 +215,53 @@ class Rig:
         self.ring_evt[i] = e
 
 
+def kernel_pass(rig, k0: int, count: int) -> float:
+    """Average duration of sgmv_lora_add alone on the table path: the segment tables of
+    `count` steps are built and uploaded first, the calls are captured in one HIP graph
+    and the replay is bracketed by HIP events."""
+    import torch
+    from adapter_gemv_amd import sgmv
+    p = rig.p
+    calls = []
+    keep = []
+    for k in range(count):
+        slot = (k0 + k) % rig.slots
+        b = sgmv.Batch.build(rig.ids[slot], rig.A, rig.B)
+        keep.append(b)
+        calls.append((slot, b))
+    torch.cuda.synchronize()
+
+    def run():
+        st = torch.cuda.current_stream()
+        for slot, b in calls:
+            t = b.table
+            rc = sgmv.sgmv_lora_add(st.cuda_stream, rig.dtype_code, rig.y[slot].data_ptr(),
+                                    rig.ld_y, rig.x[slot].data_ptr(), rig.ld_x, b.A_ptrs_addr,
+                                    b.B_ptrs_addr, b.seg_starts_addr, b.perm_addr, t.n,
+                                    t.n_segments, t.min_seg_len, t.max_seg_len, p.h_in, p.h_out,
+                                    p.r, p.scale, rig.ws.data_ptr(), rig.ws.numel())
+            if rc != 0:
+                raise RuntimeError(sgmv.sgmv_status_string(rc))
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / count
+
+
 def parity_check(rig):
     """Run slot 0 (the seeded problem) once from its initial y and compare to the oracle."""
     import torch
@@ -233,17 +281,23 @@ def parity_check(rig):
             "ok": bool(np.all(err <= tol)) and flag == 0, "workspace_flag": flag}
 
 
-def load_traffic(workload: str):
-    """HBM bytes per call from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"sgmv_lora_add_{workload}_counters.json")
+def load_traffic(workload: str, pool_path: bool):
+    """HBM bytes per call from the committed rocprofv3 counter summary (FETCH_SIZE and
+    WRITE_SIZE scaled by a plain copy of known size), if it was taken on the current
+    kernel source; otherwise None."""
+    kernel = "lora_add_pool_kernel" if pool_path else "sgmv_lora_add"
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
+    rec = {}
     with open(path) as f:
-        rec = json.load(f)
+        for line in f:
+            if ":" in line and not line.startswith(("#", "rocprofv3", "`")):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.split()[0] if v.split() else ""
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return rec.get("hbm_bytes_per_call")
+    return int(float(rec["hbm_bytes_per_call"]))
 
 
 def main(argv=None) -> int:
@@ -318,35 +372,30 @@ def main(argv=None) -> int:
         t_ev[1].record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        call_ev = None
     else:
-        call_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(args.steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         t_ev[0].record(stream)
         for k in range(args.steps):
-            rig.step(base + k, call_ev[k])
+            rig.step(base + k)
         t_ev[1].record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     wall = (t1 - t0) / args.steps
     gpu_step = t_ev[0].elapsed_time(t_ev[1]) * 1e-3 / args.steps
-    if call_ev is None:
-        # per-call kernel time: eager calls, each bracketed by events (untimed pass)
-        n_iso = min(args.steps, 500)
-        call_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(n_iso)]
-        for k in range(n_iso):
-            rig.step(base + args.steps + k, call_ev[k])
-        torch.cuda.synchronize()
-    call_ms = np.array([a.elapsed_time(b) for a, b in call_ev])
-    call_s = float(call_ms.mean()) * 1e-3
+    if use_graph:
+        # each step is one kernel, replayed back to back: the events over the timed
+        # region give the kernel's average duration
+        call_s = gpu_step
+        call_how = "HIP events over the timed graph replay / K"
+    else:
+        call_s = kernel_pass(rig, base + args.steps, min(args.steps, 500))
+        call_how = "HIP events over a graph of the same calls (tables pre-uploaded) / count"
     flag = int(rig.ws[:4].view(torch.int32).item())
 
     nbytes = algorithmic_bytes(p)
     flops = algorithmic_flops(p)
-    traffic = load_traffic(args.workload)
+    traffic = load_traffic(args.workload, rig.pool_path)
     kernel = ("lora_add_pool_kernel (one launch per call)" if rig.pool_path else
               "sgmv_lora_add table path (all kernels of one call)")
     out = {
@@ -374,8 +423,7 @@ def main(argv=None) -> int:
         },
         "us_per_step_gpu": round(gpu_step * 1e6, 3),
         "us_per_call": round(call_s * 1e6, 3),
-        "us_per_call_p10_p50_p90": [round(float(np.percentile(call_ms, q)) * 1e3, 3)
-                                    for q in (10, 50, 90)],
+        "us_per_call_how": call_how,
         "algorithmic_bytes_per_call": nbytes,
         "gflops_per_s": round(flops / call_s / 1e9, 2),
         "roofline": {
