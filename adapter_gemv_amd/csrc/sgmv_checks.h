@@ -53,4 +53,50 @@ inline int check_device() {
   return SGMV_OK;
 }
 
+// ------------------------------------------------------------------------------------
+// workspace layout shared by every entry point (the same bytes serve both paths):
+//   [0, 4)                  int32 flag (decode path: 1 = a wait timed out, 2 = bad id)
+//   [256, 16640)            decode path: one counter per row, one per 256-byte line
+//   [tile_cnt_off, ...)     table path: one counter per 16-row tile, one per 256-byte line
+//   [rowks_off, ...)        table path: split-K slice count of each sorted row
+//   [v_off, ...)            table path: final float32 v of rows of long segments
+//   [part_off, total)       float32 split-K partial sums (either path)
+// Counters are zero before a call and are left at zero by it.
+// ------------------------------------------------------------------------------------
+constexpr int kMaxPoolRows = 64;
+constexpr size_t kWsPoolCounters = 256;
+constexpr int kCounterInts = 64;  // 256 bytes per counter
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// split-K chunk (elements of h_in) of the table path's GEMV shrink and of the decode path
+inline int table_gemv_kc(int r) { return r == 16 ? 512 : 256; }
+inline int pool_kc(int r) { return 8192 / r; }
+inline int pool_part_row(int r) { return r < 32 ? 32 : r; }
+
+struct WsLayout {
+  size_t tile_cnt_off, rowks_off, v_off, part_off, total;
+  int64_t slice;  // floats per split-K slice of the table path (n * r)
+  int ks_max;     // table path: slices of the GEMV shrink (>= those of the MFMA shrink)
+};
+
+inline WsLayout ws_layout(int32_t n, int32_t h_in, int32_t r) {
+  WsLayout L{};
+  const size_t tiles = static_cast<size_t>((n + 15) / 16);
+  L.ks_max = (h_in + table_gemv_kc(r) - 1) / table_gemv_kc(r);
+  L.slice = static_cast<int64_t>(n) * r;
+  L.tile_cnt_off = kWsPoolCounters + sizeof(int32_t) * kCounterInts * kMaxPoolRows;
+  L.rowks_off = L.tile_cnt_off + sizeof(int32_t) * kCounterInts * tiles;
+  L.v_off = align_up(L.rowks_off + sizeof(int32_t) * static_cast<size_t>(n), 256);
+  L.part_off = align_up(L.v_off + sizeof(float) * static_cast<size_t>(L.slice), 256);
+  size_t part = sizeof(float) * static_cast<size_t>(L.slice) * L.ks_max;
+  if (n <= kMaxPoolRows) {
+    const size_t ksp = static_cast<size_t>((h_in + pool_kc(r) - 1) / pool_kc(r));
+    const size_t pool = sizeof(float) * ksp * static_cast<size_t>(n) * pool_part_row(r);
+    if (pool > part) part = pool;
+  }
+  L.total = L.part_off + part;
+  return L;
+}
+
 }  // namespace sgmv_host

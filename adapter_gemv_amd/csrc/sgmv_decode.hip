@@ -34,10 +34,8 @@ namespace {
 using namespace sgmv_dev;
 using namespace sgmv_host;
 
-constexpr int kPoolMaxN = 64;            // tokens per call on this path (one wavefront)
-constexpr int kWsCounters = 256;         // byte offset of the per-leader counters
-constexpr int kCounterStride = 64;       // ints: one counter per 256-byte line (no sharing)
-constexpr int kWsPartials = 32768;       // byte offset of the split-K partial sums
+constexpr int kPoolMaxN = kMaxPoolRows;  // tokens per call on this path (one wavefront)
+constexpr int kCounterStride = kCounterInts;  // one counter per 256-byte line (no sharing)
 constexpr int kSpinLimit = 1 << 22;      // bounded wait (about 0.1 s), then flag and exit
 constexpr uint32_t kNoKey = 0xffffffffu;
 
@@ -179,6 +177,7 @@ __device__ inline float load_partial(const float* q) {
 // never write into one line
 template <int R>
 constexpr int part_row() { return R < 32 ? 32 : R; }
+static_assert(part_row<16>() == 32 && part_row<64>() == 64, "matches pool_part_row");
 
 // shrink item: partial v over k in [kc*KC, (kc+1)*KC) for the adapter's rows within
 // one block of 16 caller rows (blk).  MFMA 16x16x32; lane l supplies MFMA row/column
@@ -370,8 +369,6 @@ __global__ __launch_bounds__(64) void lora_add_pool_kernel(PoolArgs p) {
   }
 }
 
-inline int pool_kc(int r) { return 8192 / r; }
-
 template <int DT, int R>
 hipError_t launch_pool(hipStream_t st, const PoolArgs& p) {
   const int grid = p.n * (p.KS + p.NS);
@@ -380,14 +377,6 @@ hipError_t launch_pool(hipStream_t st, const PoolArgs& p) {
 }
 
 }  // namespace
-
-// bytes the decode path needs in the workspace (the table path's own need is larger or
-// equal for r <= 32; sgmv_workspace_bytes returns the maximum of both)
-extern "C" size_t sgmv_pool_workspace_bytes_internal(int32_t n, int32_t h_in, int32_t r) {
-  const int ks = (h_in + pool_kc(r) - 1) / pool_kc(r);
-  const int pr = r < 32 ? 32 : r;
-  return kWsPartials + sizeof(float) * static_cast<size_t>(ks) * n * pr;
-}
 
 extern "C" int sgmv_build_segments_device(hipStream_t stream, const int32_t* adapter_ids,
                                           int32_t n, int32_t n_adapters, int32_t* perm,
@@ -448,8 +437,9 @@ extern "C" int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, in
   p.scale = scale;
   char* ws = static_cast<char*>(workspace);
   p.ws_flag = reinterpret_cast<int32_t*>(ws);
-  p.counters = reinterpret_cast<int32_t*>(ws + kWsCounters);
-  p.part = reinterpret_cast<float*>(ws + kWsPartials);
+  const WsLayout L = ws_layout(n, h_in, r);
+  p.counters = reinterpret_cast<int32_t*>(ws + kWsPoolCounters);
+  p.part = reinterpret_cast<float*>(ws + L.part_off);
 
   hipError_t e;
   if (dtype == SGMV_F16) {
