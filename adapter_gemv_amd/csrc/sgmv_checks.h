@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
+#include <algorithm>
 #include <cstdint>
 
 #include "../../include/sgmv.h"
@@ -77,13 +78,15 @@ inline int pool_part_row(int r) { return r < 32 ? 32 : r; }
 struct WsLayout {
   size_t tile_cnt_off, rowks_off, v_off, part_off, total;
   int64_t slice;  // floats per split-K slice of the table path (n * r)
-  int ks_max;     // table path: slices of the GEMV shrink (>= those of the MFMA shrink)
+  int ks_max;     // table path: split-K slices the partial-sum area holds
 };
 
 inline WsLayout ws_layout(int32_t n, int32_t h_in, int32_t r) {
   WsLayout L{};
   const size_t tiles = static_cast<size_t>((n + 15) / 16);
   L.ks_max = (h_in + table_gemv_kc(r) - 1) / table_gemv_kc(r);
+  const int ks_mfma = std::min(32, std::max(1, h_in / 256));  // MFMA shrink slices, at most
+  if (ks_mfma > L.ks_max) L.ks_max = ks_mfma;
   L.slice = static_cast<int64_t>(n) * r;
   L.tile_cnt_off = kWsPoolCounters + sizeof(int32_t) * kCounterInts * kMaxPoolRows;
   L.rowks_off = L.tile_cnt_off + sizeof(int32_t) * kCounterInts * tiles;

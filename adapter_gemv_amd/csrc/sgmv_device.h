@@ -13,6 +13,8 @@ namespace sgmv_dev {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
 // ------------------------------------------------------------------------------------
 // element helpers: 16-bit values travel packed two per 32-bit word
@@ -54,7 +56,23 @@ struct Elem<SGMV_BF16> {
   }
 };
 
+// Global-memory pointers.  A pointer read out of a device table (the per-segment weight
+// pointers) or kept in a private array is generic to the compiler, which then emits flat
+// accesses; those count against both the vector-memory and the LDS/scalar wait counters,
+// so every wait on them drains all loads in flight.  Casting to address space 1 keeps
+// them global loads with exact wait counts.
+template <typename T>
+using gptr = T __attribute__((address_space(1)))*;
+template <typename T>
+__device__ inline gptr<const T> global_ptr(const T* p) { return (gptr<const T>)p; }
+template <typename T>
+__device__ inline gptr<T> global_ptr(T* p) { return (gptr<T>)p; }
+
 __device__ inline uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ inline uint4 ld16(gptr<const uint16_t> p) {
+  const u32x4_t v = *(gptr<const u32x4_t>)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ inline uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
 // NW consecutive 32-bit words at p (p aligned to 4*NW bytes), as one vector access
@@ -79,6 +97,30 @@ __device__ inline void store_words(uint16_t* p, const uint32_t* in) {
     *reinterpret_cast<uint2*>(p) = make_uint2(in[0], in[1]);
   } else {
     *reinterpret_cast<uint32_t*>(p) = in[0];
+  }
+}
+
+template <int NW>
+__device__ inline void load_words(gptr<const uint16_t> p, uint32_t* out) {
+  if constexpr (NW == 4) {
+    const u32x4_t v = *(gptr<const u32x4_t>)p;
+    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+  } else if constexpr (NW == 2) {
+    const u32x2_t v = *(gptr<const u32x2_t>)p;
+    out[0] = v.x; out[1] = v.y;
+  } else {
+    out[0] = *(gptr<const uint32_t>)p;
+  }
+}
+
+template <int NW>
+__device__ inline void store_words(gptr<uint16_t> p, const uint32_t* in) {
+  if constexpr (NW == 4) {
+    *(gptr<u32x4_t>)p = u32x4_t{in[0], in[1], in[2], in[3]};
+  } else if constexpr (NW == 2) {
+    *(gptr<u32x2_t>)p = u32x2_t{in[0], in[1]};
+  } else {
+    *(gptr<uint32_t>)p = in[0];
   }
 }
 

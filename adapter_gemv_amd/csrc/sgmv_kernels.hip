@@ -11,7 +11,7 @@
 // products and is bound by reading A and B; it uses wavefront-reduction ("GEMV")
 // kernels with one workgroup per (segment, K chunk) and per (segment, column
 // chunk).  Longer segments (prefill) are dense contractions and go through MFMA
-// tiles over 16 sorted rows.  v = x @ A is kept in float32: the shrink kernels write
+// tiles of sorted rows.  v = x @ A is kept in float32: the shrink kernels write
 // split-K partial sums to the workspace and the expand kernels add the slices in a
 // fixed order, so results are reproducible run to run (no float atomics).
 #include <hip/hip_runtime.h>
@@ -29,7 +29,6 @@ using namespace sgmv_dev;
 using namespace sgmv_host;
 
 constexpr int kLongMin = 16;   // segments with at least this many rows use MFMA tiles
-constexpr int kTileRows = 16;  // sorted rows per tile on the long-segment path
 constexpr int kShortMax = kLongMin - 1;
 
 // ------------------------------------------------------------------------------------
@@ -62,7 +61,7 @@ __global__ __launch_bounds__(256) void shrink_gemv_kernel(
   const int j = lane % R, g = lane / R;
   const int kbase = kc * C::KC + w * C::WAVE_K + g * 8 * C::KV;
 
-  const uint16_t* Arow = A_ptrs[s] + static_cast<int64_t>(j) * h_in;
+  const gptr<const uint16_t> Arow = global_ptr(A_ptrs[s]) + static_cast<int64_t>(j) * h_in;
   uint4 a[C::KV];
 #pragma unroll
   for (int v = 0; v < C::KV; ++v) {
@@ -74,8 +73,8 @@ __global__ __launch_bounds__(256) void shrink_gemv_kernel(
 #pragma unroll
     for (int r = 0; r < C::MR; ++r) {
       const int i = i0 + r;
-      const uint16_t* xr = nullptr;
-      if (i < m) xr = x + static_cast<int64_t>(perm ? perm[seg0 + i] : seg0 + i) * ld_x;
+      gptr<const uint16_t> xr = nullptr;
+      if (i < m) xr = global_ptr(x) + static_cast<int64_t>(perm ? perm[seg0 + i] : seg0 + i) * ld_x;
 #pragma unroll
       for (int v = 0; v < C::KV; ++v) {
         const int k = kbase + 8 * v;
@@ -123,16 +122,16 @@ __global__ __launch_bounds__(64) void expand_gemv_kernel(
   const bool cin = c0 < h_out;
 
   uint4 b[NV];
-  const uint16_t* Bblk = B_ptrs[s] + static_cast<int64_t>(c0) * R;
+  const gptr<const uint16_t> Bblk = global_ptr(B_ptrs[s]) + static_cast<int64_t>(c0) * R;
 #pragma unroll
   for (int v = 0; v < NV; ++v) b[v] = cin ? ld16(Bblk + 8 * v) : zero4();
 
   uint32_t yv[kShortMax][YW];
-  uint16_t* yrow[kShortMax];
+  gptr<uint16_t> yrow[kShortMax];
 #pragma unroll
   for (int i = 0; i < kShortMax; ++i) {
     yrow[i] = nullptr;
-    if (i < m) yrow[i] = y + static_cast<int64_t>(perm ? perm[seg0 + i] : seg0 + i) * ld_y + c0;
+    if (i < m) yrow[i] = global_ptr(y) + static_cast<int64_t>(perm ? perm[seg0 + i] : seg0 + i) * ld_y + c0;
 #pragma unroll
     for (int q = 0; q < YW; ++q) yv[i][q] = 0u;
     if (i < m && cin) load_words<YW>(yrow[i], yv[i]);
@@ -180,208 +179,223 @@ __device__ inline float load_coherent(const float* q) {
   return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Segments that cover the sorted rows [r0, r1) (at most 32 rows), found in one parallel
-// pass over seg_starts: the segment of row r0, the rows inside the tile where a new
-// segment starts, and the nearest segment starts on either side.
+// Long segments overlapping the sorted rows [g0, g1) of a tile (at most ROWS rows), found
+// in one parallel pass over seg_starts: sh.rseg[q] = segment of row g0 + q if that segment
+// has at least kLongMin rows, else -1.  Returns the number of such segments (uniform).
+// A tile of ROWS rows meets at most ROWS / kLongMin + 2 long segments.
+template <int ROWS>
 struct TileSegs {
-  int seg0;        // segment of row r0
-  uint32_t bound;  // bit q (q >= 1): a segment starts at row r0 + q
-  int prev;        // first row of segment seg0
-  int next;        // first segment start >= r1 (n if none)
+  static constexpr int kMax = ROWS / kLongMin + 2;
+  int nseg;
+  int seg[kMax], st[kMax], en[kMax];
+  int rseg[ROWS];
 };
 
-struct TileSegsLds {
-  int count, prev, next;
-  unsigned bound;
-};
-
-__device__ inline TileSegs tile_segments(const int32_t* __restrict__ seg_starts, int S, int n,
-                                         int r0, int r1, TileSegsLds* sh) {
-  if (threadIdx.x == 0) {
-    sh->count = 0;
-    sh->prev = 0;
-    sh->next = n;
-    sh->bound = 0u;
-  }
+template <int ROWS, int THREADS>
+__device__ inline int tile_long_segments(const int32_t* __restrict__ seg_starts, int S, int g0,
+                                         int g1, TileSegs<ROWS>& sh) {
+  const int tid = threadIdx.x;
+  if (tid == 0) sh.nseg = 0;
   __syncthreads();
-  for (int s = 1 + static_cast<int>(threadIdx.x); s <= S; s += blockDim.x) {
-    const int st = seg_starts[s];
-    if (st <= r0) {
-      atomicAdd(&sh->count, 1);
-      atomicMax(&sh->prev, st);
-    } else if (st < r1) {
-      atomicOr(&sh->bound, 1u << (st - r0));
-    } else {
-      atomicMin(&sh->next, st);
+  for (int s = tid; s < S; s += THREADS) {
+    const int st = seg_starts[s], en = seg_starts[s + 1];
+    if (en - st >= kLongMin && st < g1 && en > g0) {
+      const int k = atomicAdd(&sh.nseg, 1);
+      if (k < TileSegs<ROWS>::kMax) {
+        sh.seg[k] = s;
+        sh.st[k] = st;
+        sh.en[k] = en;
+      }
     }
   }
   __syncthreads();
-  TileSegs t;
-  t.seg0 = sh->count;
-  t.bound = sh->bound;
-  t.prev = sh->prev;
-  t.next = sh->next;
-  return t;
-}
-
-// Run k of a tile: rows [lo, hi) of segment seg; `len` is the segment's full length.
-struct Run {
-  int seg, lo, hi, len;
-};
-
-// Iterates the runs of a tile in order; uniform across the block.
-struct RunIter {
-  TileSegs T;
-  int r0, r1;
-  int seg, lo, start;
-  __device__ RunIter(const TileSegs& t, int r0_, int r1_)
-      : T(t), r0(r0_), r1(r1_), seg(t.seg0), lo(r0_), start(t.prev) {}
-  __device__ bool next(Run* run) {
-    if (lo >= r1) return false;
-    const uint32_t later = (lo - r0 + 1 < 32) ? (T.bound >> (lo - r0 + 1)) : 0u;
-    const int hi = later ? lo + 1 + (__ffs(later) - 1) : r1;
-    const int end = later ? hi : T.next;  // first row after the segment
-    run->seg = seg;
-    run->lo = lo;
-    run->hi = hi;
-    run->len = end - start;
-    ++seg;
-    start = hi;
-    lo = hi;
-    return true;
+  const int nseg = min(sh.nseg, TileSegs<ROWS>::kMax);
+  for (int q = tid; q < ROWS; q += THREADS) {
+    const int row = g0 + q;
+    int sg = -1;
+    for (int k = 0; k < nseg; ++k)
+      if (sh.st[k] <= row && row < sh.en[k]) sg = sh.seg[k];
+    sh.rseg[q] = sg;
   }
-};
-
-// rows of long segments inside the tile (bit q: row r0 + q)
-__device__ inline uint32_t long_rows(const TileSegs& T, int r0, int r1) {
-  uint32_t mask = 0;
-  RunIter it(T, r0, r1);
-  Run run;
-  while (it.next(&run))
-    if (run.len >= kLongMin) {
-      const int w = run.hi - run.lo;
-      mask |= ((w >= 32) ? 0xffffffffu : ((1u << w) - 1u)) << (run.lo - r0);
-    }
-  return mask;
+  __syncthreads();
+  return nseg;
 }
 
-// Shrink on MFMA 16x16x32 for a tile of 16 sorted rows and a K chunk, with 16 waves per
-// workgroup.  The x tile is the A operand and the adapter's stored A rows the B operand;
-// lane l supplies row/column l%16 and k = k0 + 8*(l/16) .. +7 of each 32-wide k step, so
-// the four lanes of a row read 64 contiguous bytes per load.  The chunk is cut into
-// stages of 2048/r k dealt round-robin to the waves; each wave keeps the loads of its next
-// stage in flight while it multiplies the current one.  The 16 wave results are added
-// in a fixed order through LDS.  With one chunk per tile v is written directly;
-// otherwise chunks go out as agent-scope atomic stores and the last chunk of the tile
-// (per a counter on its own cache line) adds them in order, writes v and resets the
-// counter.
+// Next long segment of a tile at or after row q (rows are in segment order); returns -1
+// when there is none and leaves q after the segment's last row in the tile.
+template <int ROWS>
+__device__ inline int next_run(const TileSegs<ROWS>& sh, int& q) {
+  while (q < ROWS && sh.rseg[q] < 0) ++q;
+  if (q >= ROWS) return -1;
+  const int sg = sh.rseg[q];
+  while (q < ROWS && sh.rseg[q] == sg) ++q;
+  return sg;
+}
+
+// Shrink on MFMA 16x16x32 for a tile of 64 sorted rows and one K chunk.  The x rows are
+// the A operand and the adapter's stored A rows the B operand; lane l supplies row (or
+// column) l%16 and k = k0 + 8*(l/16) .. +7 of each 32-wide k step.  Each of the 4 waves
+// covers all 64 rows and R columns (4 x R/16 accumulator blocks), so A is read once per
+// 64 rows; the waves take interleaved stages of UN k steps, with the loads of the next
+// stage in flight while the current one is multiplied, and are summed through LDS in a
+// fixed order.  Rows of several long segments in one tile are handled run by run with the
+// other rows' x set to zero.  With one chunk per tile v is written directly; otherwise the
+// chunks go out as agent-scope atomic stores and the last chunk of the tile (per a
+// counter on its own cache line) adds them in order, writes v and resets the counter.
+//
+// With a multiple of 8 chunks, workgroup b (on XCD b % 8) takes chunks = b mod 8, so each
+// XCD's L2 keeps one eighth of the K range of the adapters' A.
+constexpr int kShrRows = 64;
+constexpr int kXcds = 8;
+
 template <int R>
-struct ShrinkMfmaCfg {
-  static constexpr int NB = R / 16;
-  static constexpr int UN = 64 / R;         // MFMA k-steps per stage (4 loads of A per lane)
-  static constexpr int STAGE = 32 * UN;     // k per stage
-  static constexpr int WAVES = 16;
+struct ShrCfg {
+  static constexpr int NB = R / 16;                 // column blocks of v
+  static constexpr int RB = kShrRows / 16;          // row blocks
+  static constexpr int UN = (R == 16) ? 2 : 1;      // k steps per stage
+  static constexpr int STAGE = 32 * UN;             // k per stage
+  static constexpr int WAVES_PER_SIMD = (R == 64) ? 2 : 3;
 };
 
+// Loads of one stage.  They are unconditional (out-of-range k reads offset 0 of the same
+// row, rows outside the current run read a row that exists) so that the compiler can count
+// them exactly and keep the next stage in flight; shr_mul zeroes what does not belong.
 template <int DT, int R>
-__device__ inline void mfma_stage_load(const uint16_t* xr, const uint16_t* A, int h_in, int k0,
-                                       int k_end, int mrow, int kq, uint4 (&xv)[ShrinkMfmaCfg<R>::UN],
-                                       uint4 (&av)[R / 16][ShrinkMfmaCfg<R>::UN]) {
-  constexpr int UN = ShrinkMfmaCfg<R>::UN;
+__device__ inline void shr_load(const gptr<const uint16_t> (&xr)[ShrCfg<R>::RB],
+                                const gptr<const uint16_t> (&ar)[ShrCfg<R>::NB], int k0, int k_hi, int kq,
+                                uint4 (&xv)[ShrCfg<R>::UN][ShrCfg<R>::RB],
+                                uint4 (&av)[ShrCfg<R>::UN][ShrCfg<R>::NB]) {
+  using C = ShrCfg<R>;
 #pragma unroll
-  for (int u = 0; u < UN; ++u) {
+  for (int u = 0; u < C::UN; ++u) {
     const int kk = k0 + 32 * u + 8 * kq;
-    const bool in = kk < k_end;
-    xv[u] = (in && xr) ? ld16(xr + kk) : zero4();
+    const int off = (kk < k_hi) ? kk : 0;
 #pragma unroll
-    for (int nb = 0; nb < R / 16; ++nb)
-      av[nb][u] = in ? ld16(A + static_cast<int64_t>(nb * 16 + mrow) * h_in + kk) : zero4();
+    for (int rb = 0; rb < C::RB; ++rb) xv[u][rb] = ld16(xr[rb] + off);
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) av[u][nb] = ld16(ar[nb] + off);
   }
 }
 
 template <int DT, int R>
-__device__ inline void mfma_stage_mul(const uint4 (&xv)[ShrinkMfmaCfg<R>::UN],
-                                      const uint4 (&av)[R / 16][ShrinkMfmaCfg<R>::UN],
-                                      f32x4_t (&acc)[R / 16]) {
+__device__ inline void shr_mul(const uint4 (&xv)[ShrCfg<R>::UN][ShrCfg<R>::RB],
+                               const uint4 (&av)[ShrCfg<R>::UN][ShrCfg<R>::NB], int k0, int k_hi,
+                               int kq, const bool (&xin)[ShrCfg<R>::RB],
+                               f32x4_t (&acc)[ShrCfg<R>::RB][ShrCfg<R>::NB]) {
+  using C = ShrCfg<R>;
 #pragma unroll
-  for (int u = 0; u < ShrinkMfmaCfg<R>::UN; ++u)
+  for (int u = 0; u < C::UN; ++u) {
+    const bool in = k0 + 32 * u + 8 * kq < k_hi;
+    uint4 a[C::NB];
 #pragma unroll
-    for (int nb = 0; nb < R / 16; ++nb) acc[nb] = Elem<DT>::mfma(xv[u], av[nb][u], acc[nb]);
+    for (int nb = 0; nb < C::NB; ++nb) a[nb] = in ? av[u][nb] : zero4();
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb) {
+      const uint4 xa = (in && xin[rb]) ? xv[u][rb] : zero4();
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) acc[rb][nb] = Elem<DT>::mfma(xa, a[nb], acc[rb][nb]);
+    }
+  }
 }
 
 template <int DT, int R>
-__global__ __launch_bounds__(1024) void shrink_mfma_kernel(
+__global__ __launch_bounds__(256, ShrCfg<R>::WAVES_PER_SIMD) void shrink_mfma_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, const uint16_t* const* __restrict__ A_ptrs,
     const int32_t* __restrict__ seg_starts, int32_t S, const int32_t* __restrict__ perm, int32_t n,
-    int32_t h_in, int32_t kcm, float* __restrict__ part, int64_t slice, int32_t* __restrict__ tile_cnt,
-    float* __restrict__ v_out, int32_t* __restrict__ rowks, int32_t ks) {
-  using C = ShrinkMfmaCfg<R>;
-  constexpr int NB = C::NB, UN = C::UN, STAGE = C::STAGE, WAVES = C::WAVES;
-  __shared__ TileSegsLds s_segs;
+    int32_t h_in, int32_t kcm, int32_t ks, float* __restrict__ part, int64_t slice,
+    int32_t* __restrict__ tile_cnt, float* __restrict__ v_out, int32_t* __restrict__ rowks) {
+  using C = ShrCfg<R>;
+  constexpr int NB = C::NB, RB = C::RB, UN = C::UN, STAGE = C::STAGE, MT = kShrRows;
+  __shared__ TileSegs<MT> sh;
+  __shared__ int s_prow[MT];
   __shared__ int s_last;
-  __shared__ f32x4_t red[WAVES / 2][NB][64];
-  const int r0 = blockIdx.x * kTileRows;
-  const int r1 = min(n, r0 + kTileRows);
-  const int kc = blockIdx.y;
+  __shared__ f32x4_t red[2][RB][NB][64];
+
+  const int b = blockIdx.x;
+  int tile, kc;
+  if (ks % kXcds == 0) {
+    const int m = ks / kXcds, j = b / kXcds;
+    tile = j / m;
+    kc = b % kXcds + kXcds * (j % m);
+  } else {
+    tile = b / ks;
+    kc = b % ks;
+  }
+  const int r0 = tile * MT;
+  const int r1 = min(n, r0 + MT);
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int mrow = lane & 15, kq = lane >> 4;
-  const int i = r0 + mrow;
-  const int prow = (i < r1) ? (perm ? perm[i] : i) : 0;  // issued with the segment pass
-  const TileSegs T = tile_segments(seg_starts, S, n, r0, r1, &s_segs);
-  const uint32_t lmask = long_rows(T, r0, r1);
-  if (lmask == 0) return;  // uniform: no row of a long segment here
+  if (tid < MT) s_prow[tid] = (r0 + tid < r1) ? (perm ? perm[r0 + tid] : r0 + tid) : 0;
+  if (tile_long_segments<MT, 256>(seg_starts, S, r0, r1, sh) == 0) return;  // uniform
   const int k_lo = kc * kcm;
   const int k_hi = min(h_in, k_lo + kcm);
   const int nst = (k_hi - k_lo + STAGE - 1) / STAGE;
 
-  RunIter it(T, r0, r1);
-  Run run;
-  while (it.next(&run)) {
-    if (run.len < kLongMin) continue;  // uniform across the block
-    const uint16_t* xr = (i >= run.lo && i < run.hi) ? x + static_cast<int64_t>(prow) * ld_x : nullptr;
-    const uint16_t* A = A_ptrs[run.seg];
-    f32x4_t acc[NB];
+  f32x4_t acc[RB][NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    uint4 x0[UN], a0[NB][UN], x1[UN], a1[NB][UN];
-    mfma_stage_load<DT, R>(xr, A, h_in, k_lo + w * STAGE, k_hi, mrow, kq, x0, a0);
-    for (int g = w; g < nst; g += 2 * WAVES) {
-      mfma_stage_load<DT, R>(xr, A, h_in, k_lo + (g + WAVES) * STAGE, k_hi, mrow, kq, x1, a1);
-      mfma_stage_mul<DT, R>(x0, a0, acc);
-      mfma_stage_load<DT, R>(xr, A, h_in, k_lo + (g + 2 * WAVES) * STAGE, k_hi, mrow, kq, x0, a0);
-      mfma_stage_mul<DT, R>(x1, a1, acc);
-    }
-    // fixed-order sum over the 16 waves: w + 8 into w, then slots 0..7 in order
-    if (w >= WAVES / 2) {
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) red[w - WAVES / 2][nb][lane] = acc[nb];
-    }
-    __syncthreads();
-    if (w < WAVES / 2) {
+    for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int q = 0;
+  for (int sg; (sg = next_run(sh, q)) >= 0;) {
+    // rows outside the run read row r0 of the tile (it exists) and are zeroed in shr_mul
+    gptr<const uint16_t> xr[RB];
+    bool xin[RB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) red[w][nb][lane] = acc[nb] + red[w][nb][lane];
+    for (int rb = 0; rb < RB; ++rb) {
+      xin[rb] = sh.rseg[16 * rb + mrow] == sg;
+      xr[rb] = global_ptr(x) + static_cast<int64_t>(s_prow[xin[rb] ? 16 * rb + mrow : 0]) * ld_x;
     }
-    __syncthreads();
-    if (tid < NB * 256) {
-      const int nb = tid >> 8, l = (tid >> 2) & 63, c = tid & 3;
-      float sum = 0.f;
+    const gptr<const uint16_t> A = global_ptr(A_ptrs[sg]);
+    gptr<const uint16_t> ar[NB];
 #pragma unroll
-      for (int q = 0; q < WAVES / 2; ++q) sum += red[q][nb][l][c];
-      const int row = r0 + 4 * (l >> 4) + c;
-      const int jj = nb * 16 + (l & 15);
-      if (row >= run.lo && row < run.hi) {
-        if (ks == 1)
-          v_out[static_cast<int64_t>(row) * R + jj] = sum;
-        else
-          store_coherent(part + kc * slice + static_cast<int64_t>(row) * R + jj, sum);
-      }
+    for (int nb = 0; nb < NB; ++nb) ar[nb] = A + static_cast<int64_t>(nb * 16 + mrow) * h_in;
+    uint4 x0[UN][RB], a0[UN][NB], x1[UN][RB], a1[UN][NB];
+    int k0 = k_lo + w * STAGE;
+    shr_load<DT, R>(xr, ar, k0, k_hi, kq, x0, a0);
+    for (int g = w; g < nst; g += 8) {
+      shr_load<DT, R>(xr, ar, k0 + 4 * STAGE, k_hi, kq, x1, a1);
+      shr_mul<DT, R>(x0, a0, k0, k_hi, kq, xin, acc);
+      shr_load<DT, R>(xr, ar, k0 + 8 * STAGE, k_hi, kq, x0, a0);
+      shr_mul<DT, R>(x1, a1, k0 + 4 * STAGE, k_hi, kq, xin, acc);
+      k0 += 8 * STAGE;
     }
-    __syncthreads();
+  }
+  // fixed-order sum over the waves: (w0 + w2) + (w1 + w3)
+  if (w >= 2) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) red[w - 2][rb][nb][lane] = acc[rb][nb];
+  }
+  __syncthreads();
+  if (w < 2) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) red[w][rb][nb][lane] = acc[rb][nb] + red[w][rb][nb][lane];
+  }
+  __syncthreads();
+  // entry e = (rb, nb, l): rows r0 + 16rb + 4(l/16) + c, column nb*16 + l%16
+  for (int e = tid; e < RB * NB * 64; e += 256) {
+    const int l = e & 63, nb = (e >> 6) % NB, rb = (e >> 6) / NB;
+    const f32x4_t sum = red[0][rb][nb][l] + red[1][rb][nb][l];
+    const int jj = nb * 16 + (l & 15);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int qr = 16 * rb + 4 * (l >> 4) + c;
+      if (sh.rseg[qr] < 0) continue;
+      const int64_t o = static_cast<int64_t>(r0 + qr) * R + jj;
+      if (ks == 1)
+        v_out[o] = sum[c];
+      else
+        store_coherent(part + kc * slice + o, sum[c]);
+    }
   }
   if (kc == 0)
-    for (int q = tid; q < r1 - r0; q += blockDim.x)
-      if ((lmask >> q) & 1u) rowks[r0 + q] = 0;  // v of long rows is final, not in slices
+    for (int qr = tid; qr < r1 - r0; qr += 256)
+      if (sh.rseg[qr] >= 0) rowks[r0 + qr] = 0;  // v of long rows is final, not in slices
   if (ks == 1) return;
 
   // publish this chunk, then let the last chunk of the tile reduce and write v
@@ -389,28 +403,27 @@ __global__ __launch_bounds__(1024) void shrink_mfma_kernel(
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(&tile_cnt[blockIdx.x * kCounterStride], 1,
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int old = __hip_atomic_fetch_add(&tile_cnt[tile * kCounterStride], 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
     s_last = (old == ks - 1);
-    if (s_last) __hip_atomic_store(&tile_cnt[blockIdx.x * kCounterStride], 0, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+    if (s_last)
+      __hip_atomic_store(&tile_cnt[tile * kCounterStride], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  for (int idx = tid; idx < (r1 - r0) * R; idx += blockDim.x) {
-    const int q = idx / R;
-    if (!((lmask >> q) & 1u)) continue;
+  for (int idx = tid; idx < (r1 - r0) * R; idx += 256) {
+    if (sh.rseg[idx / R] < 0) continue;
     const float* src = part + static_cast<int64_t>(r0) * R + idx;
-    float acc = 0.f;
+    float a = 0.f;
     for (int k0 = 0; k0 < ks; k0 += 8) {
       float v8[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) v8[u] = (k0 + u < ks) ? load_coherent(src + (k0 + u) * slice) : 0.f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc += v8[u];
+      for (int u = 0; u < 8; ++u) a += v8[u];
     }
-    v_out[static_cast<int64_t>(r0) * R + idx] = acc;
+    v_out[static_cast<int64_t>(r0) * R + idx] = a;
   }
 }
 
@@ -430,9 +443,6 @@ __global__ __launch_bounds__(1024) void shrink_mfma_kernel(
 constexpr int kExpRows = 32;
 constexpr int kExpCols = 256;
 constexpr int kExpPad = 4;       // floats of padding per LDS row of the sums
-constexpr int kExpMaxSegs = 4;   // long segments that can overlap 32 rows: 32/16 + 2
-constexpr int kXcds = 8;
-
 // waves per SIMD the register budget is set for: 4 workgroups per CU for r = 16, fewer for
 // the larger B fragments of r = 32 and 64
 template <int R>
@@ -450,9 +460,7 @@ __global__ __launch_bounds__(256, expand_waves<R>()) void expand_mfma_kernel(
   constexpr int NK = KT / 32;        // MFMA k-steps
   constexpr int VPT = TR * R / 256;  // v values per thread
   constexpr int YPT = TR * TC / 8 / 256;  // 16-byte vectors of y per thread
-  __shared__ int s_nseg;
-  __shared__ int s_seg[kExpMaxSegs], s_st[kExpMaxSegs], s_en[kExpMaxSegs];
-  __shared__ int s_rseg[TR];  // long segment of each tile row, -1 otherwise
+  __shared__ TileSegs<TR> sh;
   __shared__ int s_prow[TR];  // caller row of each tile row
   __shared__ __attribute__((aligned(16))) uint16_t vlds[TR][KT];
   __shared__ __attribute__((aligned(16))) float dl[TR][TC + kExpPad];
@@ -473,7 +481,6 @@ __global__ __launch_bounds__(256, expand_waves<R>()) void expand_mfma_kernel(
   const int kq = lane >> 4, l16 = lane & 15;
 
   // caller rows first, so that y is in flight while the segments are found
-  if (tid == 0) s_nseg = 0;
   if (tid < TR) s_prow[tid] = (g0 + tid < g1) ? (perm ? perm[g0 + tid] : g0 + tid) : -1;
   __syncthreads();
   // y: thread vector e = tid + 256u covers row e / 32, columns c0 + 8 * (e % 32) .. +7
@@ -490,34 +497,12 @@ __global__ __launch_bounds__(256, expand_waves<R>()) void expand_mfma_kernel(
     const int idx = tid + 256 * u;
     vv[u] = (g0 + idx / R < g1) ? v[static_cast<int64_t>(g0) * R + idx] : 0.f;
   }
-  // long segments overlapping the tile
-  for (int s = tid; s < S; s += 256) {
-    const int st = seg_starts[s], en = seg_starts[s + 1];
-    if (en - st >= kLongMin && st < g1 && en > g0) {
-      const int k = atomicAdd(&s_nseg, 1);
-      if (k < kExpMaxSegs) {
-        s_seg[k] = s;
-        s_st[k] = st;
-        s_en[k] = en;
-      }
-    }
-  }
-  __syncthreads();
-  const int nseg = min(s_nseg, kExpMaxSegs);
-  if (nseg == 0) return;  // uniform
-  if (tid < TR) {
-    const int row = g0 + tid;
-    int sg = -1;
-    for (int k = 0; k < nseg; ++k)
-      if (s_st[k] <= row && row < s_en[k]) sg = s_seg[k];
-    s_rseg[tid] = sg;
-  }
-  __syncthreads();
+  if (tile_long_segments<TR, 256>(seg_starts, S, g0, g1, sh) == 0) return;  // uniform
 
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
     const int idx = tid + 256 * u;
-    const float val = (s_rseg[idx / R] >= 0) ? scale * vv[u] : 0.f;
+    const float val = (sh.rseg[idx / R] >= 0) ? scale * vv[u] : 0.f;
     const uint32_t hw = E::pack(val, 0.f) & 0xffffu;
     const uint32_t lw = E::pack(val - E::lo(hw), 0.f) & 0xffffu;
     vlds[idx / R][idx % R] = static_cast<uint16_t>(hw);
@@ -527,7 +512,7 @@ __global__ __launch_bounds__(256, expand_waves<R>()) void expand_mfma_kernel(
 
   int rs[2];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) rs[rb] = s_rseg[16 * rb + l16];
+  for (int rb = 0; rb < 2; ++rb) rs[rb] = sh.rseg[16 * rb + l16];
   f32x4_t acc[2][4];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
@@ -535,12 +520,8 @@ __global__ __launch_bounds__(256, expand_waves<R>()) void expand_mfma_kernel(
     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // the long segments of the tile, in increasing order (the reads are uniform)
   int q = 0;
-  for (;;) {
-    while (q < TR && s_rseg[q] < 0) ++q;
-    if (q >= TR) break;
-    const int sg = s_rseg[q];
-    while (q < TR && s_rseg[q] == sg) ++q;
-    const uint16_t* B = B_ptrs[sg];
+  for (int sg; (sg = next_run(sh, q)) >= 0;) {
+    const gptr<const uint16_t> B = global_ptr(B_ptrs[sg]);
     uint4 bop[4][NK];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
@@ -575,7 +556,7 @@ __global__ __launch_bounds__(256, expand_waves<R>()) void expand_mfma_kernel(
 #pragma unroll
   for (int u = 0; u < YPT; ++u) {
     const int e = tid + 256 * u, q2 = e / (TC / 8), cc = 8 * (e % (TC / 8)), col = c0 + cc;
-    if (s_rseg[q2] < 0 || col >= h_out) continue;
+    if (sh.rseg[q2] < 0 || col >= h_out) continue;
     const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(&dl[q2][cc]);
     const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(&dl[q2][cc + 4]);
     uint4 o;
@@ -616,18 +597,19 @@ inline int gemv_kc(int r) {
 static_assert(GemvCfg<16>::KC == 512 && GemvCfg<32>::KC == 256 && GemvCfg<64>::KC == 256,
               "table_gemv_kc in sgmv_checks.h must match the GEMV shrink's chunk");
 
-// split-K chunk of the MFMA shrink: about 256 workgroups in all (one per CU), at most 8
-// chunks per tile, each a multiple of 128 k (a whole number of stages for every rank)
-inline int mfma_kcm(int32_t n, int32_t h_in, int32_t r) {
-  (void)r;
-  const int stage = ShrinkMfmaCfg<16>::STAGE;
-  const int tiles = (n + kTileRows - 1) / kTileRows;
-  int chunks = (256 + tiles - 1) / (tiles > 0 ? tiles : 1);
-  if (chunks < 1) chunks = 1;
-  if (chunks > 8) chunks = 8;
-  const int stages = (h_in + stage - 1) / stage;
-  if (chunks > stages) chunks = stages;
-  return ((stages + chunks - 1) / chunks) * stage;
+// split-K of the MFMA shrink: enough workgroups to give every CU its resident share,
+// chunks of at least 256 k, a multiple of 8 chunks where there are 8 or more (XCD-owned
+// chunks), and no more slices than the workspace holds
+inline void mfma_split(int32_t n, int32_t h_in, int32_t r, int ks_cap, int* kcm, int* ks) {
+  const int tiles = (n + kShrRows - 1) / kShrRows;
+  const int target = 256 * ((r == 64) ? ShrCfg<64>::WAVES_PER_SIMD : ShrCfg<16>::WAVES_PER_SIMD);
+  int k = (target + tiles - 1) / tiles;
+  k = min(k, max(1, h_in / 256));
+  k = max(1, min(k, ks_cap));
+  if (k >= 8) k -= k % 8;
+  const int c = ((h_in + k - 1) / k + 63) / 64 * 64;
+  *kcm = c;
+  *ks = (h_in + c - 1) / c;
 }
 
 struct Tables {
@@ -654,12 +636,12 @@ hipError_t launch_shrink(hipStream_t st, const uint16_t* x, int64_t ld_x, const 
                        T.ptrs, T.seg_starts, T.perm, h_in, part, L.slice, rowks, ks);
   }
   if (T.use_long()) {
-    const int kcm = mfma_kcm(T.n, h_in, R);
-    const int ks = (h_in + kcm - 1) / kcm;
-    const int tiles = (T.n + kTileRows - 1) / kTileRows;
-    hipLaunchKernelGGL((shrink_mfma_kernel<DT, R>), dim3(tiles, ks), dim3(1024), 0, st, x, ld_x,
-                       T.ptrs, T.seg_starts, T.S, T.perm, T.n, h_in, kcm, part, L.slice,
-                       reinterpret_cast<int32_t*>(ws + L.tile_cnt_off), v_long, rowks, ks);
+    int kcm, ks;
+    mfma_split(T.n, h_in, R, L.ks_max, &kcm, &ks);
+    const int tiles = (T.n + kShrRows - 1) / kShrRows;
+    hipLaunchKernelGGL((shrink_mfma_kernel<DT, R>), dim3(tiles * ks), dim3(256), 0, st, x, ld_x,
+                       T.ptrs, T.seg_starts, T.S, T.perm, T.n, h_in, kcm, ks, part, L.slice,
+                       reinterpret_cast<int32_t*>(ws + L.tile_cnt_off), v_long, rowks);
   }
   return hipGetLastError();
 }
