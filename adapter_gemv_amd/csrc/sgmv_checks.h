@@ -61,8 +61,10 @@ inline int check_device() {
 //   [tile_cnt_off, ...)     table path: one counter per 16-row tile, one per 256-byte line
 //   [rowks_off, ...)        table path: split-K slice count of each sorted row
 //   [v_off, ...)            table path: final float32 v of rows of long segments
-//   [part_off, total)       float32 split-K partial sums (either path)
-// Counters are zero before a call and are left at zero by it.
+//   [part_off, ...)         table path: float32 split-K partial sums
+//   [pool_off, total)       decode path (n <= 64): tagged 64-bit split-K partial sums
+// Counters and the decode path's tagged partials are zero before a call and are left at
+// zero by it; the table path's partials and v are scratch.
 // ------------------------------------------------------------------------------------
 constexpr int kMaxPoolRows = 64;
 constexpr size_t kWsPoolCounters = 256;
@@ -73,10 +75,11 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // split-K chunk (elements of h_in) of the table path's GEMV shrink and of the decode path
 inline int table_gemv_kc(int r) { return r == 16 ? 512 : 256; }
 inline int pool_kc(int r) { return 8192 / r; }
-inline int pool_part_row(int r) { return r < 32 ? 32 : r; }
+// 64-bit words per row of a decode-path partial slice (r words: at least 128 bytes)
+constexpr int pool_part_row(int r) { return r; }
 
 struct WsLayout {
-  size_t tile_cnt_off, rowks_off, v_off, part_off, total;
+  size_t tile_cnt_off, rowks_off, v_off, part_off, pool_off, total;
   int64_t slice;  // floats per split-K slice of the table path (n * r)
   int ks_max;     // table path: split-K slices the partial-sum area holds
 };
@@ -92,13 +95,14 @@ inline WsLayout ws_layout(int32_t n, int32_t h_in, int32_t r) {
   L.rowks_off = L.tile_cnt_off + sizeof(int32_t) * kCounterInts * tiles;
   L.v_off = align_up(L.rowks_off + sizeof(int32_t) * static_cast<size_t>(n), 256);
   L.part_off = align_up(L.v_off + sizeof(float) * static_cast<size_t>(L.slice), 256);
-  size_t part = sizeof(float) * static_cast<size_t>(L.slice) * L.ks_max;
+  const size_t part = sizeof(float) * static_cast<size_t>(L.slice) * L.ks_max;
+  L.pool_off = align_up(L.part_off + part, 256);
+  size_t pool = 0;
   if (n <= kMaxPoolRows) {
     const size_t ksp = static_cast<size_t>((h_in + pool_kc(r) - 1) / pool_kc(r));
-    const size_t pool = sizeof(float) * ksp * static_cast<size_t>(n) * pool_part_row(r);
-    if (pool > part) part = pool;
+    pool = sizeof(uint64_t) * ksp * static_cast<size_t>(n) * pool_part_row(r);
   }
-  L.total = L.part_off + part;
+  L.total = L.pool_off + pool;
   return L;
 }
 

@@ -8,18 +8,18 @@
 //     and finds the rows that share its adapter with one wavefront ballot -- the same
 //     row sets, in the same caller order, as the stable sort's segments;
 //   * shrink items (adapter rows within a block of 16 caller rows, K chunk) compute
-//     float32 partial sums of v = x @ A[a] on MFMA 16x16x32 tiles, publish them with
-//     agent-scope atomic stores and then bump a counter per produced row;
+//     float32 partial sums of v = x @ A[a] on MFMA 16x16x32 tiles and publish each one
+//     with a nonzero tag in the same 64-bit agent-scope atomic store;
 //   * expand items (caller row, column chunk) load their slice of B[a] and of y while
-//     the shrink runs, wait for the row's counter, add the partial sums in a fixed order and
-//     write y = y + scale * v @ B[a] with one rounding.
-// Items are ordered shrink-first in the grid.  Workgroups are dispatched in index
-// order within each XCD, so every shrink item a waiting expand item depends on has
-// already been placed on a CU; shrink items never wait, hence the waits end (they are
-// also bounded, and flag the workspace if the bound is hit).  The last item of a row
-// resets its counter, leaving the workspace ready for the next call without a
-// memset (safe under HIP graph capture).  Counters live one per 256-byte line, so items
-// of different rows never contend for a cache line.  The device-side stable sort itself is
+//     the shrink runs, poll the row's tagged partial sums until every one is present,
+//     add them in a fixed order and write y = y + scale * v @ B[a] with one rounding.
+// Items are ordered shrink-first in the grid (one wave per item).
+// Workgroups are dispatched in index order within each XCD, so every shrink item a
+// waiting expand item depends on has already been placed on a CU; shrink items never
+// wait, hence the waits end (they are also bounded, and flag the workspace if the bound
+// is hit).  The last expand item of a row (per a counter on its own 256-byte line) clears
+// the row's partials and the counter, leaving the workspace ready for the next call
+// without a memset (safe under HIP graph capture).  The device-side stable sort itself is
 // available as sgmv_build_segments_device.
 #include <hip/hip_runtime.h>
 
@@ -37,6 +37,8 @@ using namespace sgmv_host;
 constexpr int kPoolMaxN = kMaxPoolRows;  // tokens per call on this path (one wavefront)
 constexpr int kCounterStride = kCounterInts;  // one counter per 256-byte line (no sharing)
 constexpr int kSpinLimit = 1 << 22;      // bounded wait (about 0.1 s), then flag and exit
+constexpr int kItemsPerWg = 1;           // work items per workgroup (one per wave): more
+                                         // workgroups spread the loads over more CUs
 constexpr uint32_t kNoKey = 0xffffffffu;
 
 // ------------------------------------------------------------------------------------
@@ -142,9 +144,10 @@ __global__ __launch_bounds__(64) void segments_from_ids_kernel(
 // coalesced load of the ids and one ballot give every workgroup its adapter and the
 // set of rows that share it (the same rows, in the same caller order, as the stable
 // sort's segment; the order of segments does not change the result).  Split-K partial
-// sums are indexed by caller row.  They are published with agent-scope atomic stores
-// that are complete before the segment counter is bumped, and read back with
-// agent-scope atomic loads, so no L2 write-back or invalidate is needed between XCDs.
+// sums are indexed by caller row.  Each is one 64-bit word, the float32 bits in the low
+// half and a nonzero tag in the high half, written and read with agent-scope atomics:
+// a reader that sees the tag sees the value, with no L2 write-back or invalidate
+// between XCDs and no separate ready counter.
 struct PoolArgs {
   uint16_t* y;
   const uint16_t* x;
@@ -157,7 +160,7 @@ struct PoolArgs {
   float scale;
   int32_t* ws_flag;
   int32_t* counters;
-  float* part;
+  uint64_t* part;
 };
 
 struct Leader {
@@ -165,24 +168,20 @@ struct Leader {
   uint64_t rows;  // caller rows that use it
 };
 
-__device__ inline void store_partial(float* q, float v) {
-  __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+constexpr uint64_t kPartTag = 1ull << 32;
+
+__device__ inline void store_partial(uint64_t* q, float v) {
+  __hip_atomic_store(q, kPartTag | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ inline float load_partial(const float* q) {
+__device__ inline uint64_t load_partial(const uint64_t* q) {
   return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-// partial-sum rows are padded to whole 128-byte lines so items of different adapters
-// never write into one line
-template <int R>
-constexpr int part_row() { return R < 32 ? 32 : R; }
-static_assert(part_row<16>() == 32 && part_row<64>() == 64, "matches pool_part_row");
 
 // shrink item: partial v over k in [kc*KC, (kc+1)*KC) for the adapter's rows within
 // one block of 16 caller rows (blk).  MFMA 16x16x32; lane l supplies MFMA row/column
 // l%16 and the k group l/16, reading its own contiguous 8*U-element run of k for both
-// operands.  Each produced row's counter is bumped once the partials are visible.
+// operands.
 template <int DT, int R>
 __device__ inline void shrink_item(const PoolArgs& p, const Leader& L, int blk, int kc) {
   using E = Elem<DT>;
@@ -191,7 +190,7 @@ __device__ inline void shrink_item(const PoolArgs& p, const Leader& L, int blk, 
   constexpr int KC = 32 * U;
   const int lane = threadIdx.x & 63;
   const int mrow = lane & 15, kq = lane >> 4;
-  const uint16_t* A = p.A + static_cast<int64_t>(L.a) * p.A_stride;
+  const gptr<const uint16_t> A = global_ptr(p.A) + static_cast<int64_t>(L.a) * p.A_stride;
   const int kbase = kc * KC + kq * 8 * U;
   uint4 av[NB][U];
 #pragma unroll
@@ -202,43 +201,34 @@ __device__ inline void shrink_item(const PoolArgs& p, const Leader& L, int blk, 
       av[nb][u] = (kk < p.h_in) ? ld16(A + static_cast<int64_t>(nb * 16 + mrow) * p.h_in + kk)
                                 : zero4();
     }
-  const int64_t slice = static_cast<int64_t>(p.n) * part_row<R>();
-  {
-    const uint32_t bm = static_cast<uint32_t>(L.rows >> (16 * blk)) & 0xffffu;
-    const int row = 16 * blk + mrow;
-    const uint16_t* xr = ((bm >> mrow) & 1u) ? p.x + static_cast<int64_t>(row) * p.ld_x : nullptr;
-    uint4 xv[U];
+  const int64_t slice = static_cast<int64_t>(p.n) * pool_part_row(R);
+  const uint32_t bm = static_cast<uint32_t>(L.rows >> (16 * blk)) & 0xffffu;
+  const int row = 16 * blk + mrow;
+  const gptr<const uint16_t> xr =
+      ((bm >> mrow) & 1u) ? global_ptr(p.x) + static_cast<int64_t>(row) * p.ld_x : nullptr;
+  uint4 xv[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kk = kbase + 8 * u;
-      xv[u] = (xr && kk < p.h_in) ? ld16(xr + kk) : zero4();
-    }
-    f32x4_t acc[NB];
+  for (int u = 0; u < U; ++u) {
+    const int kk = kbase + 8 * u;
+    xv[u] = (xr && kk < p.h_in) ? ld16(xr + kk) : zero4();
+  }
+  f32x4_t acc[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+  for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[nb] = E::mfma(xv[u], av[nb][u], acc[nb]);
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = E::mfma(xv[u], av[nb][u], acc[nb]);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 4 * (lane >> 4) + e;
-      if ((bm >> r) & 1u) {
+  for (int e = 0; e < 4; ++e) {
+    const int r = 4 * (lane >> 4) + e;
+    if ((bm >> r) & 1u) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          store_partial(p.part + kc * slice + static_cast<int64_t>(16 * blk + r) * part_row<R>() + nb * 16 + mrow,
-                        acc[nb][e]);
-      }
+      for (int nb = 0; nb < NB; ++nb)
+        store_partial(p.part + kc * slice + static_cast<int64_t>(16 * blk + r) * pool_part_row(R) + nb * 16 + mrow,
+                      acc[nb][e]);
     }
   }
-  // every partial store has completed (and is visible device-wide) before the counts;
-  // lane l < 16 counts row 16*blk + l
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_waitcnt(0);
-  const uint32_t bm = static_cast<uint32_t>(L.rows >> (16 * blk)) & 0xffffu;
-  if (lane < 16 && ((bm >> lane) & 1u))
-    __hip_atomic_fetch_add(&p.counters[(16 * blk + lane) * kCounterStride], 1, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // expand item: one caller row r and columns [nc*64*CPL, (nc+1)*64*CPL); lane owns
@@ -254,50 +244,56 @@ __device__ inline void expand_item(const PoolArgs& p, const Leader& L, int r, in
   const int lane = threadIdx.x & 63;
   const int c0 = (nc * 64 + lane) * CPL;
   const bool cin = c0 < p.h_out;
+  const int cl = cin ? c0 : 0;  // lanes past h_out load column 0 and store nothing
 
+  // unconditional loads keep the compiler's wait counts exact
   uint4 b[16];
-  const uint16_t* Bblk = p.B + static_cast<int64_t>(L.a) * p.B_stride + static_cast<int64_t>(c0) * R;
+  const gptr<const uint16_t> Bblk =
+      global_ptr(p.B) + static_cast<int64_t>(L.a) * p.B_stride + static_cast<int64_t>(cl) * R;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) b[v] = cin ? ld16(Bblk + 8 * v) : zero4();
+  for (int v = 0; v < 16; ++v) b[v] = ld16(Bblk + 8 * v);
   uint32_t yv[YW];
-#pragma unroll
-  for (int q = 0; q < YW; ++q) yv[q] = 0u;
-  uint16_t* yrow = p.y + static_cast<int64_t>(r) * p.ld_y + c0;
-  if (cin) load_words<YW>(yrow, yv);
+  const gptr<uint16_t> yrow = global_ptr(p.y) + static_cast<int64_t>(r) * p.ld_y + cl;
+  load_words<YW>(yrow, yv);
+  asm volatile("" ::: "memory");  // keep the B and y loads ahead of the polling below
   float bf[CPL * R];
 #pragma unroll
   for (int e = 0; e < CPL * R; ++e) bf[e] = elem<DT>(b[e >> 3], e & 7);
 
-  if (lane == 0) {
-    int spins = 0;
-    while (__hip_atomic_load(&p.counters[r * kCounterStride], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT) < p.KS) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) {
-        __hip_atomic_store(p.ws_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-
-  // v[r, j]: lane (j = lane % R, g = lane / R) adds slices g, g+G, ... in order, then
-  // the G groups are combined by a fixed butterfly; every lane ends with the same sum
-  const int64_t slice = static_cast<int64_t>(p.n) * part_row<R>();
-  const float* src = p.part + static_cast<int64_t>(r) * part_row<R>() + (lane % R);
+  // v[r, j]: lane (j = lane % R, g = lane / R) takes slices g, g+G, ... of column j in
+  // batches of 8, polls each batch until every tag is present and adds it in order; the
+  // G lane groups are then combined by a fixed butterfly, so every lane ends with the
+  // same sum
+  const int64_t slice = static_cast<int64_t>(p.n) * pool_part_row(R);
+  const uint64_t* src = p.part + static_cast<int64_t>(r) * pool_part_row(R) + (lane % R);
   const int g = lane / R;
   float acc = 0.f;
-  for (int k0 = g; k0 < p.KS; k0 += 8 * G) {
-    float part8[8];
+  for (int k0 = 0; k0 < p.KS; k0 += 8 * G) {
+    uint64_t w[8];
+    for (int spins = 0;; ++spins) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int k = k0 + u * G;
-      part8[u] = (k < p.KS) ? load_partial(src + k * slice) : 0.f;
+      for (int u = 0; u < 8; ++u) {
+        const int k = k0 + g + u * G;
+        w[u] = (k < p.KS) ? load_partial(src + k * slice) : kPartTag;
+      }
+      bool ready = true;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) ready = ready && (w[u] >> 32) != 0;
+      if (__ballot(!ready) == 0) break;
+      if (spins >= kSpinLimit) {
+        if (lane == 0) __hip_atomic_store(p.ws_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc += part8[u];
+    for (int u = 0; u < 8; ++u) acc += __uint_as_float(static_cast<uint32_t>(w[u]));
   }
+  // count this reader; whether it is the row's last is looked at after the y store
+  int old = 0;
+  if (lane == 0)
+    old = __hip_atomic_fetch_add(&p.counters[r * kCounterStride], 1, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
   for (int msk = R; msk < 64; msk <<= 1) acc += __shfl_xor(acc, msk);
   // broadcast v[r, :] to scalar registers while every lane is active
@@ -323,33 +319,41 @@ __device__ inline void expand_item(const PoolArgs& p, const Leader& L, int r, in
     store_words<YW>(yrow, packed);
   }
 
-  // row r's counter sees KS shrink counts and NS expand counts; the last one leaves it
-  // at zero for the next call
-  if (lane == 0) {
-    int* c = &p.counters[r * kCounterStride];
-    const int old = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == p.KS + p.NS - 1) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the last of row r's NS readers clears the row's partials and its counter, leaving
+  // both at zero for the next call
+  if (__builtin_amdgcn_readfirstlane(old) == p.NS - 1) {
+    uint64_t* row = p.part + static_cast<int64_t>(r) * pool_part_row(R);
+    for (int idx = lane; idx < p.KS * R; idx += 64)
+      __hip_atomic_store(row + (idx / R) * slice + (idx % R), 0ull, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0)
+      __hip_atomic_store(&p.counters[r * kCounterStride], 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// Grid: n * KS shrink items (caller row r = b % n, chunk b / n; active when r is the
+// Grid: n * KS shrink items (caller row r = i % n, chunk i / n; active when r is the
 // first row of its adapter within its block of 16 rows), then n * NS expand items
-// (caller row r = e % n, column chunk e / n).  Every shrink item an expand item
-// waits for has a lower index.
+// (caller row r = i % n, column chunk i / n), kItemsPerWg items per workgroup (one per
+// wave).
+// Every shrink item an expand item waits for sits in a lower-numbered workgroup.
 template <int DT, int R>
-__global__ __launch_bounds__(64) void lora_add_pool_kernel(PoolArgs p) {
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(64 * kItemsPerWg) void lora_add_pool_kernel(PoolArgs p) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int id = lane < p.n ? p.ids[lane] : -1;
-  const int b = blockIdx.x;
   const int n_shrink = p.n * p.KS;
-  if (b == 0) {
+  const int shrink_wgs = (n_shrink + kItemsPerWg - 1) / kItemsPerWg;
+  const int b = blockIdx.x;
+  if (b == 0 && wv == 0) {
     const bool bad = __ballot(lane < p.n && (id < 0 || id >= p.n_adapters)) != 0;
     if (bad && lane == 0) __hip_atomic_store(p.ws_flag, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   Leader L;
-  if (b < n_shrink) {
+  if (b < shrink_wgs) {
     // item (row r, chunk kc) works iff r is its adapter's first row within r's block
-    const int r = b % p.n, kc = b / p.n;
+    const int it = kItemsPerWg * b + wv;
+    if (it >= n_shrink) return;
+    const int r = it % p.n, kc = it / p.n;
     const int a = __builtin_amdgcn_readlane(id, r);
     if (a < 0 || a >= p.n_adapters) return;
     L.a = a;
@@ -359,8 +363,9 @@ __global__ __launch_bounds__(64) void lora_add_pool_kernel(PoolArgs p) {
     if (bm & ((1u << (r & 15)) - 1u)) return;
     shrink_item<DT, R>(p, L, blk, kc);
   } else {
-    const int e = b - n_shrink;
-    const int r = e % p.n, nc = e / p.n;
+    const int it = kItemsPerWg * (b - shrink_wgs) + wv;
+    if (it >= p.n * p.NS) return;
+    const int r = it % p.n, nc = it / p.n;
     const int a = __builtin_amdgcn_readlane(id, r);
     if (a < 0 || a >= p.n_adapters) return;
     L.a = a;
@@ -371,8 +376,9 @@ __global__ __launch_bounds__(64) void lora_add_pool_kernel(PoolArgs p) {
 
 template <int DT, int R>
 hipError_t launch_pool(hipStream_t st, const PoolArgs& p) {
-  const int grid = p.n * (p.KS + p.NS);
-  hipLaunchKernelGGL((lora_add_pool_kernel<DT, R>), dim3(grid), dim3(64), 0, st, p);
+  const int grid = (p.n * p.KS + kItemsPerWg - 1) / kItemsPerWg +
+                   (p.n * p.NS + kItemsPerWg - 1) / kItemsPerWg;
+  hipLaunchKernelGGL((lora_add_pool_kernel<DT, R>), dim3(grid), dim3(64 * kItemsPerWg), 0, st, p);
   return hipGetLastError();
 }
 
@@ -439,7 +445,7 @@ extern "C" int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, in
   p.ws_flag = reinterpret_cast<int32_t*>(ws);
   const WsLayout L = ws_layout(n, h_in, r);
   p.counters = reinterpret_cast<int32_t*>(ws + kWsPoolCounters);
-  p.part = reinterpret_cast<float*>(ws + L.part_off);
+  p.part = reinterpret_cast<uint64_t*>(ws + L.pool_off);
 
   hipError_t e;
   if (dtype == SGMV_F16) {

@@ -168,11 +168,19 @@ def test_pool_repeat_calls_reset_counters(torch_cuda):
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
     assert int(ws[:16640].view(torch.int32).abs().sum().item()) == 0  # flag and counters at zero
-    # the table path on the same workspace agrees within tolerance
+    # the tagged partial sums (the last region of the workspace) are left at zero too
+    ks = -(-p.h_in // (8192 // 16))
+    tail = 8 * ks * p.n * 16
+    assert int(ws[-tail:].view(torch.int32).abs().sum().item()) == 0
+    # the table path on the same workspace agrees within tolerance, and a decode-path call
+    # after it still gives the same bits
     y2 = dp.lora_add(workspace=ws)
     torch.cuda.synchronize()
     _assert_close(oracle.decode(_storage(y2, "f16"), "f16"),
                   oracle.decode(_storage(outs[0], "f16"), "f16"), "pool vs table path")
+    y3 = dp.lora_add_pool(workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y3, outs[0])
 
 
 def test_pool_hip_graph_replay(torch_cuda):
