@@ -232,11 +232,11 @@ __device__ inline int next_run(const TileSegs<ROWS>& sh, int& q) {
   return sg;
 }
 
-// Shrink on MFMA 16x16x32 for a tile of 64 sorted rows and one K chunk.  The x rows are
+// Shrink on MFMA 16x16x32 for a tile of r sorted rows and one K chunk.  The x rows are
 // the A operand and the adapter's stored A rows the B operand; lane l supplies row (or
 // column) l%16 and k = k0 + 8*(l/16) .. +7 of each 32-wide k step.  Each of the 4 waves
-// covers all 64 rows and R columns (4 x R/16 accumulator blocks), so A is read once per
-// 64 rows; the waves take interleaved stages of UN k steps, with the loads of the next
+// covers all r rows and r columns (r/16 x r/16 accumulator blocks), so A and x are read
+// in equal amounts; the waves take interleaved stages of UN k steps, with the loads of the next
 // stage in flight while the current one is multiplied, and are summed through LDS in a
 // fixed order.  Rows of several long segments in one tile are handled run by run with the
 // other rows' x set to zero.  With one chunk per tile v is written directly; otherwise the
@@ -245,16 +245,17 @@ __device__ inline int next_run(const TileSegs<ROWS>& sh, int& q) {
 //
 // With a multiple of 8 chunks, workgroup b (on XCD b % 8) takes chunks = b mod 8, so each
 // XCD's L2 keeps one eighth of the K range of the adapters' A.
-constexpr int kShrRows = 64;
 constexpr int kXcds = 8;
 
 template <int R>
 struct ShrCfg {
   static constexpr int NB = R / 16;                 // column blocks of v
-  static constexpr int RB = kShrRows / 16;          // row blocks
+  static constexpr int RB = R / 16;                 // row blocks
+  static constexpr int MT = 16 * RB;                // rows per tile
   static constexpr int UN = (R == 16) ? 2 : 1;      // k steps per stage
   static constexpr int STAGE = 32 * UN;             // k per stage
   static constexpr int WAVES_PER_SIMD = (R == 64) ? 2 : 3;
+  static constexpr int TARGET_WGS = (R == 16) ? 256 : (R == 32 ? 384 : 512);
 };
 
 // Loads of one stage.  They are unconditional (out-of-range k reads offset 0 of the same
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(256, ShrCfg<R>::WAVES_PER_SIMD) void shrink_mfma_ke
     int32_t h_in, int32_t kcm, int32_t ks, float* __restrict__ part, int64_t slice,
     int32_t* __restrict__ tile_cnt, float* __restrict__ v_out, int32_t* __restrict__ rowks) {
   using C = ShrCfg<R>;
-  constexpr int NB = C::NB, RB = C::RB, UN = C::UN, STAGE = C::STAGE, MT = kShrRows;
+  constexpr int NB = C::NB, RB = C::RB, UN = C::UN, STAGE = C::STAGE, MT = C::MT;
   __shared__ TileSegs<MT> sh;
   __shared__ int s_prow[MT];
   __shared__ int s_last;
@@ -412,18 +413,34 @@ __global__ __launch_bounds__(256, ShrCfg<R>::WAVES_PER_SIMD) void shrink_mfma_ke
   __syncthreads();
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  for (int idx = tid; idx < (r1 - r0) * R; idx += 256) {
-    if (sh.rseg[idx / R] < 0) continue;
-    const float* src = part + static_cast<int64_t>(r0) * R + idx;
-    float a = 0.f;
-    for (int k0 = 0; k0 < ks; k0 += 8) {
-      float v8[8];
+  // The tile's part of each slice is contiguous (rows r0.. of R floats): thread t takes
+  // the 4-float groups t, t + 256, ..., reads up to 16 slices of them at once as 64-bit
+  // coherent loads and adds the slices in order.
+  constexpr int kSl = 16;
+  const int nq = (r1 - r0) * R / 4;
+  for (int qd = tid; qd < nq; qd += 256) {
+    if (sh.rseg[qd * 4 / R] < 0) continue;
+    const uint64_t* src = reinterpret_cast<const uint64_t*>(part + static_cast<int64_t>(r0) * R) + 2 * qd;
+    f32x4_t a = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < ks; k0 += kSl) {
+      uint64_t lo[kSl], hi[kSl];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v8[u] = (k0 + u < ks) ? load_coherent(src + (k0 + u) * slice) : 0.f;
+      for (int u = 0; u < kSl; ++u) {
+        const bool in = k0 + u < ks;
+        const uint64_t* q = src + (in ? (k0 + u) : 0) * (slice / 2);
+        lo[u] = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        hi[u] = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) a += v8[u];
+      for (int u = 0; u < kSl; ++u) {
+        const bool in = k0 + u < ks;
+        a[0] += in ? __uint_as_float(static_cast<uint32_t>(lo[u])) : 0.f;
+        a[1] += in ? __uint_as_float(static_cast<uint32_t>(lo[u] >> 32)) : 0.f;
+        a[2] += in ? __uint_as_float(static_cast<uint32_t>(hi[u])) : 0.f;
+        a[3] += in ? __uint_as_float(static_cast<uint32_t>(hi[u] >> 32)) : 0.f;
+      }
     }
-    v_out[static_cast<int64_t>(r0) * R + idx] = a;
+    *reinterpret_cast<f32x4_t*>(v_out + static_cast<int64_t>(r0) * R + 4 * qd) = a;
   }
 }
 
@@ -597,12 +614,14 @@ inline int gemv_kc(int r) {
 static_assert(GemvCfg<16>::KC == 512 && GemvCfg<32>::KC == 256 && GemvCfg<64>::KC == 256,
               "table_gemv_kc in sgmv_checks.h must match the GEMV shrink's chunk");
 
-// split-K of the MFMA shrink: enough workgroups to give every CU its resident share,
-// chunks of at least 256 k, a multiple of 8 chunks where there are 8 or more (XCD-owned
-// chunks), and no more slices than the workspace holds
-inline void mfma_split(int32_t n, int32_t h_in, int32_t r, int ks_cap, int* kcm, int* ks) {
-  const int tiles = (n + kShrRows - 1) / kShrRows;
-  const int target = 256 * ((r == 64) ? ShrCfg<64>::WAVES_PER_SIMD : ShrCfg<16>::WAVES_PER_SIMD);
+// split-K of the MFMA shrink: about TARGET_WGS workgroups (set per rank from measured
+// sweeps on MI355X: fewer, longer chunks win for r = 16, more for r = 64), chunks of at
+// least 256 k, a multiple of 8 chunks where there are 8 or more (XCD-owned chunks), and
+// no more slices than the workspace holds
+template <int R>
+inline void mfma_split(int32_t n, int32_t h_in, int ks_cap, int* kcm, int* ks) {
+  const int tiles = (n + ShrCfg<R>::MT - 1) / ShrCfg<R>::MT;
+  const int target = ShrCfg<R>::TARGET_WGS;
   int k = (target + tiles - 1) / tiles;
   k = min(k, max(1, h_in / 256));
   k = max(1, min(k, ks_cap));
@@ -637,8 +656,8 @@ hipError_t launch_shrink(hipStream_t st, const uint16_t* x, int64_t ld_x, const 
   }
   if (T.use_long()) {
     int kcm, ks;
-    mfma_split(T.n, h_in, R, L.ks_max, &kcm, &ks);
-    const int tiles = (T.n + kShrRows - 1) / kShrRows;
+    mfma_split<R>(T.n, h_in, L.ks_max, &kcm, &ks);
+    const int tiles = (T.n + ShrCfg<R>::MT - 1) / ShrCfg<R>::MT;
     hipLaunchKernelGGL((shrink_mfma_kernel<DT, R>), dim3(tiles * ks), dim3(256), 0, st, x, ld_x,
                        T.ptrs, T.seg_starts, T.S, T.perm, T.n, h_in, kcm, ks, part, L.slice,
                        reinterpret_cast<int32_t*>(ws + L.tile_cnt_off), v_long, rowks);
