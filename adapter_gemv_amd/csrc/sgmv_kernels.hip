@@ -444,43 +444,48 @@ __global__ __launch_bounds__(256, ShrCfg<R>::WAVES_PER_SIMD) void shrink_mfma_ke
   }
 }
 
-// Expand on MFMA 16x16x32 for a tile of 32 sorted rows and 256 columns, computed
+// Expand on MFMA 16x16x32 for a tile of TR sorted rows and TC columns, computed
 // transposed: D[col, row] = sum_k Bk[col, k] * Vk[k, row], where the k dimension is 2r:
 // the stored rows of B[a] twice (A operand) against scale * v split into two 16-bit
 // halves, hi = round(scale*v) and lo = round(scale*v - hi) (B operand).  The products are
 // exact and summed in float32; hi + lo carries 16 (bf16) or 22 (fp16) significant bits of
 // scale*v.  The float32 sums go through LDS so that y is read and written with whole
-// 16-byte vectors (16 lanes per 256-column row): y is loaded as soon as the caller rows
-// are known, then updated as y + sum in float32 and rounded once.
+// 16-byte vectors (TC/8 lanes per row): y is loaded as soon as the caller rows are known,
+// then updated as y + sum in float32 and rounded once.  The tile shape keeps the B bytes
+// a tile reads (TC x r) no larger than its y bytes (TR x TC).
 //
 // Workgroup b runs on XCD b % 8 (round-robin dispatch).  Each XCD owns a contiguous range
 // of column strips, so its L2 holds only that part of every B[a]; within the range the
 // workgroups go row tile by row tile, so the y traffic in flight at any time covers whole
 // rows of a few consecutive tiles.
-constexpr int kExpRows = 32;
-constexpr int kExpCols = 256;
-constexpr int kExpPad = 4;       // floats of padding per LDS row of the sums
-// waves per SIMD the register budget is set for: 4 workgroups per CU for r = 16, fewer for
-// the larger B fragments of r = 32 and 64
 template <int R>
-constexpr int expand_waves() { return R == 16 ? 4 : (R == 32 ? 3 : 2); }
+struct ExpCfg {
+  static constexpr int TR = (R == 16) ? 32 : 64;    // rows per tile
+  static constexpr int TC = (R == 16) ? 256 : 128;  // columns per tile (TC/4 per wave)
+  static constexpr int RB = TR / 16, CB = TC / 64;  // 16 x 16 blocks per wave
+  static constexpr int PAD = 4;                     // floats of padding per LDS row of sums
+  // waves per SIMD the register budget is set for
+  static constexpr int WAVES_PER_SIMD = (R == 16) ? 4 : 3;
+};
 
 template <int DT, int R>
-__global__ __launch_bounds__(256, expand_waves<R>()) void expand_mfma_kernel(
+__global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_kernel(
     uint16_t* __restrict__ y, int64_t ld_y, const float* __restrict__ v,
     const uint16_t* const* __restrict__ B_ptrs, const int32_t* __restrict__ seg_starts, int32_t S,
     const int32_t* __restrict__ perm, int32_t n, int32_t h_out, float scale, int32_t tiles,
     int32_t strips) {
   using E = Elem<DT>;
-  constexpr int TR = kExpRows, TC = kExpCols;
+  using C = ExpCfg<R>;
+  constexpr int TR = C::TR, TC = C::TC, RB = C::RB, CB = C::CB;
   constexpr int KT = 2 * R;          // k of the hi/lo product
   constexpr int NK = KT / 32;        // MFMA k-steps
   constexpr int VPT = TR * R / 256;  // v values per thread
-  constexpr int YPT = TR * TC / 8 / 256;  // 16-byte vectors of y per thread
+  constexpr int VPR = TC / 8;        // 16-byte vectors per tile row
+  constexpr int YPT = TR * VPR / 256;  // 16-byte vectors of y per thread
   __shared__ TileSegs<TR> sh;
   __shared__ int s_prow[TR];  // caller row of each tile row
   __shared__ __attribute__((aligned(16))) uint16_t vlds[TR][KT];
-  __shared__ __attribute__((aligned(16))) float dl[TR][TC + kExpPad];
+  __shared__ __attribute__((aligned(16))) float dl[TR][TC + C::PAD];
 
   // XCD x owns strips [sx0, sx1) and walks them tile-major
   const int b = blockIdx.x;
@@ -496,15 +501,16 @@ __global__ __launch_bounds__(256, expand_waves<R>()) void expand_mfma_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int kq = lane >> 4, l16 = lane & 15;
+  const int wc = c0 + (TC / 4) * w;  // first column of this wave
 
   // caller rows first, so that y is in flight while the segments are found
   if (tid < TR) s_prow[tid] = (g0 + tid < g1) ? (perm ? perm[g0 + tid] : g0 + tid) : -1;
   __syncthreads();
-  // y: thread vector e = tid + 256u covers row e / 32, columns c0 + 8 * (e % 32) .. +7
+  // y: thread vector e = tid + 256u covers row e / VPR, columns c0 + 8 * (e % VPR) .. +7
   uint4 yv[YPT];
 #pragma unroll
   for (int u = 0; u < YPT; ++u) {
-    const int e = tid + 256 * u, q = e / (TC / 8), col = c0 + 8 * (e % (TC / 8));
+    const int e = tid + 256 * u, q = e / VPR, col = c0 + 8 * (e % VPR);
     const int prow = s_prow[q];
     yv[u] = (prow >= 0 && col < h_out) ? ld16(y + static_cast<int64_t>(prow) * ld_y + col) : zero4();
   }
@@ -527,22 +533,22 @@ __global__ __launch_bounds__(256, expand_waves<R>()) void expand_mfma_kernel(
   }
   __syncthreads();
 
-  int rs[2];
+  int rs[RB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) rs[rb] = sh.rseg[16 * rb + l16];
-  f32x4_t acc[2][4];
+  for (int rb = 0; rb < RB; ++rb) rs[rb] = sh.rseg[16 * rb + l16];
+  f32x4_t acc[RB][CB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // the long segments of the tile, in increasing order (the reads are uniform)
   int q = 0;
   for (int sg; (sg = next_run(sh, q)) >= 0;) {
     const gptr<const uint16_t> B = global_ptr(B_ptrs[sg]);
-    uint4 bop[4][NK];
+    uint4 bop[CB][NK];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      const int col = c0 + 64 * w + 16 * cb + l16;
+    for (int cb = 0; cb < CB; ++cb) {
+      const int col = wc + 16 * cb + l16;
 #pragma unroll
       for (int s = 0; s < NK; ++s) {
         const int j0 = (32 * s + 8 * kq) % R;
@@ -550,29 +556,29 @@ __global__ __launch_bounds__(256, expand_waves<R>()) void expand_mfma_kernel(
       }
     }
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
       const int lq = 16 * rb + l16;
       uint4 vop[NK];
 #pragma unroll
       for (int s = 0; s < NK; ++s)
         vop[s] = (rs[rb] == sg) ? *reinterpret_cast<const uint4*>(&vlds[lq][32 * s + 8 * kq]) : zero4();
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int s = 0; s < NK; ++s) acc[rb][cb] = E::mfma(bop[cb][s], vop[s], acc[rb][cb]);
     }
   }
-  // lane: D rows 4*kq .. +3 of column block cb = tile columns 64w + 16cb + 4kq .. +3,
+  // lane: D rows 4*kq .. +3 of column block cb = tile columns (TC/4)w + 16cb + 4kq .. +3,
   // D column l16 = tile row 16rb + l16
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-      *reinterpret_cast<f32x4_t*>(&dl[16 * rb + l16][64 * w + 16 * cb + 4 * kq]) = acc[rb][cb];
+    for (int cb = 0; cb < CB; ++cb)
+      *reinterpret_cast<f32x4_t*>(&dl[16 * rb + l16][(TC / 4) * w + 16 * cb + 4 * kq]) = acc[rb][cb];
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < YPT; ++u) {
-    const int e = tid + 256 * u, q2 = e / (TC / 8), cc = 8 * (e % (TC / 8)), col = c0 + cc;
+    const int e = tid + 256 * u, q2 = e / VPR, cc = 8 * (e % VPR), col = c0 + cc;
     if (sh.rseg[q2] < 0 || col >= h_out) continue;
     const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(&dl[q2][cc]);
     const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(&dl[q2][cc + 4]);
@@ -679,8 +685,8 @@ hipError_t launch_expand(hipStream_t st, uint16_t* y, int64_t ld_y, const float*
   }
   if (T.use_long()) {
     // each XCD takes ceil(strips / 8) strips at most: pad the grid to 8 equal shares
-    const int tiles = (T.n + kExpRows - 1) / kExpRows;
-    const int strips = (h_out + kExpCols - 1) / kExpCols;
+    const int tiles = (T.n + ExpCfg<R>::TR - 1) / ExpCfg<R>::TR;
+    const int strips = (h_out + ExpCfg<R>::TC - 1) / ExpCfg<R>::TC;
     const int64_t share = static_cast<int64_t>(tiles) * ((strips + kXcds - 1) / kXcds);
     if (share * kXcds > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((expand_mfma_kernel<DT, R>), dim3(static_cast<unsigned>(share * kXcds)),

@@ -138,7 +138,7 @@ def test_exact_grid_bit_exact(torch_cuda, case, dtype):
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("r,kind,n", [(16, "perm", 24), (16, "mixed", 120), (64, "mixed", 100),
-                                      (32, "uniform", 57)])
+                                      (32, "uniform", 57), (32, "mixed", 130)])
 def test_gather_probe_bit_exact(torch_cuda, dtype, r, kind, n):
     _say(f"[gather] r={r} {kind} n={n} {dtype}")
     P = 6
@@ -166,6 +166,8 @@ RAGGED = [
     (257, 5128, 520, 16, 3, "mixed", 24, False),
     (64, 24, 4104, 64, 64, "perm", 0, False),
     (2048, 264, 264, 16, 1, "blocks", 0, True),     # one very long segment
+    (300, 1032, 1160, 32, 3, "mixed", 8, False),    # r = 32 tiles, ragged last strip
+    (129, 2056, 200, 64, 2, "blocks", 0, False),    # r = 64 tiles, narrow h_out
 ]
 
 
