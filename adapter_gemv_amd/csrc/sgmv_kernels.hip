@@ -449,7 +449,10 @@ __global__ __launch_bounds__(256, ShrCfg<R>::WAVES_PER_SIMD) void shrink_mfma_ke
 // the stored rows of B[a] twice (A operand) against scale * v split into two 16-bit
 // halves, hi = round(scale*v) and lo = round(scale*v - hi) (B operand).  The products are
 // exact and summed in float32; hi + lo carries 16 (bf16) or 22 (fp16) significant bits of
-// scale*v.  The float32 sums go through LDS so that y is read and written with whole
+// scale*v.  For fp16 each row of scale*v is first multiplied by a power of two that puts
+// its largest magnitude in [2^14, 2^15), and the row's sums are multiplied back by the
+// inverse power (both exact), so any float32 v fits fp16's range.  The float32 sums go
+// through LDS so that y is read and written with whole
 // 16-byte vectors (TC/8 lanes per row): y is loaded as soon as the caller rows are known,
 // then updated as y + sum in float32 and rounded once.  The tile shape keeps the B bytes
 // a tile reads (TC x r) no larger than its y bytes (TR x TC).
@@ -486,6 +489,7 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
   __shared__ int s_prow[TR];  // caller row of each tile row
   __shared__ __attribute__((aligned(16))) uint16_t vlds[TR][KT];
   __shared__ __attribute__((aligned(16))) float dl[TR][TC + C::PAD];
+  __shared__ int s_exp[TR];  // fp16: the row's sums are multiplied by 2^s_exp[row]
 
   // XCD x owns strips [sx0, sx1) and walks them tile-major
   const int b = blockIdx.x;
@@ -525,7 +529,16 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
     const int idx = tid + 256 * u;
-    const float val = (sh.rseg[idx / R] >= 0) ? scale * vv[u] : 0.f;
+    float val = (sh.rseg[idx / R] >= 0) ? scale * vv[u] : 0.f;
+    if constexpr (DT == SGMV_F16) {
+      // the R values of a row sit in R consecutive lanes: their largest magnitude
+      float mx = fabsf(val);
+#pragma unroll
+      for (int msk = 1; msk < R; msk <<= 1) mx = fmaxf(mx, __shfl_xor(mx, msk));
+      const int sh_up = (mx > 0.f && mx <= 3.0e38f) ? 14 - ilogbf(mx) : 0;
+      val = ldexpf(val, sh_up);
+      if (idx % R == 0) s_exp[idx / R] = -sh_up;
+    }
     const uint32_t hw = E::pack(val, 0.f) & 0xffffu;
     const uint32_t lw = E::pack(val - E::lo(hw), 0.f) & 0xffffu;
     vlds[idx / R][idx % R] = static_cast<uint16_t>(hw);
@@ -571,10 +584,18 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
   // lane: D rows 4*kq .. +3 of column block cb = tile columns (TC/4)w + 16cb + 4kq .. +3,
   // D column l16 = tile row 16rb + l16
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+  for (int rb = 0; rb < RB; ++rb) {
+    if constexpr (DT == SGMV_F16) {
+      const int ex = s_exp[16 * rb + l16];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[rb][cb][i] = ldexpf(acc[rb][cb][i], ex);
+    }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
       *reinterpret_cast<f32x4_t*>(&dl[16 * rb + l16][(TC / 4) * w + 16 * cb + 4 * kq]) = acc[rb][cb];
+  }
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < YPT; ++u) {

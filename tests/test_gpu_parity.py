@@ -186,6 +186,27 @@ def test_ragged_and_strided(torch_cuda, case, dtype):
     _assert_close(_y_f64(y, dtype), oracle.lora_add_problem(p), f"ragged {case} {dtype}")
 
 
+@pytest.mark.parametrize("r", [16, 64])
+def test_fp16_long_segments_beyond_fp16_range(torch_cuda, r):
+    """scale * v far beyond fp16's largest value (about 1.3e5 here) while every update fits
+    in fp16: the long-segment expand feeds scale * v to MFMA as fp16 halves, so it must
+    bring each row into range first; the GEMV rows of the same call check the other path."""
+    import dataclasses
+    _say(f"[fp16 range] r={r}")
+    ids = np.concatenate([np.repeat([0, 1], 48), np.arange(2, 7)]).astype(np.int32)
+    p = synth.random_problem((62, r), n=ids.size, h_in=256, h_out=648, r=r, n_adapters=7,
+                             dtype="f16", ids=ids, scale=64.0)
+    A = synth.quantize(p.A.astype(np.float32) * 2000.0, "f16")
+    B = synth.quantize(p.B.astype(np.float32) / 2000.0, "f16")
+    p = dataclasses.replace(p, A=A, B=B)
+    v = np.einsum("nk,njk->nj", p.x.astype(np.float64), A.astype(np.float64)[p.ids])
+    assert np.abs(p.scale * v).max() > 65504.0 * 1.5
+    _, y = _run_lora(p)
+    got = _y_f64(y, "f16")
+    assert np.isfinite(got).all()
+    _assert_close(got, oracle.lora_add_problem(p), f"fp16 range r={r}")
+
+
 # --------------------------------------------------------------------------------------
 # shrink and expand on their own
 # --------------------------------------------------------------------------------------
