@@ -43,7 +43,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16/fp16 MFMA, AMD published figure
 ROTATION_BYTES = 1 << 30       # operand slots cycled per pass (> 2x the 256 MB MALL)
 KERNEL_SRCS = [os.path.join(ROOT, "adapter_gemv_amd", "csrc", f)
-               for f in ("sgmv_device.h", "sgmv_kernels.hip", "sgmv_decode.hip")]
+               for f in ("sgmv_checks.h", "sgmv_device.h", "sgmv_kernels.hip", "sgmv_decode.hip")]
 
 
 def workload_problem(name: str):
