@@ -58,13 +58,18 @@ inline int check_device() {
 // workspace layout shared by every entry point (the same bytes serve both paths):
 //   [0, 4)                  int32 flag (decode path: 1 = a wait timed out, 2 = bad id)
 //   [256, 16640)            decode path: one counter per row, one per 256-byte line
-//   [tile_cnt_off, ...)     table path: one counter per 16-row tile, one per 256-byte line
+//   [tile_cnt_off, ...)     table path: one counter per shrink tile, one per 256-byte line
 //   [rowks_off, ...)        table path: split-K slice count of each sorted row
 //   [v_off, ...)            table path: final float32 v of rows of long segments
-//   [part_off, ...)         table path: float32 split-K partial sums
-//   [pool_off, total)       decode path (n <= 64): tagged 64-bit split-K partial sums
-// Counters and the decode path's tagged partials are zero before a call and are left at
-// zero by it; the table path's partials and v are scratch.
+//   [part_off, table_end)   table path: float32 split-K partial sums
+//   last pool_bytes(h_in, r) bytes of the caller's buffer (start rounded down to 256):
+//                           decode path: tagged 64-bit split-K partial sums, laid out
+//                           for 64 rows whatever n is
+// Counters and the tagged partials are zero before a call and are left at zero by it;
+// the table path's rowks, v and partials are scratch.  Every region grows with n, h_in
+// and r, and the tagged partials sit at the end of the buffer, so a buffer of
+// sgmv_workspace_bytes(n, h_in, r) bytes serves any mix of calls of at most n rows,
+// h_in and r without one call's scratch landing on another's tagged partials.
 // ------------------------------------------------------------------------------------
 constexpr int kMaxPoolRows = 64;
 constexpr size_t kWsPoolCounters = 256;
@@ -77,9 +82,21 @@ inline int table_gemv_kc(int r) { return r == 16 ? 512 : 256; }
 inline int pool_kc(int r) { return 8192 / r; }
 // 64-bit words per row of a decode-path partial slice (r words: at least 128 bytes)
 constexpr int pool_part_row(int r) { return r; }
+// 64-bit words per decode-path partial slice (64 rows)
+constexpr int64_t pool_slice(int r) { return static_cast<int64_t>(kMaxPoolRows) * pool_part_row(r); }
+
+inline size_t pool_bytes(int32_t h_in, int32_t r) {
+  const size_t ks = static_cast<size_t>((h_in + pool_kc(r) - 1) / pool_kc(r));
+  return sizeof(uint64_t) * ks * static_cast<size_t>(pool_slice(r));
+}
+
+// start of the tagged partials inside a caller buffer of ws_bytes bytes
+inline size_t pool_offset(size_t ws_bytes, int32_t h_in, int32_t r) {
+  return (ws_bytes - pool_bytes(h_in, r)) / 256 * 256;
+}
 
 struct WsLayout {
-  size_t tile_cnt_off, rowks_off, v_off, part_off, pool_off, total;
+  size_t tile_cnt_off, rowks_off, v_off, part_off, table_end, total;
   int64_t slice;  // floats per split-K slice of the table path (n * r)
   int ks_max;     // table path: split-K slices the partial-sum area holds
 };
@@ -95,14 +112,9 @@ inline WsLayout ws_layout(int32_t n, int32_t h_in, int32_t r) {
   L.rowks_off = L.tile_cnt_off + sizeof(int32_t) * kCounterInts * tiles;
   L.v_off = align_up(L.rowks_off + sizeof(int32_t) * static_cast<size_t>(n), 256);
   L.part_off = align_up(L.v_off + sizeof(float) * static_cast<size_t>(L.slice), 256);
-  const size_t part = sizeof(float) * static_cast<size_t>(L.slice) * L.ks_max;
-  L.pool_off = align_up(L.part_off + part, 256);
-  size_t pool = 0;
-  if (n <= kMaxPoolRows) {
-    const size_t ksp = static_cast<size_t>((h_in + pool_kc(r) - 1) / pool_kc(r));
-    pool = sizeof(uint64_t) * ksp * static_cast<size_t>(n) * pool_part_row(r);
-  }
-  L.total = L.pool_off + pool;
+  L.table_end = align_up(L.part_off + sizeof(float) * static_cast<size_t>(L.slice) * L.ks_max, 256);
+  // 256 bytes of slack so that the tagged partials' start, rounded down, stays past it
+  L.total = L.table_end + 256 + pool_bytes(h_in, r);
   return L;
 }
 

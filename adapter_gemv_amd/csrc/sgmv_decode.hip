@@ -201,7 +201,7 @@ __device__ inline void shrink_item(const PoolArgs& p, const Leader& L, int blk, 
       av[nb][u] = (kk < p.h_in) ? ld16(A + static_cast<int64_t>(nb * 16 + mrow) * p.h_in + kk)
                                 : zero4();
     }
-  const int64_t slice = static_cast<int64_t>(p.n) * pool_part_row(R);
+  const int64_t slice = pool_slice(R);
   const uint32_t bm = static_cast<uint32_t>(L.rows >> (16 * blk)) & 0xffffu;
   const int row = 16 * blk + mrow;
   const gptr<const uint16_t> xr =
@@ -264,7 +264,7 @@ __device__ inline void expand_item(const PoolArgs& p, const Leader& L, int r, in
   // batches of 8, polls each batch until every tag is present and adds it in order; the
   // G lane groups are then combined by a fixed butterfly, so every lane ends with the
   // same sum
-  const int64_t slice = static_cast<int64_t>(p.n) * pool_part_row(R);
+  const int64_t slice = pool_slice(R);
   const uint64_t* src = p.part + static_cast<int64_t>(r) * pool_part_row(R) + (lane % R);
   const int g = lane / R;
   float acc = 0.f;
@@ -443,9 +443,8 @@ extern "C" int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, in
   p.scale = scale;
   char* ws = static_cast<char*>(workspace);
   p.ws_flag = reinterpret_cast<int32_t*>(ws);
-  const WsLayout L = ws_layout(n, h_in, r);
   p.counters = reinterpret_cast<int32_t*>(ws + kWsPoolCounters);
-  p.part = reinterpret_cast<uint64_t*>(ws + L.pool_off);
+  p.part = reinterpret_cast<uint64_t*>(ws + pool_offset(workspace_bytes, h_in, r));
 
   hipError_t e;
   if (dtype == SGMV_F16) {

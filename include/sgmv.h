@@ -115,10 +115,13 @@ int sgmv_build_ptr_table(const uint64_t* adapter_base, int32_t n_adapters,
                          const int32_t* seg_adapter, int32_t n_segments, uint64_t* seg_ptrs);
 
 /*
- * Bytes of device workspace that sgmv_shrink and sgmv_lora_add need for a batch of
- * n rows (fp32 split-K partial sums plus a few counters).  The workspace must be
- * 256-byte aligned and zero-filled once before its first use; every call leaves it
- * ready for the next one.  Returns 0 for invalid sizes.
+ * Bytes of device workspace that sgmv_shrink, sgmv_lora_add and sgmv_lora_add_pool need
+ * for calls of up to n rows, h_in and rank r: float32 split-K partial sums, a few
+ * counters, and the decode path's tagged partial sums, which sit at the end of the
+ * buffer.  The workspace must be 256-byte aligned and zero-filled once before its first
+ * use; every call leaves it ready for the next one.  One workspace may serve any mix of
+ * calls (either path, any shapes) if it is sized with the largest n, h_in and r among
+ * them and the calls are stream-ordered.  Returns 0 for invalid sizes.
  */
 size_t sgmv_workspace_bytes(int32_t n, int32_t h_in, int32_t r);
 

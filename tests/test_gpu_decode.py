@@ -168,9 +168,10 @@ def test_pool_repeat_calls_reset_counters(torch_cuda):
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
     assert int(ws[:16640].view(torch.int32).abs().sum().item()) == 0  # flag and counters at zero
-    # the tagged partial sums (the last region of the workspace) are left at zero too
+    # the tagged partial sums (the end of the workspace, laid out for 64 rows) are left
+    # at zero too
     ks = -(-p.h_in // (8192 // 16))
-    tail = 8 * ks * p.n * 16
+    tail = 8 * ks * 64 * 16 + 256
     assert int(ws[-tail:].view(torch.int32).abs().sum().item()) == 0
     # the table path on the same workspace agrees within tolerance, and a decode-path call
     # after it still gives the same bits
@@ -220,4 +221,36 @@ def test_pool_hip_graph_replay(torch_cuda):
             assert torch.equal(ys[k], ref[k]), f"replay {rep} call {k}"
         _ = (dp.x.float() * 2).sum()                 # eager work between replays
         torch.cuda.synchronize()
+    assert int(ws[:16640].view(torch.int32).abs().sum().item()) == 0
+
+
+def test_shared_workspace_across_shapes(torch_cuda):
+    """One workspace sized for the largest call serves decode-path calls of varying n and
+    h_in interleaved with table-path calls whose scratch is larger: every result matches
+    the oracle, and each decode call gives the same bits as on a fresh workspace."""
+    torch = torch_cuda
+    from adapter_gemv_amd import sgmv
+    big = synth.random_problem((85, 1), n=600, h_in=5120, h_out=1032, r=16, n_adapters=3,
+                               dtype="bf16", id_dist="uniform")
+    dec = [synth.random_problem((85, 2, n, h), n=n, h_in=h, h_out=1032, r=16, n_adapters=40,
+                                dtype="bf16", id_dist="zipf", zipf_s=1.1)
+           for n, h in [(32, 4096), (17, 2048), (64, 5120), (5, 4096)]]
+    ws = sgmv.make_workspace(big.n, big.h_in, 16, torch.device("cuda"))
+    for rep in range(2):
+        for q in dec:
+            _say(f"[shared ws] rep {rep} decode n={q.n} h_in={q.h_in}")
+            dq = _upload(q)
+            y = dq.lora_add_pool(workspace=ws)
+            torch.cuda.synchronize()
+            fresh = dq.lora_add_pool()
+            torch.cuda.synchronize()
+            assert torch.equal(y, fresh)
+            _assert_close(oracle.decode(_storage(y, "bf16"), "bf16"), oracle.lora_add_problem(q),
+                          f"shared ws decode n={q.n}")
+            _say(f"[shared ws] rep {rep} table n={big.n}")
+            db = _upload(big)
+            yb = db.lora_add(workspace=ws)
+            torch.cuda.synchronize()
+            _assert_close(oracle.decode(_storage(yb, "bf16"), "bf16"), oracle.lora_add_problem(big),
+                          "shared ws table")
     assert int(ws[:16640].view(torch.int32).abs().sum().item()) == 0
