@@ -2,6 +2,8 @@
 """SGMV benchmark on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode7b]
+    python bench.py --sweep decode|prefill     (time per call against batch size or
+                                                 prompt length, one JSON line)
 
 One step is one batch through the whole SGMV path, with every input resident in HBM:
   * batches of <= 64 tokens (the decode workloads) take the one-launch path,
@@ -47,10 +49,19 @@ KERNEL_SRCS = [os.path.join(ROOT, "adapter_gemv_amd", "csrc", f)
 
 
 def workload_problem(name: str):
+    """The named workload; also decode7b_bs<N> (N = 1..64 tokens) and
+    prefill13b_<proj>_len<L> (4 requests of L tokens) for the batch sweeps."""
     table = dict(synth.all_workloads())
-    if name not in table:
-        raise SystemExit(f"unknown workload {name!r}; choose from {sorted(table)}")
-    return table[name]()
+    if name in table:
+        return table[name]()
+    if name.startswith("decode7b_bs") and name[11:].isdigit():
+        return synth.decode7b_bs(int(name[11:]))
+    for proj in synth.PREFILL13B_SHAPES:
+        pre = f"prefill13b_{proj}_len"
+        if name.startswith(pre) and name[len(pre):].isdigit():
+            return synth.prefill13b_len(int(name[len(pre):]), proj)
+    raise SystemExit(f"unknown workload {name!r}; choose from {sorted(table)}, "
+                     "decode7b_bs<N>, prefill13b_<proj>_len<L>")
 
 
 def algorithmic_bytes(p) -> int:
@@ -300,6 +311,108 @@ def load_traffic(workload: str, pool_path: bool):
     return int(float(rec["hbm_bytes_per_call"]))
 
 
+def measure(p, device, steps: int, warmup: int, eager: bool = False, force_table: bool = False):
+    """Check slot 0 against the oracle, then time `steps` steps after `warmup` untimed
+    ones: wall time per step, GPU time per step, and the SGMV call's average duration."""
+    import torch
+    rig = Rig(p, device)
+    if force_table:
+        rig.pool_path = False
+    parity = parity_check(rig)
+    print(f"# {p.name}: slots={rig.slots} pool_path={rig.pool_path} parity={parity}",
+          file=sys.stderr, flush=True)
+    use_graph = rig.pool_path and not eager
+    for k in range(warmup):
+        rig.step(1 + k)
+    torch.cuda.synchronize()
+    base = 1 + warmup
+    stream = torch.cuda.current_stream()
+    t_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    if use_graph:
+        # capture the K timed steps (each on its own slot) into one graph
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            rig.step(base)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for k in range(steps):
+                rig.step(base + k)
+        graph.replay()                     # untimed: uploads the graph, K warm steps
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        t_ev[0].record(stream)
+        graph.replay()
+        t_ev[1].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        del graph
+    else:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        t_ev[0].record(stream)
+        for k in range(steps):
+            rig.step(base + k)
+        t_ev[1].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    wall = (t1 - t0) / steps
+    gpu_step = t_ev[0].elapsed_time(t_ev[1]) * 1e-3 / steps
+    if use_graph:
+        # each step is one kernel, replayed back to back: the events over the timed
+        # region give the kernel's average duration
+        call_s = gpu_step
+        call_how = "HIP events over the timed graph replay / K"
+    else:
+        call_s = kernel_pass(rig, base + steps, min(steps, 500))
+        call_how = "HIP events over a graph of the same calls (tables pre-uploaded) / count"
+    flag = int(rig.ws[:4].view(torch.int32).item())
+    return dict(rig=rig, parity=parity, use_graph=use_graph, wall=wall, gpu_step=gpu_step,
+                call_s=call_s, call_how=call_how, flag=flag)
+
+
+SWEEPS = {
+    # the pages' idea I5: latency against batch size, per stage
+    "decode": [f"decode7b_bs{n}" for n in (1, 2, 4, 8, 16, 24, 32, 48, 64)],
+    "prefill": [f"prefill13b_gateup_len{L}" for L in (16, 32, 64, 128, 256, 512, 1024)],
+}
+
+
+def run_sweep(kind: str, device, args) -> int:
+    """SGMV time per call against batch size (decode shape) or prompt length (prefill
+    shape); one JSON line with one entry per point."""
+    import torch
+    points = []
+    ok = True
+    for name in SWEEPS[kind]:
+        p = workload_problem(name)
+        steps = args.steps if kind == "decode" else max(20, args.steps // 20)
+        m = measure(p, device, steps, min(args.warmup, steps), eager=args.eager)
+        nbytes = algorithmic_bytes(p)
+        points.append({
+            "workload": p.name, "n_tokens": p.n, "distinct_adapters": p.distinct_adapters(),
+            "path": "one launch (sgmv_lora_add_pool)" if m["rig"].pool_path else
+                    "table (sgmv_lora_add)",
+            "us_per_call": round(m["call_s"] * 1e6, 3),
+            "us_per_step": round(m["wall"] * 1e6, 3),
+            "algorithmic_bytes_per_call": nbytes,
+            "GB_per_s": round(nbytes / m["call_s"] / 1e9, 2),
+            "frac_of_hbm_peak": round(nbytes / m["call_s"] / 1e9 / HBM_PEAK_GBS, 4),
+            "parity_ok": m["parity"]["ok"] and m["flag"] == 0,
+        })
+        ok = ok and points[-1]["parity_ok"]
+        del m
+        torch.cuda.empty_cache()
+    print(json.dumps({
+        "metric": f"SGMV us/call against {'batch size' if kind == 'decode' else 'prompt length'}",
+        "sweep": kind, "unit": "us", "higher_is_better": False, "n_gpus": 1,
+        "data": "synthetic", "cache": "cold (rotating slots)", "points": points,
+    }), flush=True)
+    return 0 if ok else 1
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -311,6 +424,8 @@ def main(argv=None) -> int:
                     help="auto: one-launch path for batches of <= 64 tokens")
     ap.add_argument("--eager", action="store_true", help="no HIP graph on the one-launch path")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--sweep", choices=sorted(SWEEPS),
+                    help="time a batch-size (decode) or prompt-length (prefill) sweep instead")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args(argv)
@@ -337,61 +452,15 @@ def main(argv=None) -> int:
         print(json.dumps({"copy_probe_bytes": 2 * n}))
         return 0
 
-    p = workload_problem(args.workload)
-    rig = Rig(p, device)
-    if args.path == "table":
-        rig.pool_path = False
-    parity = parity_check(rig)
-    print(f"# {p.name}: slots={rig.slots} pool_path={rig.pool_path} parity={parity}",
-          file=sys.stderr, flush=True)
-    use_graph = rig.pool_path and not args.eager
+    if args.sweep:
+        return run_sweep(args.sweep, device, args)
 
-    for k in range(args.warmup):
-        rig.step(1 + k)
-    torch.cuda.synchronize()
-    base = 1 + args.warmup
-    stream = torch.cuda.current_stream()
-    t_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    if use_graph:
-        # capture the K timed steps (each on its own slot) into one graph
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            rig.step(base)
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for k in range(args.steps):
-                rig.step(base + k)
-        graph.replay()                     # untimed: uploads the graph, K warm steps
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        t_ev[0].record(stream)
-        graph.replay()
-        t_ev[1].record(stream)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-    else:
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        t_ev[0].record(stream)
-        for k in range(args.steps):
-            rig.step(base + k)
-        t_ev[1].record(stream)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-    wall = (t1 - t0) / args.steps
-    gpu_step = t_ev[0].elapsed_time(t_ev[1]) * 1e-3 / args.steps
-    if use_graph:
-        # each step is one kernel, replayed back to back: the events over the timed
-        # region give the kernel's average duration
-        call_s = gpu_step
-        call_how = "HIP events over the timed graph replay / K"
-    else:
-        call_s = kernel_pass(rig, base + args.steps, min(args.steps, 500))
-        call_how = "HIP events over a graph of the same calls (tables pre-uploaded) / count"
-    flag = int(rig.ws[:4].view(torch.int32).item())
+    p = workload_problem(args.workload)
+    m = measure(p, device, args.steps, args.warmup, eager=args.eager,
+                force_table=args.path == "table")
+    rig, parity, use_graph = m["rig"], m["parity"], m["use_graph"]
+    wall, gpu_step, call_s, call_how, flag = (m["wall"], m["gpu_step"], m["call_s"],
+                                              m["call_how"], m["flag"])
 
     nbytes = algorithmic_bytes(p)
     flops = algorithmic_flops(p)

@@ -218,6 +218,26 @@ def mixed70b(proj: str, r: int) -> Problem:
                           name=f"mixed70b_r{r}_{proj}")
 
 
+def decode7b_bs(n: int) -> Problem:
+    """The 7B decode projection at batch size n (1..64): n tokens, each on its own adapter
+    (a seeded permutation of ids 0..n-1), h = 4096, r = 16, fp16, scale 2."""
+    assert 1 <= n <= 64
+    return random_problem((6, n), n=n, h_in=4096, h_out=4096, r=16, n_adapters=n,
+                          dtype=F16, scale=2.0, id_dist="permutation",
+                          name=f"decode7b_bs{n}")
+
+
+def prefill13b_len(length: int, proj: str = "gateup") -> Problem:
+    """The 13B prefill projection with 4 requests of `length` tokens each (request-major
+    rows, each request on its own adapter), r = 16, bf16, scale 2."""
+    h_in, h_out = PREFILL13B_SHAPES[proj]
+    rng = _streams((7, length), 6)[5]
+    ids = np.repeat(rng.permutation(4).astype(np.int32), length)
+    return random_problem((7, length, h_in), n=4 * length, h_in=h_in, h_out=h_out, r=16,
+                          n_adapters=4, dtype=BF16, scale=2.0, ids=ids,
+                          name=f"prefill13b_{proj}_len{length}")
+
+
 def all_workloads(include_large: bool = True):
     """(name, factory) pairs for every workload projection."""
     out = [("tiny", tiny), ("decode7b", decode7b)]
