@@ -4,6 +4,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode7b]
     python bench.py --sweep decode|prefill     (time per call against batch size or
                                                  prompt length, one JSON line)
+    python bench.py --layer                    (backbone GEMM alone vs the LoRA layer)
 
 One step is one batch through the whole SGMV path, with every input resident in HBM:
   * batches of <= 64 tokens (the decode workloads) take the one-launch path,
@@ -373,6 +374,116 @@ def measure(p, device, steps: int, warmup: int, eager: bool = False, force_table
                 call_s=call_s, call_how=call_how, flag=flag)
 
 
+def layer_measure(p, device, steps: int) -> dict:
+    """The LoRA linear layer end to end: the backbone y = x @ W (one torch matrix product,
+    hipBLASLt, shared by every request) and then the SGMV add-on on the same stream.
+    Times K steps of the backbone alone and K steps of the whole layer, each captured in
+    one HIP graph (table-path segment tables are uploaded before capture).  Parity: the
+    layer output of slot 0 against the oracle applied to the GPU backbone's output."""
+    import torch
+    import oracle
+    from adapter_gemv_amd import sgmv
+    from adapter_gemv_amd.device_problem import to_numpy_storage
+    rig = Rig(p, device)
+    tdt = rig.x.dtype
+    g = torch.Generator(device=device)
+    g.manual_seed(4321)
+    # W stored as [h_in, h_out] so the product needs no transposed view
+    Wt = (torch.randn((p.h_in, p.h_out), generator=g, device=device) / np.sqrt(p.h_in)).to(tdt)
+    st = torch.cuda.current_stream()
+    tables = {}
+
+    def sgmv_call(k):
+        slot = k % rig.slots
+        if rig.pool_path:
+            rig.step_pool(k)
+            return
+        b = tables[slot]
+        t = b.table
+        rc = sgmv.sgmv_lora_add(torch.cuda.current_stream().cuda_stream, rig.dtype_code,
+                                rig.y[slot].data_ptr(), rig.ld_y,
+                                rig.x[slot].data_ptr(), rig.ld_x, b.A_ptrs_addr, b.B_ptrs_addr,
+                                b.seg_starts_addr, b.perm_addr, t.n, t.n_segments,
+                                t.min_seg_len, t.max_seg_len, p.h_in, p.h_out, p.r, p.scale,
+                                rig.ws.data_ptr(), rig.ws.numel())
+        if rc != 0:
+            raise RuntimeError(sgmv.sgmv_status_string(rc))
+
+    def gemm(k):
+        slot = k % rig.slots
+        torch.mm(rig.x[slot], Wt, out=rig.y[slot])
+
+    count = min(steps, rig.slots * 4)
+    if not rig.pool_path:
+        for k in range(count + 1):
+            slot = k % rig.slots
+            if slot not in tables:
+                tables[slot] = sgmv.Batch.build(rig.ids[slot], rig.A, rig.B)
+    # parity on slot 0
+    gemm(0)
+    torch.cuda.synchronize()
+    y_bb = to_numpy_storage(rig.y[0], p.dtype).copy()
+    sgmv_call(0)
+    torch.cuda.synchronize()
+    got = oracle.decode(to_numpy_storage(rig.y[0], p.dtype), p.dtype)
+    ref = oracle.lora_add(y_bb, p.x, p.ids, p.A, p.B, p.scale, p.dtype)
+    err = np.abs(got - ref)
+    tol = 1e-2 + 1e-2 * np.abs(ref)
+    parity = {"max_abs_err": float(err.max()), "worst_err_over_tol": float((err / tol).max()),
+              "ok": bool(np.all(err <= tol))}
+
+    def timed(body):
+        side = torch.cuda.Stream()
+        side.wait_stream(st)
+        with torch.cuda.stream(side):
+            for k in range(3):
+                body(1 + k)
+        st.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for k in range(count):
+                body(1 + k)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        graph.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / count
+
+    def layer(k):
+        gemm(k)
+        sgmv_call(k)
+
+    t_gemm = timed(gemm)
+    t_layer = timed(layer)
+    return {"workload": p.name, "n_tokens": p.n, "h_in": p.h_in, "h_out": p.h_out, "r": p.r,
+            "path": "one launch (sgmv_lora_add_pool)" if rig.pool_path else "table (sgmv_lora_add)",
+            "steps": count, "backbone_us": round(t_gemm * 1e6, 3), "layer_us": round(t_layer * 1e6, 3),
+            "sgmv_added_us": round((t_layer - t_gemm) * 1e6, 3),
+            "sgmv_overhead_frac": round((t_layer - t_gemm) / t_gemm, 4), "parity": parity}
+
+
+LAYER_WORKLOADS = ["decode7b", "sweep_b", "prefill13b_qo", "prefill13b_gateup", "prefill13b_down",
+                   "mixed70b_r16_gate", "mixed70b_r64_gate"]
+
+
+def run_layer(device, args) -> int:
+    """One JSON line: backbone GEMM vs the whole LoRA layer for each layer workload."""
+    import torch
+    rows = []
+    for name in LAYER_WORKLOADS:
+        rows.append(layer_measure(workload_problem(name), device, args.steps))
+        print(f"# {json.dumps(rows[-1])}", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "LoRA linear layer: backbone GEMM alone vs GEMM + SGMV, us per call",
+                      "unit": "us", "higher_is_better": False, "n_gpus": 1, "data": "synthetic",
+                      "cache": "cold (rotating slots)", "points": rows}), flush=True)
+    return 0 if all(r["parity"]["ok"] for r in rows) else 1
+
+
 SWEEPS = {
     # the pages' idea I5: latency against batch size, per stage
     "decode": [f"decode7b_bs{n}" for n in (1, 2, 4, 8, 16, 24, 32, 48, 64)],
@@ -426,6 +537,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--sweep", choices=sorted(SWEEPS),
                     help="time a batch-size (decode) or prompt-length (prefill) sweep instead")
+    ap.add_argument("--layer", action="store_true",
+                    help="time the LoRA linear layer (backbone GEMM + SGMV) on several workloads")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args(argv)
@@ -454,6 +567,8 @@ def main(argv=None) -> int:
 
     if args.sweep:
         return run_sweep(args.sweep, device, args)
+    if args.layer:
+        return run_layer(device, args)
 
     p = workload_problem(args.workload)
     m = measure(p, device, args.steps, args.warmup, eager=args.eager,

@@ -313,3 +313,30 @@ def test_deterministic_and_workspace_reuse(torch_cuda, dtype):
     outs = [dp.lora_add(workspace=ws) for _ in range(3)]
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+
+
+# --------------------------------------------------------------------------------------
+# the LoRA linear layer end to end (backbone GEMM + SGMV on one stream, graph-captured)
+# --------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["decode7b", "tiny"])
+def test_lora_layer_end_to_end(torch_cuda, name):
+    import bench
+    _say(f"[layer] {name}")
+    p = FACT[name]() if name in FACT else bench.workload_problem(name)
+    r = bench.layer_measure(p, torch_cuda.device("cuda:0"), 8)
+    _say(f"[layer] {name}: {r}")
+    assert r["parity"]["ok"], r["parity"]
+    assert r["layer_us"] > 0 and r["backbone_us"] > 0
+
+
+def test_lora_layer_table_path(torch_cuda):
+    """A prefill-sized layer through the table path (segment tables uploaded before
+    graph capture)."""
+    import bench
+    _say("[layer] table path")
+    p = synth.random_problem((91,), n=300, h_in=1032, h_out=776, r=16, n_adapters=3,
+                             dtype="bf16", id_dist="uniform")
+    r = bench.layer_measure(p, torch_cuda.device("cuda:0"), 8)
+    _say(f"[layer] table: {r}")
+    assert r["path"].startswith("table")
+    assert r["parity"]["ok"], r["parity"]
