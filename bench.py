@@ -5,6 +5,7 @@
     python bench.py --sweep decode|prefill     (time per call against batch size or
                                                  prompt length, one JSON line)
     python bench.py --layer                    (backbone GEMM alone vs the LoRA layer)
+    python bench.py --load                     (adapter uploads, host to HBM)
 
 One step is one batch through the whole SGMV path, with every input resident in HBM:
   * batches of <= 64 tokens (the decode workloads) take the one-launch path,
@@ -484,6 +485,48 @@ def run_layer(device, args) -> int:
     return 0 if all(r["parity"]["ok"] for r in rows) else 1
 
 
+def run_load(device, args) -> int:
+    """Adapter loading: host-to-HBM copies of LoRA adapters into a device adapter pool,
+    from pinned and from pageable host memory, timed with HIP events; every copy is
+    read back and compared bit for bit.  Sizes are Llama2-7B LoRA adapters at r = 16
+    (fp16): one projection pair, q/k/v/o over 32 layers, and all seven projections."""
+    import torch
+    r, h, f, layers = 16, 4096, 11008, 32
+    pair = 2 * r * h
+    qkvo = layers * 4 * pair
+    full = layers * (4 * pair + 2 * r * (h + f) + r * (f + h))
+    rows = []
+    ok = True
+    st = torch.cuda.current_stream()
+    for label, elems in [("one projection (A and B, 4096 x 16)", pair),
+                         ("q/k/v/o, 32 layers", qkvo), ("all 7 projections, 32 layers", full)]:
+        for pinned in (True, False):
+            src = torch.randn(elems, dtype=torch.float32).to(torch.float16)
+            if pinned:
+                src = src.pin_memory()
+            dst = torch.empty(elems, dtype=torch.float16, device=device)
+            for _ in range(3):
+                dst.copy_(src, non_blocking=pinned)
+            torch.cuda.synchronize()
+            reps = 20
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(reps):
+                dst.copy_(src, non_blocking=pinned)
+            e1.record(st)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / reps
+            same = bool(torch.equal(dst.cpu().view(torch.int16), src.view(torch.int16)))
+            ok = ok and same
+            rows.append({"adapter": label, "bytes": 2 * elems, "host_memory": "pinned" if pinned else "pageable",
+                         "ms_per_upload": round(t * 1e3, 4), "GB_per_s": round(2 * elems / t / 1e9, 2),
+                         "bit_exact": same})
+            del src, dst
+    print(json.dumps({"metric": "LoRA adapter upload, host to HBM", "unit": "ms", "higher_is_better": False,
+                      "n_gpus": 1, "data": "synthetic", "points": rows}), flush=True)
+    return 0 if ok else 1
+
+
 SWEEPS = {
     # the pages' idea I5: latency against batch size, per stage
     "decode": [f"decode7b_bs{n}" for n in (1, 2, 4, 8, 16, 24, 32, 48, 64)],
@@ -539,6 +582,8 @@ def main(argv=None) -> int:
                     help="time a batch-size (decode) or prompt-length (prefill) sweep instead")
     ap.add_argument("--layer", action="store_true",
                     help="time the LoRA linear layer (backbone GEMM + SGMV) on several workloads")
+    ap.add_argument("--load", action="store_true",
+                    help="time LoRA adapter uploads from host memory into HBM")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args(argv)
@@ -569,6 +614,8 @@ def main(argv=None) -> int:
         return run_sweep(args.sweep, device, args)
     if args.layer:
         return run_layer(device, args)
+    if args.load:
+        return run_load(device, args)
 
     p = workload_problem(args.workload)
     m = measure(p, device, args.steps, args.warmup, eager=args.eager,
