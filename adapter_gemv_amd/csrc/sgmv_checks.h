@@ -61,7 +61,10 @@ inline int check_device() {
 //   [tile_cnt_off, ...)     table path: one counter per shrink tile, one per 256-byte line
 //   [rowks_off, ...)        table path: split-K slice count of each sorted row
 //   [v_off, ...)            table path: final float32 v of rows of long segments
-//   [part_off, table_end)   table path: float32 split-K partial sums
+//   [part_off, ...)         table path: float32 split-K partial sums
+//   [dtab_off, table_end)   segment tables built on the device for n > 64 (meta word
+//                           [S, min_len, max_len, n_valid], n_segments, perm, seg_starts,
+//                           seg_adapter, sorted ids, A and B pointer tables)
 //   last pool_bytes(h_in, r) bytes of the caller's buffer (start rounded down to 256):
 //                           decode path: tagged 64-bit split-K partial sums, laid out
 //                           for 64 rows whatever n is
@@ -95,8 +98,32 @@ inline size_t pool_offset(size_t ws_bytes, int32_t h_in, int32_t r) {
   return (ws_bytes - pool_bytes(h_in, r)) / 256 * 256;
 }
 
+// rows the one-workgroup device sort handles (sgmv_build_segments_device and the decode
+// entry point for 64 < n <= kDevSortMax)
+constexpr int kDevSortMax = 4096;
+
+// device segment tables inside the workspace, offsets from dtab_off
+struct DevTabLayout {
+  size_t meta, n_segments, perm, seg_starts, seg_adapter, sorted_ids, A_ptrs, B_ptrs, bytes;
+};
+
+inline DevTabLayout dev_tab_layout(int32_t n) {
+  DevTabLayout D{};
+  const size_t nn = static_cast<size_t>(n);
+  D.meta = 0;
+  D.n_segments = 16;
+  D.perm = 256;
+  D.seg_starts = align_up(D.perm + 4 * nn, 256);
+  D.seg_adapter = align_up(D.seg_starts + 4 * (nn + 1), 256);
+  D.sorted_ids = align_up(D.seg_adapter + 4 * nn, 256);
+  D.A_ptrs = align_up(D.sorted_ids + 4 * nn, 256);
+  D.B_ptrs = align_up(D.A_ptrs + 8 * nn, 256);
+  D.bytes = align_up(D.B_ptrs + 8 * nn, 256);
+  return D;
+}
+
 struct WsLayout {
-  size_t tile_cnt_off, rowks_off, v_off, part_off, table_end, total;
+  size_t tile_cnt_off, rowks_off, v_off, part_off, dtab_off, table_end, total;
   int64_t slice;  // floats per split-K slice of the table path (n * r)
   int ks_max;     // table path: split-K slices the partial-sum area holds
 };
@@ -112,10 +139,21 @@ inline WsLayout ws_layout(int32_t n, int32_t h_in, int32_t r) {
   L.rowks_off = L.tile_cnt_off + sizeof(int32_t) * kCounterInts * tiles;
   L.v_off = align_up(L.rowks_off + sizeof(int32_t) * static_cast<size_t>(n), 256);
   L.part_off = align_up(L.v_off + sizeof(float) * static_cast<size_t>(L.slice), 256);
-  L.table_end = align_up(L.part_off + sizeof(float) * static_cast<size_t>(L.slice) * L.ks_max, 256);
+  L.dtab_off = align_up(L.part_off + sizeof(float) * static_cast<size_t>(L.slice) * L.ks_max, 256);
+  L.table_end = L.dtab_off + dev_tab_layout(n).bytes;
   // 256 bytes of slack so that the tagged partials' start, rounded down, stays past it
   L.total = L.table_end + 256 + pool_bytes(h_in, r);
   return L;
 }
+
+// The table path on segment tables that live on the device (sgmv_kernels.hip): the
+// tables and their meta word [S, min_len, max_len, n_valid] as written by the device sort;
+// S_max bounds S.
+hipError_t table_lora_add_device(hipStream_t st, int32_t dtype, int32_t r, void* y, int64_t ld_y,
+                                 const void* x, int64_t ld_x, const void* const* A_ptrs,
+                                 const void* const* B_ptrs, const int32_t* seg_starts,
+                                 const int32_t* perm, const int32_t* meta, int32_t n,
+                                 int32_t S_max, int32_t h_in, int32_t h_out, float scale,
+                                 void* workspace);
 
 }  // namespace sgmv_host

@@ -138,6 +138,178 @@ __global__ __launch_bounds__(64) void segments_from_ids_kernel(
 }
 
 // ------------------------------------------------------------------------------------
+// a1 on the device for up to kDevSortMax rows: rank by counting, then one scan
+// ------------------------------------------------------------------------------------
+// Row i's sorted position is the number of valid rows with a smaller id plus the number
+// of earlier rows with the same id: the stable sort by adapter id.  rank_kernel computes
+// it for every row (each workgroup holds all ids in LDS and each thread counts for one
+// row) and scatters the row and its id to that position.  tables_kernel, one workgroup,
+// then finds the segment starts in the sorted ids (where the id changes), numbers them
+// with an exclusive scan and writes the tables.  Rows with an id outside [0, n_adapters)
+// are left out (their perm entries are -1 past the valid rows).
+struct SortOut {
+  int32_t* perm;            // [n]
+  int32_t* seg_starts;      // [S + 1]
+  int32_t* seg_adapter;     // [S]
+  int32_t* n_segments;      // [1]: S, or -1 if an id was out of range
+  int32_t* sorted_ids;      // [n] scratch: the id at each sorted position
+  int32_t* meta;            // nullable: [S, min_len, max_len, n_valid]
+  const uint16_t** A_ptrs;  // nullable: per-segment pointers into the pools
+  const uint16_t** B_ptrs;
+  const uint16_t* A_pool;
+  const uint16_t* B_pool;
+  int64_t A_stride, B_stride;
+  int32_t* ws_flag;         // nullable: set to 2 if an id was out of range
+};
+
+constexpr int kRankThreads = 256;  // 4 waves: 64 rows per workgroup, ids split in quarters
+constexpr int kRankRows = 64;
+constexpr int kTabThreads = 1024;
+constexpr int32_t kNoId = 0x7fffffff;  // larger than every valid id
+
+__global__ __launch_bounds__(kRankThreads) void rank_kernel(const int32_t* __restrict__ ids,
+                                                            int32_t n, int32_t n_adapters,
+                                                            SortOut o) {
+  __shared__ __attribute__((aligned(16))) int32_t sid[kDevSortMax + 16];
+  __shared__ int part[kRankThreads / 64][kRankRows];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n16 = (n + 15) / 16 * 16;
+  for (int j = tid; j < n16; j += kRankThreads) {
+    int v = kNoId;
+    if (j < n) {
+      const int id = ids[j];
+      if (id >= 0 && id < n_adapters) v = id;
+    }
+    sid[j] = v;
+  }
+  __syncthreads();
+  const int i = blockIdx.x * kRankRows + lane;
+  const int me = (i < n) ? sid[i] : kNoId;
+  // wave w counts over ids [j0, j1), 16 at a time (four 16-byte LDS reads in flight)
+  const int quarter = (n16 / 16 + 3) / 4 * 16;
+  const int j0 = w * quarter, j1 = min(n16, j0 + quarter);
+  int before = 0;
+  for (int j = j0; j < j1; j += 16) {
+    int4 q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) q[u] = *reinterpret_cast<const int4*>(&sid[j + 4 * u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int jj = j + 4 * u;
+      before += (q[u].x < me) + (q[u].y < me) + (q[u].z < me) + (q[u].w < me);
+      before += (q[u].x == me && jj < i) + (q[u].y == me && jj + 1 < i) +
+                (q[u].z == me && jj + 2 < i) + (q[u].w == me && jj + 3 < i);
+    }
+  }
+  part[w][lane] = before;
+  __syncthreads();
+  if (w == 0 && i < n && me != kNoId) {
+    const int pos = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+    o.perm[pos] = i;
+    o.sorted_ids[pos] = me;
+  }
+}
+
+__global__ __launch_bounds__(kTabThreads) void tables_kernel(const int32_t* __restrict__ ids,
+                                                              int32_t n, int32_t n_adapters,
+                                                              SortOut o) {
+  constexpr int T = kTabThreads, PER = kDevSortMax / kTabThreads;
+  __shared__ int32_t sid[kDevSortMax];
+  __shared__ int pos[kDevSortMax + 1];
+  __shared__ int wsum[T / 64];
+  __shared__ int s_valid, s_bad, s_min, s_max, s_S;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid == 0) {
+    s_valid = 0;
+    s_bad = 0;
+    s_min = 0x7fffffff;
+    s_max = 0;
+  }
+  __syncthreads();
+  // the ids (to count the valid rows) and the sorted ids are read in the same round; the
+  // sorted ids past the valid rows are stale and never looked at
+  int nv = 0;
+  for (int i = tid; i < n; i += T) {
+    const int id = ids[i];
+    sid[i] = o.sorted_ids[i];
+    if (id >= 0 && id < n_adapters) ++nv;
+  }
+  if (nv) atomicAdd(&s_valid, nv);
+  __syncthreads();
+  const int n_valid = s_valid;
+  if (tid == 0 && n_valid < n) s_bad = 1;
+  for (int p = n_valid + tid; p < n; p += T) o.perm[p] = -1;
+  // thread t takes sorted positions PER*t .. PER*t + PER-1
+  int starts = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int p = PER * tid + u;
+    if (p < n_valid && (p == 0 || sid[p - 1] != sid[p])) ++starts;
+  }
+  int incl = starts;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int up = __shfl_up(incl, d);
+    if (lane >= d) incl += up;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int q = 0; q < T / 64; ++q) {
+    if (q < wv) before += wsum[q];
+    total += wsum[q];
+  }
+  int seg = before + incl - starts;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int p = PER * tid + u;
+    if (p < n_valid && (p == 0 || sid[p - 1] != sid[p])) {
+      pos[seg] = p;
+      o.seg_starts[seg] = p;
+      o.seg_adapter[seg] = sid[p];
+      ++seg;
+    }
+  }
+  if (tid == 0) {
+    pos[total] = n_valid;
+    o.seg_starts[total] = n_valid;
+    s_S = total;
+  }
+  __syncthreads();
+  const int S = s_S;
+  for (int sg = tid; sg < S; sg += T) {
+    const int len = pos[sg + 1] - pos[sg];
+    atomicMin(&s_min, len);
+    atomicMax(&s_max, len);
+    if (o.A_ptrs) {
+      const int64_t a = sid[pos[sg]];
+      o.A_ptrs[sg] = o.A_pool + a * o.A_stride;
+      o.B_ptrs[sg] = o.B_pool + a * o.B_stride;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    o.n_segments[0] = s_bad ? -1 : S;
+    if (o.meta) {
+      o.meta[0] = S;
+      o.meta[1] = S ? s_min : 0;
+      o.meta[2] = s_max;
+      o.meta[3] = n_valid;
+    }
+    if (s_bad && o.ws_flag)
+      __hip_atomic_store(o.ws_flag, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+inline hipError_t launch_device_sort(hipStream_t st, const int32_t* ids, int32_t n,
+                                     int32_t n_adapters, const SortOut& o) {
+  hipLaunchKernelGGL(rank_kernel, dim3((n + kRankRows - 1) / kRankRows), dim3(kRankThreads), 0, st,
+                     ids, n, n_adapters, o);
+  hipLaunchKernelGGL(tables_kernel, dim3(1), dim3(kTabThreads), 0, st, ids, n, n_adapters, o);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------
 // fused shrink + expand
 // ------------------------------------------------------------------------------------
 // Work items are keyed by a *leader* row: the first caller row of each adapter.  One
@@ -388,13 +560,25 @@ extern "C" int sgmv_build_segments_device(hipStream_t stream, const int32_t* ada
                                           int32_t n, int32_t n_adapters, int32_t* perm,
                                           int32_t* seg_starts, int32_t* seg_adapter,
                                           int32_t* n_segments) {
-  if (n < 0 || n > kPoolMaxN || n_adapters <= 0 || n_adapters > (1 << 24)) return SGMV_ERR_SHAPE;
+  if (n < 0 || n > kDevSortMax || n_adapters <= 0 || n_adapters > (1 << 24)) return SGMV_ERR_SHAPE;
   if (!seg_starts || !n_segments || (n > 0 && (!adapter_ids || !perm || !seg_adapter)))
     return SGMV_ERR_NULL;
   int st = check_device();
   if (st) return st;
-  hipLaunchKernelGGL(segments_from_ids_kernel, dim3(1), dim3(64), 0, stream, adapter_ids, n,
-                     n_adapters, perm, seg_starts, seg_adapter, n_segments);
+  if (n <= kPoolMaxN) {
+    hipLaunchKernelGGL(segments_from_ids_kernel, dim3(1), dim3(64), 0, stream, adapter_ids, n,
+                       n_adapters, perm, seg_starts, seg_adapter, n_segments);
+  } else {
+    // the sorted ids go to seg_adapter first (it has n entries); tables_kernel reads them
+    // into LDS before it writes the segments' adapters there
+    SortOut o{};
+    o.perm = perm;
+    o.seg_starts = seg_starts;
+    o.seg_adapter = seg_adapter;
+    o.n_segments = n_segments;
+    o.sorted_ids = seg_adapter;
+    return hip_status(launch_device_sort(stream, adapter_ids, n, n_adapters, o));
+  }
   return hip_status(hipGetLastError());
 }
 
@@ -406,7 +590,7 @@ extern "C" int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, in
                                   void* workspace, size_t workspace_bytes) {
   if (dtype != SGMV_F16 && dtype != SGMV_BF16) return SGMV_ERR_UNSUPPORTED;
   if (!rank_ok(r)) return SGMV_ERR_UNSUPPORTED;
-  if (n < 0 || n > kPoolMaxN || n_adapters <= 0 || n_adapters > (1 << 24)) return SGMV_ERR_SHAPE;
+  if (n < 0 || n > kDevSortMax || n_adapters <= 0 || n_adapters > (1 << 24)) return SGMV_ERR_SHAPE;
   int st = check_dim(h_in, ld_x);
   if (st) return st;
   if ((st = check_dim(h_out, ld_y))) return st;
@@ -423,6 +607,35 @@ extern "C" int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, in
       (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return SGMV_ERR_WORKSPACE;
   if ((st = check_device())) return st;
+
+  if (n > kPoolMaxN) {
+    // device sort into the workspace, then the table path on those tables
+    char* wsb = static_cast<char*>(workspace);
+    const WsLayout L = ws_layout(n, h_in, r);
+    const DevTabLayout D = dev_tab_layout(n);
+    char* dt = wsb + L.dtab_off;
+    SortOut o{};
+    o.perm = reinterpret_cast<int32_t*>(dt + D.perm);
+    o.seg_starts = reinterpret_cast<int32_t*>(dt + D.seg_starts);
+    o.seg_adapter = reinterpret_cast<int32_t*>(dt + D.seg_adapter);
+    o.n_segments = reinterpret_cast<int32_t*>(dt + D.n_segments);
+    o.meta = reinterpret_cast<int32_t*>(dt + D.meta);
+    o.A_ptrs = reinterpret_cast<const uint16_t**>(dt + D.A_ptrs);
+    o.B_ptrs = reinterpret_cast<const uint16_t**>(dt + D.B_ptrs);
+    o.A_pool = static_cast<const uint16_t*>(A_pool);
+    o.B_pool = static_cast<const uint16_t*>(B_pool);
+    o.A_stride = A_stride;
+    o.B_stride = B_stride;
+    o.ws_flag = reinterpret_cast<int32_t*>(wsb);
+    o.sorted_ids = reinterpret_cast<int32_t*>(dt + D.sorted_ids);
+    hipError_t e = launch_device_sort(stream, adapter_ids, n, n_adapters, o);
+    if (e != hipSuccess) return hip_status(e);
+    const int32_t S_max = n < n_adapters ? n : n_adapters;
+    return hip_status(table_lora_add_device(
+        stream, dtype, r, y, ld_y, x, ld_x, reinterpret_cast<const void* const*>(o.A_ptrs),
+        reinterpret_cast<const void* const*>(o.B_ptrs), o.seg_starts, o.perm, o.meta, n, S_max,
+        h_in, h_out, scale, workspace));
+  }
 
   PoolArgs p;
   p.y = static_cast<uint16_t*>(y);

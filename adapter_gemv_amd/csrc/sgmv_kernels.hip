@@ -50,13 +50,19 @@ template <int DT, int R>
 __global__ __launch_bounds__(256) void shrink_gemv_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, const uint16_t* const* __restrict__ A_ptrs,
     const int32_t* __restrict__ seg_starts, const int32_t* __restrict__ perm, int32_t h_in,
-    float* __restrict__ part, int64_t slice, int32_t* __restrict__ rowks, int32_t ks) {
+    float* __restrict__ part, int64_t slice, int32_t* __restrict__ rowks, int32_t ks,
+    const int32_t* __restrict__ meta) {
   using C = GemvCfg<R>;
   __shared__ float red[4][kShortMax][R];
-  const int s = blockIdx.x, kc = blockIdx.y;
+  const int kc = blockIdx.y;
+  // segments blockIdx.x, + gridDim.x, ... (the count comes from the device tables' meta
+  // word when the tables were built on the device)
+  const int S = meta ? meta[0] : static_cast<int>(gridDim.x);
+  if (meta && meta[1] >= kLongMin) return;  // no short segment at all
+  for (int s = blockIdx.x; s < S; s += gridDim.x) {
   const int seg0 = seg_starts[s];
   const int m = seg_starts[s + 1] - seg0;
-  if (m <= 0 || m >= kLongMin) return;
+  if (m <= 0 || m >= kLongMin) continue;  // uniform
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int j = lane % R, g = lane / R;
   const int kbase = kc * C::KC + w * C::WAVE_K + g * 8 * C::KV;
@@ -99,6 +105,8 @@ __global__ __launch_bounds__(256) void shrink_gemv_kernel(
   }
   if (kc == 0)
     for (int i = threadIdx.x; i < m; i += 256) rowks[seg0 + i] = ks;
+  __syncthreads();  // red is reused by the next segment
+  }
 }
 
 // Lane owns CPL = 128/R consecutive output columns: its block of B (CPL rows of the
@@ -107,16 +115,19 @@ template <int DT, int R>
 __global__ __launch_bounds__(64) void expand_gemv_kernel(
     uint16_t* __restrict__ y, int64_t ld_y, const float* __restrict__ vsrc, int64_t slice,
     int32_t ks, const uint16_t* const* __restrict__ B_ptrs, const int32_t* __restrict__ seg_starts,
-    const int32_t* __restrict__ perm, int32_t h_out, float scale) {
+    const int32_t* __restrict__ perm, int32_t h_out, float scale,
+    const int32_t* __restrict__ meta) {
   using E = Elem<DT>;
   constexpr int CPL = 128 / R;
   constexpr int NV = 16;  // CPL * R / 8
   constexpr int YW = CPL / 2;  // 32-bit words of y per lane and row
   __shared__ float vs[kShortMax][R];
-  const int s = blockIdx.x;
+  const int S = meta ? meta[0] : static_cast<int>(gridDim.x);
+  if (meta && meta[1] >= kLongMin) return;  // no short segment at all
+  for (int s = blockIdx.x; s < S; s += gridDim.x) {
   const int seg0 = seg_starts[s];
   const int m = seg_starts[s + 1] - seg0;
-  if (m <= 0 || m >= kLongMin) return;
+  if (m <= 0 || m >= kLongMin) continue;  // uniform
   const int lane = threadIdx.x;
   const int c0 = (blockIdx.y * 64 + lane) * CPL;
   const bool cin = c0 < h_out;
@@ -142,11 +153,10 @@ __global__ __launch_bounds__(64) void expand_gemv_kernel(
     vs[i][jj] = sum_slices(vsrc + static_cast<int64_t>(seg0 + i) * R + jj, slice, ks);
   }
   __syncthreads();
-  if (!cin) return;
 
 #pragma unroll
   for (int i = 0; i < kShortMax; ++i) {
-    if (i >= m) continue;
+    if (i >= m || !cin) continue;
     float out[CPL];
 #pragma unroll
     for (int cc = 0; cc < CPL; ++cc) {
@@ -164,6 +174,8 @@ __global__ __launch_bounds__(64) void expand_gemv_kernel(
 #pragma unroll
     for (int q = 0; q < YW; ++q) packed[q] = E::pack(out[2 * q], out[2 * q + 1]);
     store_words<YW>(yrow[i], packed);
+  }
+  __syncthreads();  // vs is reused by the next segment
   }
 }
 
@@ -302,9 +314,12 @@ __device__ inline void shr_mul(const uint4 (&xv)[ShrCfg<R>::UN][ShrCfg<R>::RB],
 template <int DT, int R>
 __global__ __launch_bounds__(256, ShrCfg<R>::WAVES_PER_SIMD) void shrink_mfma_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, const uint16_t* const* __restrict__ A_ptrs,
-    const int32_t* __restrict__ seg_starts, int32_t S, const int32_t* __restrict__ perm, int32_t n,
-    int32_t h_in, int32_t kcm, int32_t ks, float* __restrict__ part, int64_t slice,
-    int32_t* __restrict__ tile_cnt, float* __restrict__ v_out, int32_t* __restrict__ rowks) {
+    const int32_t* __restrict__ seg_starts, int32_t S_host, const int32_t* __restrict__ perm,
+    int32_t n, int32_t h_in, int32_t kcm, int32_t ks, float* __restrict__ part, int64_t slice,
+    int32_t* __restrict__ tile_cnt, float* __restrict__ v_out, int32_t* __restrict__ rowks,
+    const int32_t* __restrict__ meta) {
+  const int S = meta ? meta[0] : S_host;
+  if (meta && meta[2] < kLongMin) return;  // no long segment at all
   using C = ShrCfg<R>;
   constexpr int NB = C::NB, RB = C::RB, UN = C::UN, STAGE = C::STAGE, MT = C::MT;
   __shared__ TileSegs<MT> sh;
@@ -474,9 +489,11 @@ struct ExpCfg {
 template <int DT, int R>
 __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_kernel(
     uint16_t* __restrict__ y, int64_t ld_y, const float* __restrict__ v,
-    const uint16_t* const* __restrict__ B_ptrs, const int32_t* __restrict__ seg_starts, int32_t S,
-    const int32_t* __restrict__ perm, int32_t n, int32_t h_out, float scale, int32_t tiles,
-    int32_t strips) {
+    const uint16_t* const* __restrict__ B_ptrs, const int32_t* __restrict__ seg_starts,
+    int32_t S_host, const int32_t* __restrict__ perm, int32_t n, int32_t h_out, float scale,
+    int32_t tiles, int32_t strips, const int32_t* __restrict__ meta) {
+  const int S = meta ? meta[0] : S_host;
+  if (meta && meta[2] < kLongMin) return;  // no long segment at all
   using E = Elem<DT>;
   using C = ExpCfg<R>;
   constexpr int TR = C::TR, TC = C::TC, RB = C::RB, CB = C::CB;
@@ -658,13 +675,19 @@ inline void mfma_split(int32_t n, int32_t h_in, int ks_cap, int* kcm, int* ks) {
   *ks = (h_in + c - 1) / c;
 }
 
+// Segment tables of one call.  With host tables S, min_len and max_len are exact.  With
+// tables built on the device, meta points at their [S, min_len, max_len, n_valid] word,
+// S is only an upper bound (it sizes the grids) and every kernel reads the count from meta.
 struct Tables {
   const uint16_t* const* ptrs;
   const int32_t* seg_starts;
   const int32_t* perm;
   int32_t n, S, min_len, max_len;
-  bool use_gemv() const { return min_len < kLongMin; }
-  bool use_long() const { return max_len >= kLongMin; }
+  const int32_t* meta = nullptr;
+  bool use_gemv() const { return meta || min_len < kLongMin; }
+  bool use_long() const { return meta || max_len >= kLongMin; }
+  // grid width of the GEMV kernels (they loop over the segments beyond it)
+  unsigned gemv_grid() const { return static_cast<unsigned>(meta ? (S < 256 ? S : 256) : S); }
 };
 
 // shrink kernels: short segments leave split-K slices (ks_gemv of them, counted in rowks),
@@ -678,8 +701,8 @@ hipError_t launch_shrink(hipStream_t st, const uint16_t* x, int64_t ld_x, const 
   if (T.use_gemv()) {
     const int ks = (h_in + GemvCfg<R>::KC - 1) / GemvCfg<R>::KC;
     *ks_gemv = ks;
-    hipLaunchKernelGGL((shrink_gemv_kernel<DT, R>), dim3(T.S, ks), dim3(256), 0, st, x, ld_x,
-                       T.ptrs, T.seg_starts, T.perm, h_in, part, L.slice, rowks, ks);
+    hipLaunchKernelGGL((shrink_gemv_kernel<DT, R>), dim3(T.gemv_grid(), ks), dim3(256), 0, st, x,
+                       ld_x, T.ptrs, T.seg_starts, T.perm, h_in, part, L.slice, rowks, ks, T.meta);
   }
   if (T.use_long()) {
     int kcm, ks;
@@ -687,7 +710,7 @@ hipError_t launch_shrink(hipStream_t st, const uint16_t* x, int64_t ld_x, const 
     const int tiles = (T.n + ShrCfg<R>::MT - 1) / ShrCfg<R>::MT;
     hipLaunchKernelGGL((shrink_mfma_kernel<DT, R>), dim3(tiles * ks), dim3(256), 0, st, x, ld_x,
                        T.ptrs, T.seg_starts, T.S, T.perm, T.n, h_in, kcm, ks, part, L.slice,
-                       reinterpret_cast<int32_t*>(ws + L.tile_cnt_off), v_long, rowks);
+                       reinterpret_cast<int32_t*>(ws + L.tile_cnt_off), v_long, rowks, T.meta);
   }
   return hipGetLastError();
 }
@@ -701,8 +724,9 @@ hipError_t launch_expand(hipStream_t st, uint16_t* y, int64_t ld_y, const float*
   constexpr int CPL = 128 / R;
   if (T.use_gemv()) {
     const int chunks = (h_out + 64 * CPL - 1) / (64 * CPL);
-    hipLaunchKernelGGL((expand_gemv_kernel<DT, R>), dim3(T.S, chunks), dim3(64), 0, st, y, ld_y,
-                       vsrc, slice, ks_gemv, T.ptrs, T.seg_starts, T.perm, h_out, scale);
+    hipLaunchKernelGGL((expand_gemv_kernel<DT, R>), dim3(T.gemv_grid(), chunks), dim3(64), 0, st,
+                       y, ld_y, vsrc, slice, ks_gemv, T.ptrs, T.seg_starts, T.perm, h_out, scale,
+                       T.meta);
   }
   if (T.use_long()) {
     // each XCD takes ceil(strips / 8) strips at most: pad the grid to 8 equal shares
@@ -712,7 +736,7 @@ hipError_t launch_expand(hipStream_t st, uint16_t* y, int64_t ld_y, const float*
     if (share * kXcds > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((expand_mfma_kernel<DT, R>), dim3(static_cast<unsigned>(share * kXcds)),
                        dim3(256), 0, st, y, ld_y, v_long, T.ptrs, T.seg_starts, T.S, T.perm, T.n,
-                       h_out, scale, tiles, strips);
+                       h_out, scale, tiles, strips, T.meta);
   }
   return hipGetLastError();
 }
@@ -779,6 +803,26 @@ struct LoraOp {
 
 
 }  // namespace
+
+namespace sgmv_host {
+
+hipError_t table_lora_add_device(hipStream_t st, int32_t dtype, int32_t r, void* y, int64_t ld_y,
+                                 const void* x, int64_t ld_x, const void* const* A_ptrs,
+                                 const void* const* B_ptrs, const int32_t* seg_starts,
+                                 const int32_t* perm, const int32_t* meta, int32_t n,
+                                 int32_t S_max, int32_t h_in, int32_t h_out, float scale,
+                                 void* workspace) {
+  const WsLayout L = ws_layout(n, h_in, r);
+  Tables TA{reinterpret_cast<const uint16_t* const*>(A_ptrs), seg_starts, perm, n, S_max, 1, n};
+  Tables TB{reinterpret_cast<const uint16_t* const*>(B_ptrs), seg_starts, perm, n, S_max, 1, n};
+  TA.meta = meta;
+  TB.meta = meta;
+  return dispatch<LoraOp>(dtype, r, st, static_cast<uint16_t*>(y), ld_y,
+                          static_cast<const uint16_t*>(x), ld_x, TA, TB, h_in, h_out, scale, L,
+                          static_cast<char*>(workspace));
+}
+
+}  // namespace sgmv_host
 
 extern "C" size_t sgmv_workspace_bytes(int32_t n, int32_t h_in, int32_t r) {
   if (n < 0 || h_in < 8 || h_in > kMaxDim || !rank_ok(r)) return 0;

@@ -59,7 +59,8 @@ class DeviceProblem:
         return y
 
     def lora_add_pool(self, y=None, workspace=None, scale=None, ids=None):
-        """The one-launch decode path (n <= 64) with device-resident ids."""
+        """The device-id path (one launch for n <= 64, device sort + table kernels up to
+        4096 rows)."""
         import torch
         y = self.fresh_y() if y is None else y
         if ids is None:

@@ -295,11 +295,12 @@ def sgmv_lora_add_pool(stream, dtype, y, ld_y, x, ld_x, adapter_ids, n, A_pool, 
                                          float(scale), workspace, workspace_bytes)
 
 
-POOL_MAX_TOKENS = 64
+DECODE_MAX_TOKENS = 64   # one-launch decode kernel
+POOL_MAX_TOKENS = 4096   # device-side segment sort, then the table kernels
 
 
 def build_segments_device(ids, n_adapters: int, stream=None):
-    """Device segment tables for device int32 ids (n <= 64): (perm, seg_starts,
+    """Device segment tables for device int32 ids (n <= 4096): (perm, seg_starts,
     seg_adapter, n_segments) as int32 tensors; n_segments[0] is -1 if an id is out of
     range."""
     torch = _torch()
@@ -317,7 +318,8 @@ def build_segments_device(ids, n_adapters: int, stream=None):
 
 
 def lora_add_pool(y, x, ids, A_pool, B_pool, scale: float, workspace=None, stream=None):
-    """y[t] += scale * (x[t] @ A_pool[ids[t]]) @ B_pool[ids[t]] in one launch (n <= 64).
+    """y[t] += scale * (x[t] @ A_pool[ids[t]]) @ B_pool[ids[t]] with device ids (n <= 4096):
+    one launch for n <= 64, device segment sort plus the table kernels above.
 
     ``ids`` is a device int32 tensor [n]; ``A_pool`` [P, r, h_in] and ``B_pool``
     [P, h_out, r] are device tensors with contiguous adapters."""

@@ -152,7 +152,7 @@ class Rig:
         self.ws = sgmv.make_workspace(p.n, p.h_in, p.r, device)
         self.dtype_code = sgmv.dtype_code(self.x)
         self.ld_x, self.ld_y = p.h_in, p.h_out
-        self.pool_path = p.n <= sgmv.POOL_MAX_TOKENS
+        self.pool_path = p.n <= sgmv.DECODE_MAX_TOKENS
         # table path: metadata staging ring (pinned host -> device)
         self.A_bases = sgmv.adapter_bases(self.A)
         self.B_bases = sgmv.adapter_bases(self.B)
@@ -313,13 +313,19 @@ def load_traffic(workload: str, pool_path: bool):
     return int(float(rec["hbm_bytes_per_call"]))
 
 
-def measure(p, device, steps: int, warmup: int, eager: bool = False, force_table: bool = False):
+def measure(p, device, steps: int, warmup: int, eager: bool = False, force_table: bool = False,
+            force_device: bool = False):
     """Check slot 0 against the oracle, then time `steps` steps after `warmup` untimed
     ones: wall time per step, GPU time per step, and the SGMV call's average duration."""
     import torch
+    from adapter_gemv_amd import sgmv
     rig = Rig(p, device)
     if force_table:
         rig.pool_path = False
+    if force_device:
+        if p.n > sgmv.POOL_MAX_TOKENS:
+            raise SystemExit(f"--path device takes at most {sgmv.POOL_MAX_TOKENS} tokens")
+        rig.pool_path = True
     parity = parity_check(rig)
     print(f"# {p.name}: slots={rig.slots} pool_path={rig.pool_path} parity={parity}",
           file=sys.stderr, flush=True)
@@ -574,8 +580,10 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="decode7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", choices=["auto", "table"], default="auto",
-                    help="auto: one-launch path for batches of <= 64 tokens")
+    ap.add_argument("--path", choices=["auto", "table", "device"], default="auto",
+                    help="auto: one-launch path for batches of <= 64 tokens, host-built tables "
+                         "above; device: device ids for any batch up to 4096 tokens "
+                         "(device sort + table kernels, graph-captured); table: host tables")
     ap.add_argument("--eager", action="store_true", help="no HIP graph on the one-launch path")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--sweep", choices=sorted(SWEEPS),
@@ -619,16 +627,20 @@ def main(argv=None) -> int:
 
     p = workload_problem(args.workload)
     m = measure(p, device, args.steps, args.warmup, eager=args.eager,
-                force_table=args.path == "table")
+                force_table=args.path == "table", force_device=args.path == "device")
     rig, parity, use_graph = m["rig"], m["parity"], m["use_graph"]
     wall, gpu_step, call_s, call_how, flag = (m["wall"], m["gpu_step"], m["call_s"],
                                               m["call_how"], m["flag"])
 
     nbytes = algorithmic_bytes(p)
     flops = algorithmic_flops(p)
-    traffic = load_traffic(args.workload, rig.pool_path)
-    kernel = ("lora_add_pool_kernel (one launch per call)" if rig.pool_path else
-              "sgmv_lora_add table path (all kernels of one call)")
+    traffic = load_traffic(args.workload, rig.pool_path and p.n <= 64) if args.path != "device" or p.n <= 64 else None
+    if rig.pool_path and p.n <= 64:
+        kernel = "lora_add_pool_kernel (one launch per call)"
+    elif rig.pool_path:
+        kernel = "sgmv_lora_add_pool: device segment sort + table kernels (all launches of one call)"
+    else:
+        kernel = "sgmv_lora_add table path (all kernels of one call)"
     out = {
         "metric": METRIC,
         "value": round(nbytes / wall / 1e9, 3),
@@ -647,7 +659,9 @@ def main(argv=None) -> int:
             "distinct_adapters": p.distinct_adapters(), "adapter_pool": p.n_adapters,
             "scale": p.scale, "rotation_slots": rig.slots,
             "rotation_bytes": rig.slots * nbytes, "cache": "cold (rotating slots)",
-            "step": ("sgmv_lora_add_pool: device segment sort + shrink + expand, one launch" +
+            "step": (("sgmv_lora_add_pool: device segment sort + shrink + expand, one launch"
+                      if p.n <= 64 else
+                      "sgmv_lora_add_pool: device segment sort, then the table kernels") +
                      (", K steps replayed from one HIP graph" if use_graph else ", eager"))
                     if rig.pool_path else
                     "host segment build + pinned H2D tables + sgmv_lora_add, eager",

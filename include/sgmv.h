@@ -159,23 +159,31 @@ int sgmv_lora_add(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
                   void* workspace, size_t workspace_bytes);
 
 /*
- * Segment metadata on the device, for a batch of at most 64 tokens whose adapter ids
- * are already in device memory: the same stable sort as sgmv_build_segments, done by
- * one wavefront (paper summary, idea I2).  All pointers are device memory.
- *   adapter_ids  int32[n] in; n <= 64
- *   perm         int32[n] out (first n_valid entries written)
+ * Segment metadata on the device, for a batch of at most 4096 tokens whose adapter ids
+ * are already in device memory: the same stable sort as sgmv_build_segments (paper
+ * summary, idea I2), done by one wavefront for n <= 64 and by one workgroup (a bitonic
+ * sort of (id, row) keys in LDS and a scan of the segment starts) above.  All pointers
+ * are device memory.
+ *   adapter_ids  int32[n] in; n <= 4096
+ *   perm         int32[n] out (the first n_valid entries are the sorted caller rows;
+ *                for n > 64 the remaining entries are set to -1)
  *   seg_starts   int32[n+1] out, seg_adapter int32[n] out
  *   n_segments   int32[1] out: S, or -1 if some id lies outside [0, n_adapters)
  *                (rows with such ids are left out of the tables)
- * Returns SGMV_ERR_SHAPE for n > 64.  Asynchronous on `stream`.
+ * Returns SGMV_ERR_SHAPE for n > 4096.  Asynchronous on `stream`.
  */
 int sgmv_build_segments_device(hipStream_t stream, const int32_t* adapter_ids, int32_t n,
                                int32_t n_adapters, int32_t* perm, int32_t* seg_starts,
                                int32_t* seg_adapter, int32_t* n_segments);
 
 /*
- * Decode-sized fused LoRA add-on, one kernel launch: segment metadata, shrink and
- * expand for a batch of at most 64 tokens, y[t] += scale * (x[t] @ A[a_t]) @ B[a_t].
+ * Fused LoRA add-on for adapter ids in device memory and adapters in pools,
+ * y[t] += scale * (x[t] @ A[a_t]) @ B[a_t], with no host work that depends on the ids
+ * (the call can be captured in a HIP graph and replayed with new ids):
+ *   n <= 64:        one kernel launch: segment metadata, shrink and expand (decode);
+ *   64 < n <= 4096: the device sort of sgmv_build_segments_device writes the segment
+ *                   tables and pointer tables into the workspace, then the kernels of
+ *                   sgmv_lora_add run on them (prefill and mixed batches).
  *   adapter_ids  device int32[n]: adapter of caller row t (device memory, so a HIP
  *                graph can capture the call and replay it with new ids)
  *   A_pool       device: adapter a's A ([r, h_in] row-major) starts at
@@ -185,7 +193,7 @@ int sgmv_build_segments_device(hipStream_t stream, const int32_t* adapter_ids, i
  *                zero-filled once); calls sharing a workspace must be stream-ordered
  * Rows whose id lies outside [0, n_adapters) are left unchanged and set the int32 at
  * the start of the workspace to 2 (a device-side wait that timed out sets it to 1;
- * it is never cleared by the library).  Returns SGMV_ERR_SHAPE for n > 64.
+ * it is never cleared by the library).  Returns SGMV_ERR_SHAPE for n > 4096.
  */
 int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
                        const void* x, int64_t ld_x, const int32_t* adapter_ids, int32_t n,

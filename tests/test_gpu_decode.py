@@ -50,6 +50,15 @@ ID_CASES = [
     ("uniform64", np.random.default_rng(1).integers(0, 64, 64).astype(np.int32), 64),
     ("zipf40", synth.truncated_zipf_ids(np.random.default_rng(2), 40, 4096, 1.2), 4096),
     ("sparse_pool", np.random.default_rng(3).choice([5, 900, 4000], 33).astype(np.int32), 4096),
+    # the one-workgroup device sort (n > 64)
+    ("n65", np.random.default_rng(4).integers(0, 9, 65).astype(np.int32), 9),
+    ("uniform300", np.random.default_rng(5).integers(0, 300, 300).astype(np.int32), 300),
+    ("zipf1000", synth.truncated_zipf_ids(np.random.default_rng(6), 1000, 5000, 1.1), 5000),
+    ("distinct4096", np.random.default_rng(7).permutation(4096).astype(np.int32), 4096),
+    ("same4096", np.full(4096, 3, np.int32), 4),
+    ("mixed70b", synth.mixed70b_ids(np.random.default_rng(8)), 50),
+    ("big_ids", np.random.default_rng(9).choice([0, 1 << 19, (1 << 20) - 1], 777).astype(np.int32),
+     1 << 20),
 ]
 
 
@@ -75,6 +84,20 @@ def test_device_segments_flag_bad_ids(torch_cuda):
     d = torch.as_tensor(np.array([0, 5, 1], np.int32), device="cuda")
     _, _, _, S = sgmv.build_segments_device(d, 3)
     assert int(S.item()) == -1
+    # large sort: the valid rows are still sorted and the rest of perm is -1
+    ids = np.random.default_rng(10).integers(0, 6, 500).astype(np.int32)
+    ids[[7, 123, 499]] = [6, -2, 100]
+    perm, starts, seg_ad, S = sgmv.build_segments_device(torch.as_tensor(ids, device="cuda"), 6)
+    torch.cuda.synchronize()
+    assert int(S.item()) == -1
+    keep = (ids >= 0) & (ids < 6)
+    rp, rs, ra = oracle.segments(np.where(keep, ids, 0).astype(np.int32)[keep], 6)
+    rows = np.flatnonzero(keep)
+    got = perm.cpu().numpy()
+    assert np.array_equal(got[: keep.sum()], rows[rp])
+    assert np.all(got[keep.sum():] == -1)
+    assert np.array_equal(starts.cpu().numpy()[: len(ra) + 1], rs)
+    assert np.array_equal(seg_ad.cpu().numpy()[: len(ra)], ra)
 
 
 DECODE = ["tiny", "decode7b", "sweep_a", "sweep_b", "sweep_c"]
@@ -253,4 +276,133 @@ def test_shared_workspace_across_shapes(torch_cuda):
             torch.cuda.synchronize()
             _assert_close(oracle.decode(_storage(yb, "bf16"), "bf16"), oracle.lora_add_problem(big),
                           "shared ws table")
+    assert int(ws[:16640].view(torch.int32).abs().sum().item()) == 0
+
+
+# --------------------------------------------------------------------------------------
+# device ids, 64 < n <= 4096: device sort + table kernels
+# --------------------------------------------------------------------------------------
+LARGE = [
+    # name, n, h_in, h_out, r, P, ids kind, dtype
+    ("prefill_blocks", 512, 1032, 776, 16, 4, "blocks", "bf16"),
+    ("mixed_r64", 520, 1024, 1160, 64, 50, "mixed70b", "bf16"),
+    ("many_short", 1000, 520, 264, 32, 500, "uniform", "f16"),
+    ("one_long", 4096, 264, 136, 16, 1, "blocks", "f16"),
+    ("ragged_r16", 333, 200, 3000, 16, 7, "zipf", "bf16"),
+]
+
+
+def _large_ids(kind, n, P, rng):
+    if kind == "blocks":
+        return np.repeat(rng.permutation(P), -(-n // P))[:n].astype(np.int32)
+    if kind == "uniform":
+        return rng.integers(0, P, n).astype(np.int32)
+    if kind == "zipf":
+        return synth.truncated_zipf_ids(rng, n, P, 1.1)
+    dec = synth.truncated_zipf_ids(rng, 64, P - 2, 1.2)
+    half = (n - 64) // 2
+    return np.concatenate([dec, np.full(half, P - 2, np.int32),
+                           np.full(n - 64 - half, P - 1, np.int32)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("case", LARGE, ids=[c[0] for c in LARGE])
+def test_pool_large_batches(torch_cuda, case):
+    name, n, h_in, h_out, r, P, kind, dtype = case
+    _say(f"[pool large] {case}")
+    ids = _large_ids(kind, n, P, np.random.default_rng(n + r))
+    p = synth.random_problem((86, n, r), n=n, h_in=h_in, h_out=h_out, r=r, n_adapters=P,
+                             dtype=dtype, ids=ids, scale=1.5)
+    y = _upload(p).lora_add_pool()
+    torch_cuda.cuda.synchronize()
+    _assert_close(oracle.decode(_storage(y, dtype), dtype), oracle.lora_add_problem(p),
+                  f"pool large {name}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("r,kind,n", [(16, "mixed70b", 300), (32, "blocks", 256),
+                                      (64, "uniform", 200)])
+def test_pool_large_exact_bit_exact(torch_cuda, dtype, r, kind, n):
+    _say(f"[pool large exact] r={r} {kind} n={n} {dtype}")
+    P = 12
+    ids = _large_ids(kind, n, P, np.random.default_rng(3 * n + r))
+    p = synth.exact_problem((87, n, r), n=n, h_in=1032, h_out=648, r=r, n_adapters=P,
+                            dtype=dtype, ids=ids)
+    y = _upload(p).lora_add_pool()
+    torch_cuda.cuda.synchronize()
+    want = oracle.round_io(oracle.lora_add_problem(p), dtype).view(np.uint16)
+    assert np.array_equal(_storage(y, dtype).view(np.uint16), want)
+
+
+@pytest.mark.parametrize("name", ["prefill13b_gateup", "mixed70b_r64_gate"])
+def test_pool_large_full_workloads(torch_cuda, name):
+    """The full prefill / mixed batches with device ids (2048 and 2112 rows)."""
+    _say(f"[pool large full] {name}")
+    p = FACT[name]()
+    y = _upload(p).lora_add_pool()
+    torch_cuda.cuda.synchronize()
+    got = oracle.decode(_storage(y, p.dtype), p.dtype)
+    rows = np.r_[0:64, np.random.default_rng(11).choice(np.arange(64, p.n), 64, replace=False)]
+    ref = oracle.lora_add(p.y[rows], p.x[rows], p.ids[rows], p.A, p.B, p.scale, p.dtype)
+    _assert_close(got[rows], ref, f"pool large full {name}")
+
+
+def test_pool_large_invalid_ids(torch_cuda):
+    torch = torch_cuda
+    from adapter_gemv_amd import sgmv
+    p = synth.random_problem((88,), n=400, h_in=520, h_out=264, r=16, n_adapters=5,
+                             dtype="bf16", id_dist="uniform")
+    dp = _upload(p)
+    ids = p.ids.copy()
+    bad = [0, 17, 399]
+    ids[bad] = [5, -1, 70000]
+    ws = sgmv.make_workspace(p.n, p.h_in, 16, dp.x.device)
+    y = dp.lora_add_pool(ids=torch.as_tensor(ids, device="cuda"), workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32).item()) == 2
+    keep = np.ones(p.n, bool)
+    keep[bad] = False
+    got = oracle.decode(_storage(y, "bf16"), "bf16")
+    ref = oracle.lora_add(p.y[keep], p.x[keep], p.ids[keep], p.A, p.B, p.scale, "bf16")
+    _assert_close(got[keep], ref, "large valid rows")
+    assert np.array_equal(got[~keep], oracle.decode(p.y[~keep], "bf16"))
+
+
+def test_pool_large_hip_graph_replay(torch_cuda):
+    """Capture large device-id calls (device sort + table kernels) in one HIP graph;
+    every replay, with eager work between replays, must match the eager result."""
+    torch = torch_cuda
+    from adapter_gemv_amd import sgmv
+    p = synth.random_problem((89,), n=700, h_in=1032, h_out=776, r=16, n_adapters=9,
+                             dtype="bf16", id_dist="zipf", zipf_s=1.3)
+    dp = _upload(p)
+    ws = sgmv.make_workspace(p.n, p.h_in, 16, dp.x.device)
+    rng = np.random.default_rng(12)
+    id_sets = [torch.as_tensor(synth.truncated_zipf_ids(rng, p.n, 9, s), device="cuda")
+               for s in (0.8, 1.3, 2.0)]
+    ys = [dp.fresh_y() for _ in range(3)]
+    ref = [dp.fresh_y() for _ in range(3)]
+    for k in range(3):
+        sgmv.lora_add_pool(ref[k], dp.x, id_sets[k], dp.A, dp.B, p.scale, ws)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for k in range(3):
+            sgmv.lora_add_pool(dp.fresh_y(), dp.x, id_sets[k], dp.A, dp.B, p.scale, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k in range(3):
+            sgmv.lora_add_pool(ys[k], dp.x, id_sets[k], dp.A, dp.B, p.scale, ws)
+    for rep in range(3):
+        for k in range(3):
+            ys[k].copy_(dp.y0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in range(3):
+            assert torch.equal(ys[k], ref[k]), f"replay {rep} call {k}"
+        _ = (dp.x.float() * 2).sum()
+        torch.cuda.synchronize()
     assert int(ws[:16640].view(torch.int32).abs().sum().item()) == 0

@@ -209,7 +209,7 @@ def _pool(**kw):
 
 
 POOL_REJECTS = [
-    ("n>64", dict(n=65), _lib.ERR_SHAPE),
+    ("n>4096", dict(n=4097), _lib.ERR_SHAPE),
     ("rank", dict(r=8), _lib.ERR_UNSUPPORTED),
     ("dtype", dict(dtype=7), _lib.ERR_UNSUPPORTED),
     ("A_stride small", dict(A_stride=16 * 4096 - 8), _lib.ERR_SHAPE),
@@ -229,5 +229,5 @@ def test_lora_add_pool_rejects(name, kw, code):
 
 def test_build_segments_device_rejects():
     L = _lib.lib()
-    assert L.sgmv_build_segments_device(None, TAB, 65, 4, V, V, V, V) == _lib.ERR_SHAPE
+    assert L.sgmv_build_segments_device(None, TAB, 4097, 4, V, V, V, V) == _lib.ERR_SHAPE
     assert L.sgmv_build_segments_device(None, None, 3, 4, V, V, V, V) == _lib.ERR_NULL
