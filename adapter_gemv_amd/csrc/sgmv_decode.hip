@@ -162,7 +162,7 @@ struct SortOut {
   int32_t* ws_flag;         // nullable: set to 2 if an id was out of range
 };
 
-constexpr int kRankThreads = 256;  // 4 waves: 64 rows per workgroup, ids split in quarters
+constexpr int kRankThreads = 1024;  // 16 waves: 64 rows per workgroup, the ids split 16 ways
 constexpr int kRankRows = 64;
 constexpr int kTabThreads = 1024;
 constexpr int32_t kNoId = 0x7fffffff;  // larger than every valid id
@@ -171,7 +171,8 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(const int32_t* __res
                                                             int32_t n, int32_t n_adapters,
                                                             SortOut o) {
   __shared__ __attribute__((aligned(16))) int32_t sid[kDevSortMax + 16];
-  __shared__ int part[kRankThreads / 64][kRankRows];
+  constexpr int W = kRankThreads / 64;
+  __shared__ int part[W][kRankRows];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n16 = (n + 15) / 16 * 16;
   for (int j = tid; j < n16; j += kRankThreads) {
@@ -186,8 +187,8 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(const int32_t* __res
   const int i = blockIdx.x * kRankRows + lane;
   const int me = (i < n) ? sid[i] : kNoId;
   // wave w counts over ids [j0, j1), 16 at a time (four 16-byte LDS reads in flight)
-  const int quarter = (n16 / 16 + 3) / 4 * 16;
-  const int j0 = w * quarter, j1 = min(n16, j0 + quarter);
+  const int share = (n16 / 16 + W - 1) / W * 16;
+  const int j0 = w * share, j1 = min(n16, j0 + share);
   int before = 0;
   for (int j = j0; j < j1; j += 16) {
     int4 q[4];
@@ -204,7 +205,9 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(const int32_t* __res
   part[w][lane] = before;
   __syncthreads();
   if (w == 0 && i < n && me != kNoId) {
-    const int pos = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+    int pos = 0;
+#pragma unroll
+    for (int q = 0; q < W; ++q) pos += part[q][lane];
     o.perm[pos] = i;
     o.sorted_ids[pos] = me;
   }
@@ -611,7 +614,7 @@ extern "C" int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, in
   if (n > kPoolMaxN) {
     // device sort into the workspace, then the table path on those tables
     char* wsb = static_cast<char*>(workspace);
-    const WsLayout L = ws_layout(n, h_in, r);
+    const WsLayout L = ws_layout(n, h_in, r, workspace_bytes);
     const DevTabLayout D = dev_tab_layout(n);
     char* dt = wsb + L.dtab_off;
     SortOut o{};
@@ -634,7 +637,7 @@ extern "C" int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, in
     return hip_status(table_lora_add_device(
         stream, dtype, r, y, ld_y, x, ld_x, reinterpret_cast<const void* const*>(o.A_ptrs),
         reinterpret_cast<const void* const*>(o.B_ptrs), o.seg_starts, o.perm, o.meta, n, S_max,
-        h_in, h_out, scale, workspace));
+        h_in, h_out, scale, workspace, workspace_bytes));
   }
 
   PoolArgs p;

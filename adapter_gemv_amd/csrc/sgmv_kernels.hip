@@ -811,8 +811,8 @@ hipError_t table_lora_add_device(hipStream_t st, int32_t dtype, int32_t r, void*
                                  const void* const* B_ptrs, const int32_t* seg_starts,
                                  const int32_t* perm, const int32_t* meta, int32_t n,
                                  int32_t S_max, int32_t h_in, int32_t h_out, float scale,
-                                 void* workspace) {
-  const WsLayout L = ws_layout(n, h_in, r);
+                                 void* workspace, size_t workspace_bytes) {
+  const WsLayout L = ws_layout(n, h_in, r, workspace_bytes);
   Tables TA{reinterpret_cast<const uint16_t* const*>(A_ptrs), seg_starts, perm, n, S_max, 1, n};
   Tables TB{reinterpret_cast<const uint16_t* const*>(B_ptrs), seg_starts, perm, n, S_max, 1, n};
   TA.meta = meta;
@@ -844,7 +844,7 @@ extern "C" int sgmv_shrink(hipStream_t stream, int32_t dtype, float* v, const vo
   if (!aligned16(x) || !aligned16(v)) return SGMV_ERR_ALIGNMENT;
   if (ranges_overlap(v, sizeof(float) * static_cast<size_t>(n) * r, x, matrix_bytes(n, ld_x, h_in)))
     return SGMV_ERR_ALIAS;
-  const WsLayout L = ws_layout(n, h_in, r);
+  const WsLayout L = ws_layout(n, h_in, r, workspace_bytes);
   if (!workspace || workspace_bytes < L.total ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return SGMV_ERR_WORKSPACE;
@@ -893,7 +893,7 @@ extern "C" int sgmv_lora_add(hipStream_t stream, int32_t dtype, void* y, int64_t
   if (!aligned16(x) || !aligned16(y)) return SGMV_ERR_ALIGNMENT;
   if (ranges_overlap(x, matrix_bytes(n, ld_x, h_in), y, matrix_bytes(n, ld_y, h_out)))
     return SGMV_ERR_ALIAS;
-  const WsLayout L = ws_layout(n, h_in, r);
+  const WsLayout L = ws_layout(n, h_in, r, workspace_bytes);
   if (!workspace || workspace_bytes < L.total ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return SGMV_ERR_WORKSPACE;

@@ -161,9 +161,10 @@ int sgmv_lora_add(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
 /*
  * Segment metadata on the device, for a batch of at most 4096 tokens whose adapter ids
  * are already in device memory: the same stable sort as sgmv_build_segments (paper
- * summary, idea I2), done by one wavefront for n <= 64 and by one workgroup (a bitonic
- * sort of (id, row) keys in LDS and a scan of the segment starts) above.  All pointers
- * are device memory.
+ * summary, idea I2), done by one wavefront for n <= 64; above, every row's sorted
+ * position is its count of smaller ids plus equal ids in earlier rows (one workgroup per
+ * 64 rows), then one workgroup finds and numbers the segment starts.  All pointers are
+ * device memory.
  *   adapter_ids  int32[n] in; n <= 4096
  *   perm         int32[n] out (the first n_valid entries are the sorted caller rows;
  *                for n > 64 the remaining entries are set to -1)

@@ -279,6 +279,46 @@ def test_shared_workspace_across_shapes(torch_cuda):
     assert int(ws[:16640].view(torch.int32).abs().sum().item()) == 0
 
 
+def test_shared_workspace_table_shapes(torch_cuda):
+    """Table-path calls of different n, h_in and r (host tables and device-sorted tables)
+    share one workspace sized for the largest: each gives the same bits as on a fresh
+    workspace, the results match the oracle, and the counters and tagged partials are
+    zero afterwards."""
+    torch = torch_cuda
+    from adapter_gemv_amd import sgmv
+    big = synth.random_problem((86, 1), n=2048, h_in=5120, h_out=1032, r=64, n_adapters=4,
+                               dtype="bf16", ids=np.repeat(np.int32([2, 0, 3, 1]), 512))
+    probs = [
+        synth.random_problem((86, 2), n=64, h_in=4096, h_out=776, r=16, n_adapters=40,
+                             dtype="bf16", id_dist="zipf", zipf_s=1.1),
+        big,
+        synth.random_problem((86, 3), n=300, h_in=2048, h_out=1032, r=32, n_adapters=7,
+                             dtype="bf16", id_dist="uniform"),
+    ]
+    dev = [_upload(q) for q in probs]
+    fresh = []
+    for q, d in zip(probs, dev):
+        fresh.append((d.lora_add(), d.lora_add_pool()))
+        torch.cuda.synchronize()
+        _assert_close(oracle.decode(_storage(fresh[-1][0], "bf16"), "bf16"),
+                      oracle.lora_add_problem(q), f"fresh ws n={q.n}")
+    ws = sgmv.make_workspace(big.n, big.h_in, 64, torch.device("cuda"))
+    for rep in range(2):
+        for q, d, (f_tab, f_pool) in zip(probs, dev, fresh):
+            _say(f"[shared ws tables] rep {rep} n={q.n} h_in={q.h_in} r={q.r}")
+            y = d.lora_add(workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(y, f_tab)
+            y = d.lora_add_pool(workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(y, f_pool)
+    assert int(ws[:16640].view(torch.int32).abs().sum().item()) == 0
+    # the largest call's tile counters and tagged partials: the last
+    # 8 * ceil(h_in / (8192 / r)) * 64 * r bytes plus one 256-byte line per 16 rows
+    tail = 8 * (-(-big.h_in // (8192 // 64))) * 64 * 64 + 256 * (big.n // 16)
+    assert int(ws[-tail:].view(torch.int32).abs().sum().item()) == 0
+
+
 # --------------------------------------------------------------------------------------
 # device ids, 64 < n <= 4096: device sort + table kernels
 # --------------------------------------------------------------------------------------

@@ -115,6 +115,22 @@ def test_workspace_bytes_monotone():
                 assert b <= b2, ((n, h, r), (n2, h2, r2))
 
 
+def test_workspace_layout_sharing_rule(tmp_path):
+    """The layout code itself (sgmv_checks.h, built for the host by tests/ws_layout_check.cpp):
+    in a buffer sized for the largest shape, no smaller call's scratch reaches the counters
+    or tagged partials of any other smaller call."""
+    import shutil
+    import subprocess
+    cxx = shutil.which("g++")
+    if cxx is None:
+        pytest.skip("g++ not found")
+    exe = str(tmp_path / "ws_layout_check")
+    subprocess.run([cxx, "-O1", "-std=c++17", "-I/opt/rocm/include", "-D__HIP_PLATFORM_AMD__",
+                    os.path.join(ROOT, "tests", "ws_layout_check.cpp"), "-o", exe], check=True)
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0 and out.stdout.startswith("ok"), out.stdout
+
+
 # --------------------------------------------------------------------------------------
 # validation: every one of these returns before any HIP call
 # --------------------------------------------------------------------------------------
