@@ -49,6 +49,18 @@ SIGNATURES = {
                                           _i64, _i32, _i32, _i32, _i32, ctypes.c_float, _p, _sz]),
 }
 
+
+class RankGroup(ctypes.Structure):
+    """sgmv_rank_group (include/sgmv.h)."""
+    _fields_ = [("r", _i32), ("row0", _i32), ("n", _i32), ("seg0", _i32), ("starts0", _i32),
+                ("n_segments", _i32), ("min_seg_len", _i32), ("max_seg_len", _i32),
+                ("scale", ctypes.c_float)]
+
+
+SIGNATURES["sgmv_build_segments_ranked"] = (ctypes.c_int, [_p, _i32, _i32, _p, _p, _p, _p, _p, _p])
+SIGNATURES["sgmv_lora_add_ranked"] = (ctypes.c_int, [_p, _i32, _p, _i64, _p, _i64, _p, _p, _p, _p,
+                                                     _i32, _p, _i32, _i32, _i32, _p, _sz])
+
 _LIB = None
 
 

@@ -906,3 +906,53 @@ extern "C" int sgmv_lora_add(hipStream_t stream, int32_t dtype, void* y, int64_t
                                      static_cast<const uint16_t*>(x), ld_x, TA, TB, h_in, h_out,
                                      scale, L, static_cast<char*>(workspace)));
 }
+
+// Mixed ranks: each rank group runs as sgmv_lora_add on its slice of the tables (pointer
+// offsets only), one group after another on the caller's stream.
+extern "C" int sgmv_lora_add_ranked(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
+                                    const void* x, int64_t ld_x, const void* const* A_ptrs,
+                                    const void* const* B_ptrs, const int32_t* seg_starts,
+                                    const int32_t* perm, int32_t n, const sgmv_rank_group* groups,
+                                    int32_t n_groups, int32_t h_in, int32_t h_out, void* workspace,
+                                    size_t workspace_bytes) {
+  if (dtype != SGMV_F16 && dtype != SGMV_BF16) return SGMV_ERR_UNSUPPORTED;
+  if (n < 0 || n_groups < 0) return SGMV_ERR_SHAPE;
+  if (n_groups > 0 && !groups) return SGMV_ERR_NULL;
+  int st;
+  if ((st = check_dim(h_in, ld_x))) return st;
+  if ((st = check_dim(h_out, ld_y))) return st;
+  size_t ws_need = 0;
+  for (int32_t g = 0; g < n_groups; ++g) {
+    const sgmv_rank_group& G = groups[g];
+    if (!rank_ok(G.r)) return SGMV_ERR_UNSUPPORTED;
+    if ((st = check_segments(G.n, G.n_segments, G.min_seg_len, G.max_seg_len))) return st;
+    if (G.row0 < 0 || G.seg0 < 0 || G.starts0 < 0 || static_cast<int64_t>(G.row0) + G.n > n)
+      return SGMV_ERR_SHAPE;
+    if (G.n > 0) ws_need = std::max(ws_need, ws_layout(G.n, h_in, G.r).total);
+  }
+  if (n == 0 || ws_need == 0) return SGMV_OK;
+  if (!y || !x || !A_ptrs || !B_ptrs || !seg_starts || !perm) return SGMV_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return SGMV_ERR_ALIGNMENT;
+  if (ranges_overlap(x, matrix_bytes(n, ld_x, h_in), y, matrix_bytes(n, ld_y, h_out)))
+    return SGMV_ERR_ALIAS;
+  if (!workspace || workspace_bytes < ws_need ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return SGMV_ERR_WORKSPACE;
+  if ((st = check_device())) return st;
+  for (int32_t g = 0; g < n_groups; ++g) {
+    const sgmv_rank_group& G = groups[g];
+    if (G.n == 0) continue;
+    const auto A = reinterpret_cast<const uint16_t* const*>(A_ptrs) + G.seg0;
+    const auto B = reinterpret_cast<const uint16_t* const*>(B_ptrs) + G.seg0;
+    const Tables TA{A, seg_starts + G.starts0, perm + G.row0, G.n, G.n_segments, G.min_seg_len,
+                    G.max_seg_len};
+    const Tables TB{B, seg_starts + G.starts0, perm + G.row0, G.n, G.n_segments, G.min_seg_len,
+                    G.max_seg_len};
+    const WsLayout L = ws_layout(G.n, h_in, G.r, workspace_bytes);
+    const hipError_t e = dispatch<LoraOp>(dtype, G.r, stream, static_cast<uint16_t*>(y), ld_y,
+                                          static_cast<const uint16_t*>(x), ld_x, TA, TB, h_in,
+                                          h_out, G.scale, L, static_cast<char*>(workspace));
+    if (e != hipSuccess) return SGMV_ERR_HIP;
+  }
+  return SGMV_OK;
+}

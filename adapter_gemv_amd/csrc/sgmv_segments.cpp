@@ -78,3 +78,56 @@ extern "C" int sgmv_build_ptr_table(const uint64_t* adapter_base, int32_t n_adap
   }
   return SGMV_OK;
 }
+
+// Mixed ranks: the same counting sort with (rank class, adapter id) as the key.  Each
+// non-empty rank class becomes one group with its own relative segment starts, so that
+// the fused call can run every group through the kernels built for its rank.
+extern "C" int sgmv_build_segments_ranked(const int32_t* adapter_ids, int32_t n,
+                                          int32_t n_adapters, const int32_t* adapter_rank,
+                                          int32_t* perm, int32_t* seg_starts,
+                                          int32_t* seg_adapter, sgmv_rank_group* groups,
+                                          int32_t* n_groups) {
+  if (n < 0 || n_adapters <= 0) return SGMV_ERR_SHAPE;
+  if (!seg_starts || !groups || !n_groups || !adapter_rank ||
+      (n > 0 && (!adapter_ids || !perm || !seg_adapter)))
+    return SGMV_ERR_NULL;
+  for (int32_t a = 0; a < n_adapters; ++a) {
+    const int32_t r = adapter_rank[a];
+    if (r != 16 && r != 32 && r != 64) return SGMV_ERR_UNSUPPORTED;
+  }
+  for (int32_t t = 0; t < n; ++t)
+    if (adapter_ids[t] < 0 || adapter_ids[t] >= n_adapters) return SGMV_ERR_ADAPTER_ID;
+
+  std::vector<int32_t> count(static_cast<size_t>(n_adapters), 0), slot(count.size(), 0);
+  for (int32_t t = 0; t < n; ++t) ++count[adapter_ids[t]];
+  int32_t G = 0, S = 0, row = 0;
+  for (int32_t r = 16; r <= 64; r *= 2) {
+    sgmv_rank_group g{};
+    g.r = r;
+    g.row0 = row;
+    g.seg0 = S;
+    g.starts0 = S + G;
+    g.min_seg_len = n;
+    g.max_seg_len = 0;
+    g.scale = 1.0f;
+    for (int32_t a = 0; a < n_adapters; ++a) {
+      const int32_t cnt = count[a];
+      if (adapter_rank[a] != r || cnt == 0) continue;
+      seg_starts[S + G] = row - g.row0;
+      seg_adapter[S] = a;
+      slot[a] = row;
+      row += cnt;
+      ++S;
+      if (cnt < g.min_seg_len) g.min_seg_len = cnt;
+      if (cnt > g.max_seg_len) g.max_seg_len = cnt;
+    }
+    if (row == g.row0) continue;  // no rows of this rank
+    g.n = row - g.row0;
+    g.n_segments = S - g.seg0;
+    seg_starts[S + G] = g.n;
+    groups[G++] = g;
+  }
+  for (int32_t t = 0; t < n; ++t) perm[slot[adapter_ids[t]]++] = t;
+  *n_groups = G;
+  return SGMV_OK;
+}

@@ -14,6 +14,7 @@ Layouts (see include/sgmv.h): x [n, h_in], y [n, h_out] row-major; an adapter po
 """
 from __future__ import annotations
 
+import ctypes
 import dataclasses
 from typing import Optional, Sequence, Union
 
@@ -276,6 +277,119 @@ def expand(y, v, batch: Batch, scale: float, stream=None):
 
 def _infer_rank(batch: Batch) -> int:
     return int(batch.rank)
+
+
+# --------------------------------------------------------------------------------------
+# mixed ranks: adapters of ranks 16, 32 and 64 in one call
+# --------------------------------------------------------------------------------------
+@dataclasses.dataclass
+class RankedTable:
+    """Host segment metadata of a mixed-rank batch (see sgmv_build_segments_ranked)."""
+    perm: np.ndarray          # int32 [n]
+    seg_starts: np.ndarray    # int32 [S + G]: per group, starts relative to its row0
+    seg_adapter: np.ndarray   # int32 [S]
+    groups: list              # [_lib.RankGroup], ascending r
+
+    @property
+    def n(self) -> int:
+        return int(self.perm.shape[0])
+
+    @property
+    def n_segments(self) -> int:
+        return int(self.seg_adapter.shape[0])
+
+
+def sgmv_build_segments_ranked(adapter_ids, adapter_rank) -> RankedTable:
+    ids = np.ascontiguousarray(np.asarray(adapter_ids), dtype=np.int32)
+    rank = np.ascontiguousarray(np.asarray(adapter_rank), dtype=np.int32)
+    n = int(ids.shape[0])
+    perm = np.zeros(max(n, 1), np.int32)
+    starts = np.zeros(n + 3, np.int32)
+    seg_ad = np.zeros(max(n, 1), np.int32)
+    groups = (_lib.RankGroup * 3)()
+    G = np.zeros(1, np.int32)
+    st = _lib.lib().sgmv_build_segments_ranked(_ptr(ids), n, int(rank.shape[0]), _ptr(rank),
+                                               _ptr(perm), _ptr(starts), _ptr(seg_ad),
+                                               ctypes.addressof(groups), _ptr(G))
+    check(st, "sgmv_build_segments_ranked")
+    gs = [groups[i] for i in range(int(G[0]))]
+    S = sum(g.n_segments for g in gs)
+    return RankedTable(perm[:n].copy(), starts[: S + len(gs)].copy(), seg_ad[:S].copy(), gs)
+
+
+def sgmv_lora_add_ranked(stream, dtype, y, ld_y, x, ld_x, A_ptrs, B_ptrs, seg_starts, perm, n,
+                         groups, n_groups, h_in, h_out, workspace, workspace_bytes) -> int:
+    return _lib.lib().sgmv_lora_add_ranked(stream, dtype, y, ld_y, x, ld_x, A_ptrs, B_ptrs,
+                                           seg_starts, perm, n, groups, n_groups, h_in, h_out,
+                                           workspace, workspace_bytes)
+
+
+@dataclasses.dataclass
+class RankedBatch:
+    """Segment metadata of a mixed-rank batch on the device.  Adapter ids index the
+    concatenation of the pools: pool k holds ids offset_k .. offset_k + P_k - 1."""
+    table: RankedTable
+    dev: object
+    A_ptrs_addr: int
+    B_ptrs_addr: int
+    seg_starts_addr: int
+    perm_addr: int
+
+    @property
+    def n(self) -> int:
+        return self.table.n
+
+    @property
+    def max_rank(self) -> int:
+        return max((g.r for g in self.table.groups), default=16)
+
+    @classmethod
+    def build(cls, adapter_ids, pools):
+        """``pools`` is a list of (A_pool [P_k, r_k, h_in], B_pool [P_k, h_out, r_k]) device
+        tensors."""
+        torch = _torch()
+        rank = np.concatenate([np.full(int(A.shape[0]), int(A.shape[1]), np.int32)
+                               for A, _ in pools])
+        tab = sgmv_build_segments_ranked(adapter_ids, rank)
+        a_base = np.concatenate([adapter_bases(A) for A, _ in pools])
+        b_base = np.concatenate([adapter_bases(B) for _, B in pools])
+        a_ptr = sgmv_build_ptr_table(a_base, tab.seg_adapter)
+        b_ptr = sgmv_build_ptr_table(b_base, tab.seg_adapter)
+        S, n = tab.n_segments, tab.n
+        ns = int(tab.seg_starts.shape[0])
+        nbytes = 16 * S + 4 * ns + 4 * n
+        buf = np.zeros(max(nbytes, 16), np.uint8)
+        buf[: 8 * S] = a_ptr[:S].view(np.uint8)
+        buf[8 * S: 16 * S] = b_ptr[:S].view(np.uint8)
+        buf[16 * S: 16 * S + 4 * ns] = tab.seg_starts.view(np.uint8)
+        buf[16 * S + 4 * ns: nbytes] = tab.perm.view(np.uint8)
+        dev = torch.from_numpy(buf).to(pools[0][0].device)
+        base = int(dev.data_ptr())
+        return cls(tab, dev, base, base + 8 * S, base + 16 * S, base + 16 * S + 4 * ns)
+
+
+def lora_add_ranked(y, x, batch: RankedBatch, scales, workspace=None, stream=None):
+    """y[t] += scale_r * (x[t] @ A[a_t]) @ B[a_t] in place, where r is the rank of a_t's
+    pool and ``scales`` maps each rank to its scale."""
+    n = batch.n
+    _check_rows(x, n, "x")
+    _check_rows(y, n, "y")
+    if x.dtype != y.dtype:
+        raise TypeError("x and y must share a dtype")
+    gs = batch.table.groups
+    arr = (_lib.RankGroup * max(len(gs), 1))()
+    for i, g in enumerate(gs):
+        arr[i] = g
+        arr[i].scale = float(scales[g.r])
+    if workspace is None:
+        workspace = make_workspace(n, x.shape[1], batch.max_rank, x.device)
+    st = sgmv_lora_add_ranked(_stream_handle(stream), dtype_code(y), y.data_ptr(), y.stride(0),
+                              x.data_ptr(), x.stride(0), batch.A_ptrs_addr, batch.B_ptrs_addr,
+                              batch.seg_starts_addr, batch.perm_addr, n, ctypes.addressof(arr),
+                              len(gs), x.shape[1], y.shape[1], workspace.data_ptr(),
+                              workspace.numel())
+    check(st, "sgmv_lora_add_ranked")
+    return y
 
 
 # --------------------------------------------------------------------------------------

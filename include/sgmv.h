@@ -105,6 +105,47 @@ int sgmv_build_segments(const int32_t* adapter_ids, int32_t n, int32_t n_adapter
                         int32_t* n_segments, int32_t* min_seg_len, int32_t* max_seg_len);
 
 /*
+ * One rank class of a mixed-rank batch: adapters of different ranks r in one call.  The
+ * rows are grouped first by their adapter's rank, then by adapter (the paper summary's
+ * idea I2, sorting the batch by adapter, with the rank as the leading key, so that each
+ * rank's rows run through kernels built for that r).  The group's rows are sorted
+ * positions row0 .. row0+n-1 of perm; its segments are entries seg0 .. seg0+n_segments-1
+ * of seg_adapter and of the pointer tables; its segment starts, relative to row0, are
+ * seg_starts[starts0 .. starts0+n_segments].
+ */
+typedef struct sgmv_rank_group {
+  int32_t r;            /* 16, 32 or 64 */
+  int32_t row0;         /* first sorted position of the group */
+  int32_t n;            /* rows of the group */
+  int32_t seg0;         /* first segment of the group */
+  int32_t starts0;      /* index in seg_starts of the group's first start (= seg0 + the
+                           group's index: each group's starts end with its own n) */
+  int32_t n_segments;
+  int32_t min_seg_len;  /* exact shortest / longest segment of the group */
+  int32_t max_seg_len;
+  float scale;          /* y += scale * ... for this group's rows; the builder writes 1 */
+} sgmv_rank_group;
+
+/*
+ * Segment metadata of a mixed-rank batch (host).  Stable counting sort of the caller's
+ * rows by (rank of the row's adapter, adapter id): groups in ascending r, segments in
+ * ascending adapter id inside a group, rows of one adapter in caller order.
+ *   adapter_ids   host int32[n]: adapter of caller row t, in [0, n_adapters)
+ *   adapter_rank  host int32[n_adapters]: rank of every adapter, each in {16, 32, 64}
+ *   perm          host int32[n] out: caller row at sorted position i
+ *   seg_starts    host int32[n+3] out: per group, its relative starts (see
+ *                 sgmv_rank_group); n_segments + n_groups entries are written
+ *   seg_adapter   host int32[n] out: adapter of segment s (all groups, in order)
+ *   groups        host sgmv_rank_group[3] out: the non-empty groups, ascending r
+ *   n_groups      host out: number of non-empty groups (0 when n == 0)
+ * Returns SGMV_ERR_ADAPTER_ID for an id out of range, SGMV_ERR_UNSUPPORTED for a rank
+ * outside {16, 32, 64}, SGMV_ERR_NULL / SGMV_ERR_SHAPE for bad arguments.
+ */
+int sgmv_build_segments_ranked(const int32_t* adapter_ids, int32_t n, int32_t n_adapters,
+                               const int32_t* adapter_rank, int32_t* perm, int32_t* seg_starts,
+                               int32_t* seg_adapter, sgmv_rank_group* groups, int32_t* n_groups);
+
+/*
  * Per-segment pointer table (host): seg_ptrs[s] = adapter_base[seg_adapter[s]].
  *   adapter_base  host uint64[n_adapters]: device address of each adapter's A (or B)
  *   seg_ptrs      host uint64[n_segments] out
@@ -157,6 +198,26 @@ int sgmv_lora_add(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
                   int32_t n, int32_t n_segments, int32_t min_seg_len, int32_t max_seg_len,
                   int32_t h_in, int32_t h_out, int32_t r, float scale,
                   void* workspace, size_t workspace_bytes);
+
+/*
+ * Fused LoRA add-on for a mixed-rank batch: for every group g of `groups` (host array,
+ * as written by sgmv_build_segments_ranked, with the scales filled in), the rows of g get
+ * y[t] += g.scale * (x[t] @ A[a_t]) @ B[a_t] with A[a_t] of g.r columns.  The groups run
+ * one after another on `stream`, each as sgmv_lora_add on its part of the tables:
+ *   A_ptrs, B_ptrs  device per-segment pointer tables over all groups' segments
+ *   seg_starts      device int32: the builder's seg_starts array
+ *   perm            device int32[n]: the builder's perm (required)
+ *   n               rows of the batch (x and y have n rows; perm entries are < n)
+ *   workspace       at least sgmv_workspace_bytes(n, h_in, largest r of the groups)
+ * Every group is checked before anything is launched.  Rows that belong to no group are
+ * left unchanged.  Returns SGMV_ERR_SHAPE if a group's rows or segment bounds do not fit.
+ */
+int sgmv_lora_add_ranked(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
+                         const void* x, int64_t ld_x, const void* const* A_ptrs,
+                         const void* const* B_ptrs, const int32_t* seg_starts,
+                         const int32_t* perm, int32_t n, const sgmv_rank_group* groups,
+                         int32_t n_groups, int32_t h_in, int32_t h_out, void* workspace,
+                         size_t workspace_bytes);
 
 /*
  * Segment metadata on the device, for a batch of at most 4096 tokens whose adapter ids

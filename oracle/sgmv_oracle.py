@@ -28,7 +28,11 @@ The pages give no layout, scale or precision; the readings taken here:
 * storage (shared with the input generator): ``A_pool[a]`` is ``[r, h_in]`` (row j is
   column j of A) and ``B_pool[a]`` is ``[h_out, r]`` (row c is column c of B);
 * the segment table is a *stable* sort by adapter id: ties keep caller order,
-  segments appear in ascending adapter id, adapters with no rows make no segment.
+  segments appear in ascending adapter id, adapters with no rows make no segment;
+* the pages fix no rank and no scale per adapter.  For a batch whose adapters have
+  different ranks, every row uses its own adapter's A, B and rank, and each rank has
+  its own scale (LoRA scales are usually alpha / r); rows are grouped by rank first,
+  then by adapter.
 
 Every function here is pinned by tests that do not reuse its code: exact rational
 brute force on tiny inputs, a hand-worked example, a closed form, invariants, and
@@ -161,3 +165,52 @@ def lora_add(y: np.ndarray, x: np.ndarray, ids: np.ndarray, A_pool: np.ndarray,
 def lora_add_problem(p) -> np.ndarray:
     """``lora_add`` on a ``workloads.Problem``."""
     return lora_add(p.y, p.x, p.ids, p.A, p.B, p.scale, p.dtype)
+
+
+# --------------------------------------------------------------------------------------
+# mixed ranks: adapters of several ranks in one call
+# --------------------------------------------------------------------------------------
+def segments_ranked(ids: np.ndarray, adapter_rank: np.ndarray):
+    """Stable sort of the caller's rows by (rank of the row's adapter, adapter id): the
+    batch sorted by adapter (paper summary, "Interesting ideas", I2) with the rank as the
+    leading key.  Returns (perm, [(r, row0, n, seg_starts relative to row0, seg_adapter)]
+    for every rank present, ascending r)."""
+    ids = np.asarray(ids, dtype=np.int64)
+    rank = np.asarray(adapter_rank, dtype=np.int64)
+    keys = [(int(rank[a]), int(a), t) for t, a in enumerate(ids)]
+    keys.sort()
+    perm = np.array([k[2] for k in keys], dtype=np.int32)
+    groups = []
+    for r in sorted(set(int(rank[a]) for a in ids)):
+        pos = [i for i, k in enumerate(keys) if k[0] == r]
+        row0, n = pos[0], len(pos)
+        starts, seg_ad = [], []
+        for i in pos:
+            a = keys[i][1]
+            if not seg_ad or seg_ad[-1] != a:
+                starts.append(i - row0)
+                seg_ad.append(a)
+        starts.append(n)
+        groups.append((r, row0, n, np.array(starts, np.int32), np.array(seg_ad, np.int32)))
+    return perm, groups
+
+
+def lora_add_ranked(y: np.ndarray, x: np.ndarray, ids: np.ndarray, pools, scales,
+                    dtype: str) -> np.ndarray:
+    """Mixed ranks: ``pools`` is a list of (A_pool [P_k, r_k, h_in], B_pool [P_k, h_out, r_k])
+    whose adapters are numbered one after another (pool k holds ids off_k .. off_k+P_k-1),
+    and ``scales[r]`` is the scale of rank r.  Row t gets
+    y_in[t] + scales[r] * (x[t] @ A[ids[t]]) @ B[ids[t]] with its adapter's own rank r;
+    float64, unrounded."""
+    ids = np.asarray(ids)
+    out = decode(y, dtype).copy()
+    off = 0
+    for A_k, B_k in pools:
+        P, r = int(A_k.shape[0]), int(A_k.shape[1])
+        rows = np.nonzero((ids >= off) & (ids < off + P))[0]
+        if rows.size:
+            local = (ids[rows] - off).astype(np.int32)
+            v = shrink(x[rows], local, A_k, dtype)
+            out[rows] = expand(y[rows], v, local, B_k, scales[r], dtype)
+        off += P
+    return out

@@ -38,3 +38,14 @@ def test_multi_gpu_request_exits_with_message():
                        text=True, cwd=bench.ROOT, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_ranked_bytes_by_hand():
+    # pools of ranks 16 (2 adapters) and 64 (1 adapter); rows on adapters 0, 2, 2
+    q = synth.random_ranked_problem((9,), n=3, h_in=8, h_out=16, pools=[(2, 16), (1, 64)],
+                                    dtype="bf16", ids=np.array([0, 2, 2], np.int32))
+    assert bench.ranked_bytes(q) == 2 * (3 * 8 + 2 * 3 * 16 + (16 + 64) * (8 + 16))
+    assert bench.ranked_flops(q) == 2 * (16 + 64 + 64) * (8 + 16)
+    q = synth.mixed70b_ranked("k")
+    assert q.n == 2112 and sorted(q.scales) == [16, 64]
+    assert set(q.ranks()[q.ids[64:1088]]) == {16} and set(q.ranks()[q.ids[1088:]]) == {64}

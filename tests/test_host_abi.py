@@ -10,6 +10,7 @@ import pytest
 
 import oracle
 from adapter_gemv_amd import _lib, sgmv
+from workloads import synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sgmv.h")
@@ -247,3 +248,84 @@ def test_build_segments_device_rejects():
     L = _lib.lib()
     assert L.sgmv_build_segments_device(None, TAB, 4097, 4, V, V, V, V) == _lib.ERR_SHAPE
     assert L.sgmv_build_segments_device(None, None, 3, 4, V, V, V, V) == _lib.ERR_NULL
+
+
+# --------------------------------------------------------------------------------------
+# mixed ranks
+# --------------------------------------------------------------------------------------
+RANKED_CASES = [
+    ("random", np.random.default_rng(21).integers(0, 7, 300), [64, 16, 32, 16, 64, 16, 32]),
+    ("one_rank", np.random.default_rng(22).integers(0, 5, 50), [32] * 5),
+    ("mixed70b", synth.mixed70b_ids(np.random.default_rng(23)), [16, 64] * 25),
+    ("n1", np.array([2]), [16, 16, 64]),
+    ("n0", np.zeros(0), [16]),
+]
+
+
+@pytest.mark.parametrize("name,ids,rank", RANKED_CASES, ids=[c[0] for c in RANKED_CASES])
+def test_build_segments_ranked_matches_oracle(name, ids, rank):
+    ids = np.asarray(ids, np.int32)
+    tab = sgmv.sgmv_build_segments_ranked(ids, rank)
+    perm, groups = oracle.segments_ranked(ids, np.array(rank, np.int32))
+    assert np.array_equal(tab.perm, perm)
+    assert len(tab.groups) == len(groups)
+    for g, (r, row0, n, starts, seg_ad) in zip(tab.groups, groups):
+        assert (g.r, g.row0, g.n, g.n_segments) == (r, row0, n, len(seg_ad))
+        assert np.array_equal(tab.seg_starts[g.starts0: g.starts0 + g.n_segments + 1], starts)
+        assert np.array_equal(tab.seg_adapter[g.seg0: g.seg0 + g.n_segments], seg_ad)
+        lens = np.diff(starts)
+        assert (g.min_seg_len, g.max_seg_len) == (int(lens.min()), int(lens.max()))
+        assert g.scale == 1.0
+
+
+def test_build_segments_ranked_rejects():
+    with pytest.raises(sgmv.SgmvError) as e:
+        sgmv.sgmv_build_segments_ranked(np.array([0, 3], np.int32), [16, 16, 16])
+    assert e.value.status == _lib.ERR_ADAPTER_ID
+    with pytest.raises(sgmv.SgmvError) as e:
+        sgmv.sgmv_build_segments_ranked(np.array([0, 1], np.int32), [16, 24])
+    assert e.value.status == _lib.ERR_UNSUPPORTED
+
+
+def _groups(*gs):
+    arr = (_lib.RankGroup * max(len(gs), 1))()
+    for i, g in enumerate(gs):
+        arr[i] = _lib.RankGroup(*g)
+    return arr
+
+
+def _ranked(groups, n_groups=None, **kw):
+    a = dict(stream=None, dtype=1, y=Y, ld_y=4096, x=X, ld_x=4096, A_ptrs=TAB, B_ptrs=TAB + 256,
+             seg_starts=TAB + 512, perm=TAB + 1024, n=64, h_in=4096, h_out=4096, workspace=WS,
+             workspace_bytes=1 << 30)
+    a.update(kw)
+    arr = _groups(*groups)
+    return sgmv.sgmv_lora_add_ranked(groups=ctypes.addressof(arr),
+                                     n_groups=len(groups) if n_groups is None else n_groups, **a)
+
+
+G16 = (16, 0, 32, 0, 0, 32, 1, 1, 2.0)      # r, row0, n, seg0, starts0, S, min, max, scale
+G64 = (64, 32, 32, 32, 33, 2, 16, 16, 0.5)
+RANKED_REJECTS = [
+    ("rank", [G16, (24,) + G64[1:]], {}, _lib.ERR_UNSUPPORTED),
+    ("rows past n", [G16, G64[:1] + (40,) + G64[2:]], {}, _lib.ERR_SHAPE),
+    ("segment bounds", [G16, G64[:5] + (2, 20, 20, 0.5)], {}, _lib.ERR_SHAPE),
+    ("negative seg0", [G16, G64[:3] + (-1,) + G64[4:]], {}, _lib.ERR_SHAPE),
+    ("n_groups<0", [G16], dict(n_groups=-1), _lib.ERR_SHAPE),
+    ("perm null", [G16, G64], dict(perm=None), _lib.ERR_NULL),
+    ("dtype", [G16], dict(dtype=5), _lib.ERR_UNSUPPORTED),
+    ("ws for r=16 only", [G16, G64], dict(workspace_bytes=sgmv.sgmv_workspace_bytes(64, 4096, 16)),
+     _lib.ERR_WORKSPACE),
+    ("alias", [G16, G64], dict(y=X + 64), _lib.ERR_ALIAS),
+    ("h_in%8", [G16], dict(h_in=4092, ld_x=4092), _lib.ERR_ALIGNMENT),
+]
+
+
+@pytest.mark.parametrize("name,gs,kw,code", RANKED_REJECTS, ids=[r[0] for r in RANKED_REJECTS])
+def test_lora_add_ranked_rejects(name, gs, kw, code):
+    assert _ranked(gs, **kw) == code
+
+
+def test_lora_add_ranked_empty_is_ok():
+    assert _ranked([], n_groups=0, x=None, y=None) == _lib.OK
+    assert _ranked([G16[:2] + (0, 0, 0, 0, 0, 0, 1.0)], n=0) == _lib.OK

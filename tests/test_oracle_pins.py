@@ -284,6 +284,96 @@ def test_ptr_table():
 
 
 # --------------------------------------------------------------------------------------
+# mixed ranks
+# --------------------------------------------------------------------------------------
+def _ranked_tiny(dtype, seed=0):
+    """Three pools of ranks 1, 2 and 3 (any r is valid for the oracle), ids over all of
+    them, a different scale per rank."""
+    rng = np.random.default_rng(700 + seed)
+    n, h_in, h_out = 7, 16, 8
+    pools = []
+    for k, (P, r) in enumerate([(2, 1), (3, 2), (1, 3)]):
+        q = synth.random_problem((701, seed, k), n=1, h_in=h_in, h_out=h_out, r=r,
+                                 n_adapters=P, dtype=dtype)
+        pools.append((q.A, q.B))
+    base = synth.random_problem((702, seed), n=n, h_in=h_in, h_out=h_out, r=1, n_adapters=6,
+                                dtype=dtype)
+    ids = rng.integers(0, 6, n).astype(np.int32)
+    scales = {1: 0.75, 2: 2.0, 3: -1.5}
+    return base.x, base.y, ids, pools, scales
+
+
+def brute_force_ranked(x, y, ids, pools, scales, dtype):
+    """Exact rationals, row by row: the row's pool k and local index give its A, B and r,
+    and the rank's scale multiplies the product."""
+    out = np.empty((ids.size, y.shape[1]), dtype=object)
+    off = 0
+    for A_k, B_k in pools:
+        P, r = A_k.shape[0], A_k.shape[1]
+        for t in range(ids.size):
+            if off <= ids[t] < off + P:
+                row = synth.Problem("row", dtype, np.array([ids[t] - off], np.int32),
+                                    x[t:t + 1], y[t:t + 1], A_k, B_k, scales[r])
+                out[t] = brute_force(row)[1][0]
+        off += P
+    return out
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("seed", range(2))
+def test_ranked_brute_force_exact_rationals(dtype, seed):
+    x, y, ids, pools, scales = _ranked_tiny(dtype, seed)
+    want = _as_f64(brute_force_ranked(x, y, ids, pools, scales, dtype))
+    got = oracle.lora_add_ranked(y, x, ids, pools, scales, dtype)
+    assert np.all(np.abs(got - want) <= 1e-12 * (1 + np.abs(want)))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_ranked_equals_zero_padded_single_rank(dtype):
+    """Adapters of rank 16 padded with zero columns of A and zero rows of B to rank 64 give
+    the same update, so with one scale for both ranks the mixed batch equals a rank-64
+    batch over the padded pool."""
+    p16 = synth.random_problem((703, 1), n=40, h_in=64, h_out=48, r=16, n_adapters=3,
+                               dtype=dtype)
+    p64 = synth.random_problem((703, 2), n=40, h_in=64, h_out=48, r=64, n_adapters=2,
+                               dtype=dtype)
+    ids = np.random.default_rng(704).integers(0, 5, 40).astype(np.int32)
+    A16 = np.zeros((3, 64, 64), p16.A.dtype)
+    A16[:, :16, :] = p16.A
+    B16 = np.zeros((3, 48, 64), p16.B.dtype)
+    B16[:, :, :16] = p16.B
+    A = np.concatenate([A16, p64.A])
+    B = np.concatenate([B16, p64.B])
+    got = oracle.lora_add_ranked(p16.y, p16.x, ids, [(p16.A, p16.B), (p64.A, p64.B)],
+                                 {16: 1.25, 64: 1.25}, dtype)
+    want = oracle.lora_add(p16.y, p16.x, ids, A, B, 1.25, dtype)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", ["random", "one_rank", "n1", "n0"])
+def test_segments_ranked_definition(case):
+    rng = np.random.default_rng(9)
+    rank = np.array([64, 16, 32, 16, 64, 16, 32], np.int32)
+    ids = {"random": rng.integers(0, 7, 120), "one_rank": rng.choice([1, 3, 5], 30),
+           "n1": np.array([4]), "n0": np.zeros(0)}[case].astype(np.int32)
+    perm, groups = oracle.segments_ranked(ids, rank)
+    n = ids.size
+    assert sorted(perm.tolist()) == list(range(n))
+    keys = [(int(rank[ids[i]]), int(ids[i]), int(i)) for i in perm]
+    assert all(keys[i] < keys[i + 1] for i in range(n - 1))
+    assert [g[0] for g in groups] == sorted(set(int(rank[a]) for a in ids))
+    row = 0
+    for r, row0, gn, starts, seg_ad in groups:
+        assert row0 == row and starts[0] == 0 and starts[-1] == gn and np.all(np.diff(starts) > 0)
+        for s, a in enumerate(seg_ad):
+            rows = perm[row0 + starts[s]: row0 + starts[s + 1]]
+            assert rank[a] == r and np.all(ids[rows] == a)
+        assert np.array_equal(seg_ad, np.unique(ids[perm[row0:row0 + gn]]))
+        row += gn
+    assert row == n
+
+
+# --------------------------------------------------------------------------------------
 # planted mistakes: a mutated oracle must fail at least one pin
 # --------------------------------------------------------------------------------------
 MUTATIONS = [
@@ -294,7 +384,10 @@ MUTATIONS = [
     ("unstable sort", "for i, t in enumerate(ids):", "for i, t in reversed(list(enumerate(ids))):"),
     ("bf16 shift", "<< np.uint32(16)", "<< np.uint32(15)"),
     ("round toward zero", "np.rint(np.ldexp(m, 8))", "np.trunc(np.ldexp(m, 8))"),
-    ("y not added", "out = decode(y, dtype).copy()", "out = np.zeros_like(decode(y, dtype))"),
+    ("y not added", "out = decode(y, dtype).copy()\n    for a in", "out = np.zeros_like(decode(y, dtype))\n    for a in"),
+    ("ranked: one scale for every rank", "B_k, scales[r], dtype)", "B_k, scales[min(scales)], dtype)"),
+    ("ranked: pools not offset", "        off += P\n    return out", "        off += 0\n    return out"),
+    ("ranked: rank not the leading key", "keys = [(int(rank[a]), int(a), t)", "keys = [(0 * int(rank[a]), int(a), t)"),
 ]
 
 
@@ -326,6 +419,15 @@ def _pins_pass(mod, golden_dir):
         ids = np.array([2, 0, 2, 1, 0, 2], np.int32)
         perm, _, _ = mod.segments(ids, 3)
         if not np.array_equal(perm, np.argsort(ids, kind="stable")):
+            return False
+        x, y, rids, pools, scales = _ranked_tiny("bf16")
+        want = _as_f64(brute_force_ranked(x, y, rids, pools, scales, "bf16"))
+        if not np.allclose(mod.lora_add_ranked(y, x, rids, pools, scales, "bf16"), want,
+                           rtol=1e-12, atol=1e-12):
+            return False
+        perm, groups = mod.segments_ranked(np.array([0, 1, 0, 2], np.int32),
+                                           np.array([64, 16, 32], np.int32))
+        if perm.tolist() != [1, 3, 0, 2] or [g[0] for g in groups] != [16, 32, 64]:
             return False
     except Exception:
         return False

@@ -238,6 +238,70 @@ def prefill13b_len(length: int, proj: str = "gateup") -> Problem:
                           name=f"prefill13b_{proj}_len{length}")
 
 
+@dataclasses.dataclass
+class RankedProblem:
+    """One mixed-rank call: adapters numbered across ``pools`` (pool k holds ids
+    off_k .. off_k + P_k - 1, off_k = sum of the earlier pools' sizes); row t gets
+    ``y[t] += scales[r] * (x[t] @ A[ids[t]]) @ B[ids[t]]`` with its adapter's rank r."""
+
+    name: str
+    dtype: str
+    ids: np.ndarray          # int32 [n]
+    x: np.ndarray            # [n, h_in]
+    y: np.ndarray            # [n, h_out]
+    pools: list              # [(A [P_k, r_k, h_in], B [P_k, h_out, r_k])]
+    scales: dict             # rank -> scale
+
+    @property
+    def n(self) -> int:
+        return int(self.ids.shape[0])
+
+    @property
+    def h_in(self) -> int:
+        return int(self.x.shape[1])
+
+    @property
+    def h_out(self) -> int:
+        return int(self.y.shape[1])
+
+    def ranks(self) -> np.ndarray:
+        """Rank of every adapter id."""
+        return np.concatenate([np.full(A.shape[0], A.shape[1], np.int32) for A, _ in self.pools])
+
+
+def random_ranked_problem(seed: Sequence[int], *, n: int, h_in: int, h_out: int, pools,
+                          dtype: str, ids: Optional[np.ndarray] = None,
+                          name: str = "ranked") -> RankedProblem:
+    """``pools`` = [(P_k, r_k)]; ids uniform over all adapters unless given; the scale of
+    rank r is 32 / r."""
+    g_ids, g_x, g_y, g_a, g_b = _streams(seed)
+    total = sum(P for P, _ in pools)
+    if ids is None:
+        ids = g_ids.integers(0, total, size=n, dtype=np.int32)
+    x = quantize(_normal(g_x, (n, h_in), 1.0), dtype)
+    y = quantize(_normal(g_y, (n, h_out), 1.0), dtype)
+    out = []
+    for P, r in pools:
+        A = quantize(_normal(g_a, (P, r, h_in), 1.0 / np.sqrt(h_in)), dtype)
+        B = quantize(_normal(g_b, (P, h_out, r), 1.0 / np.sqrt(r)), dtype)
+        out.append((A, B))
+    scales = {r: 32.0 / r for _, r in pools}
+    return RankedProblem(name, dtype, np.ascontiguousarray(ids, dtype=np.int32), x, y, out, scales)
+
+
+def mixed70b_ranked(proj: str) -> RankedProblem:
+    """The 70B mixed batch with both ranks in one call: of the 50 adapters, the even ones
+    (including prefill adapter 48) have r = 16 and the odd ones (including 49) r = 64.
+    Pool 0 holds the 25 rank-16 adapters, pool 1 the 25 rank-64 ones; scale 32 / r."""
+    h_in, h_out = MIXED70B_SHAPES[proj]
+    idx = list(MIXED70B_SHAPES).index(proj)
+    orig = mixed70b_ids(_streams((5, 0), 6)[5])
+    ids = np.where(orig % 2 == 0, orig // 2, 25 + orig // 2).astype(np.int32)
+    return random_ranked_problem((8, idx), n=ids.size, h_in=h_in, h_out=h_out,
+                                 pools=[(25, 16), (25, 64)], dtype=BF16, ids=ids,
+                                 name=f"mixed70b_rmix_{proj}")
+
+
 def all_workloads(include_large: bool = True):
     """(name, factory) pairs for every workload projection."""
     out = [("tiny", tiny), ("decode7b", decode7b)]
