@@ -483,8 +483,24 @@ struct ExpCfg {
   static constexpr int RB = TR / 16, CB = TC / 64;  // 16 x 16 blocks per wave
   static constexpr int PAD = 4;                     // floats of padding per LDS row of sums
   // waves per SIMD the register budget is set for
-  static constexpr int WAVES_PER_SIMD = (R == 16) ? 4 : 3;
+  static constexpr int WAVES_PER_SIMD = 4;
 };
+
+// The B operand of one run for a wave's CB column blocks: lane (l16, kq) takes column
+// wc + 16cb + l16 and B values 32s + 8kq .. +7 (mod r) of it, s < NKU.
+template <int R, int CB, int NKU>
+__device__ inline void exp_load_b(gptr<const uint16_t> B, int wc, int l16, int kq, int h_out,
+                                  uint4 (&bop)[CB][NKU]) {
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int col = wc + 16 * cb + l16;
+#pragma unroll
+    for (int s = 0; s < NKU; ++s) {
+      const int j0 = (32 * s + 8 * kq) % R;
+      bop[cb][s] = (col < h_out) ? ld16(B + static_cast<int64_t>(col) * R + j0) : zero4();
+    }
+  }
+}
 
 template <int DT, int R>
 __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_kernel(
@@ -499,13 +515,20 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
   constexpr int TR = C::TR, TC = C::TC, RB = C::RB, CB = C::CB;
   constexpr int KT = 2 * R;          // k of the hi/lo product
   constexpr int NK = KT / 32;        // MFMA k-steps
+  constexpr int NKU = (R >= 32) ? R / 32 : 1;  // distinct B loads per column block
   constexpr int VPT = TR * R / 256;  // v values per thread
   constexpr int VPR = TC / 8;        // 16-byte vectors per tile row
   constexpr int YPT = TR * VPR / 256;  // 16-byte vectors of y per thread
   __shared__ TileSegs<TR> sh;
   __shared__ int s_prow[TR];  // caller row of each tile row
-  __shared__ __attribute__((aligned(16))) uint16_t vlds[TR][KT];
-  __shared__ __attribute__((aligned(16))) float dl[TR][TC + C::PAD];
+  // The hi/lo halves of scale * v (vlds) and, after the products, the float32 sums (dl)
+  // share one LDS buffer.  vlds rows are padded by 16 bytes: the 16 lanes that read one k
+  // range of 16 different rows then fall on 16 different bank groups instead of one.
+  typedef uint16_t VRows[TR][KT + 8];
+  typedef float DRows[TR][TC + C::PAD];
+  __shared__ __attribute__((aligned(16))) char smem[sizeof(DRows) > sizeof(VRows) ? sizeof(DRows) : sizeof(VRows)];
+  VRows& vlds = *reinterpret_cast<VRows*>(smem);
+  DRows& dl = *reinterpret_cast<DRows*>(smem);
   __shared__ int s_exp[TR];  // fp16: the row's sums are multiplied by 2^s_exp[row]
 
   // XCD x owns strips [sx0, sx1) and walks them tile-major
@@ -543,6 +566,15 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
   }
   if (tile_long_segments<TR, 256>(seg_starts, S, g0, g1, sh) == 0) return;  // uniform
 
+  // B of the tile's first long run goes out now, so that its latency (a dependent pointer
+  // load, then the B rows) overlaps the wait for v.  B row c holds the r values of column
+  // c; the product's k runs over the hi halves, then the lo halves, so the k-steps past r
+  // reuse the same B bytes: only NKU = r / 32 distinct loads per column block.
+  int q = 0;
+  int sg = next_run(sh, q);  // the tile meets a long segment, so there is a first run
+  uint4 bop[CB][NKU];
+  exp_load_b<R, CB, NKU>(global_ptr(B_ptrs[sg]), wc, l16, kq, h_out, bop);
+
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
     const int idx = tid + 256 * u;
@@ -572,19 +604,7 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // the long segments of the tile, in increasing order (the reads are uniform)
-  int q = 0;
-  for (int sg; (sg = next_run(sh, q)) >= 0;) {
-    const gptr<const uint16_t> B = global_ptr(B_ptrs[sg]);
-    uint4 bop[CB][NK];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int col = wc + 16 * cb + l16;
-#pragma unroll
-      for (int s = 0; s < NK; ++s) {
-        const int j0 = (32 * s + 8 * kq) % R;
-        bop[cb][s] = (col < h_out) ? ld16(B + static_cast<int64_t>(col) * R + j0) : zero4();
-      }
-    }
+  for (;;) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int lq = 16 * rb + l16;
@@ -595,9 +615,12 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int s = 0; s < NK; ++s) acc[rb][cb] = E::mfma(bop[cb][s], vop[s], acc[rb][cb]);
+        for (int s = 0; s < NK; ++s) acc[rb][cb] = E::mfma(bop[cb][s % NKU], vop[s], acc[rb][cb]);
     }
+    if ((sg = next_run(sh, q)) < 0) break;
+    exp_load_b<R, CB, NKU>(global_ptr(B_ptrs[sg]), wc, l16, kq, h_out, bop);
   }
+  __syncthreads();  // every wave is done reading vlds before dl overwrites it
   // lane: D rows 4*kq .. +3 of column block cb = tile columns (TC/4)w + 16cb + 4kq .. +3,
   // D column l16 = tile row 16rb + l16
 #pragma unroll
