@@ -67,16 +67,14 @@ inline int check_device() {
 //                           [S, min_len, max_len, n_valid], n_segments, perm, seg_starts,
 //                           seg_adapter, sorted ids, A and B pointer tables)
 //   ... free ...
-//   [tile_cnt_off, pool)    table path: one counter per shrink tile, one per 256-byte
-//                           line, just below the tagged partials
 //   [pool, end)             last pool_bytes(h_in, r) bytes of the caller's buffer (start
 //                           rounded down to 256): decode path: tagged 64-bit split-K
 //                           partial sums, laid out for 64 rows whatever n is
 // Counters and the tagged partials are zero before a call and are left at zero by it;
 // rowks, v, the partial sums and the device tables are scratch.  The scratch end grows
-// with n, h_in and r and so does the size of the zero regions at the back, so in a buffer
-// of sgmv_workspace_bytes(n, h_in, r) bytes no call of at most n rows, h_in and r writes
-// scratch over another such call's counters or tagged partials.
+// with n, h_in and r and so does the size of the tagged partials at the back, so in a
+// buffer of sgmv_workspace_bytes(n, h_in, r) bytes no call of at most n rows, h_in and r
+// writes scratch over another such call's counters or tagged partials.
 // ------------------------------------------------------------------------------------
 constexpr int kMaxPoolRows = 64;
 constexpr size_t kWsPoolCounters = 256;
@@ -127,16 +125,14 @@ inline DevTabLayout dev_tab_layout(int32_t n) {
 }
 
 struct WsLayout {
-  size_t rowks_off, v_off, part_off, dtab_off, table_end, tile_cnt_off, total;
+  size_t rowks_off, v_off, part_off, dtab_off, table_end, total;
   int64_t slice;  // floats per split-K slice of the table path (n * r)
   int ks_max;     // table path: split-K slices the partial-sum area holds
 };
 
-// Layout of a call of n rows, h_in and rank r in a buffer of ws_bytes bytes (0: the
-// smallest buffer that fits, whose size is .total).
-inline WsLayout ws_layout(int32_t n, int32_t h_in, int32_t r, size_t ws_bytes = 0) {
+// Layout of a call of n rows, h_in and rank r; .total is the smallest buffer that fits.
+inline WsLayout ws_layout(int32_t n, int32_t h_in, int32_t r) {
   WsLayout L{};
-  const size_t tiles = static_cast<size_t>((n + 15) / 16);
   L.ks_max = (h_in + table_gemv_kc(r) - 1) / table_gemv_kc(r);
   const int ks_mfma = std::min(32, std::max(1, h_in / 256));  // MFMA shrink slices, at most
   if (ks_mfma > L.ks_max) L.ks_max = ks_mfma;
@@ -146,11 +142,9 @@ inline WsLayout ws_layout(int32_t n, int32_t h_in, int32_t r, size_t ws_bytes = 
   L.part_off = align_up(L.v_off + sizeof(float) * static_cast<size_t>(L.slice), 256);
   L.dtab_off = align_up(L.part_off + sizeof(float) * static_cast<size_t>(L.slice) * L.ks_max, 256);
   L.table_end = L.dtab_off + dev_tab_layout(n).bytes;
-  const size_t cnt = sizeof(int32_t) * kCounterInts * tiles;
   // 256 bytes of slack so that the tagged partials' start, rounded down, stays past the
-  // tile counters
-  L.total = L.table_end + 256 + cnt + pool_bytes(h_in, r);
-  L.tile_cnt_off = pool_offset(ws_bytes ? ws_bytes : L.total, h_in, r) - cnt;
+  // scratch
+  L.total = L.table_end + 256 + pool_bytes(h_in, r);
   return L;
 }
 
@@ -162,6 +156,6 @@ hipError_t table_lora_add_device(hipStream_t st, int32_t dtype, int32_t r, void*
                                  const void* const* B_ptrs, const int32_t* seg_starts,
                                  const int32_t* perm, const int32_t* meta, int32_t n,
                                  int32_t S_max, int32_t h_in, int32_t h_out, float scale,
-                                 void* workspace, size_t workspace_bytes);
+                                 void* workspace);
 
 }  // namespace sgmv_host

@@ -614,7 +614,7 @@ extern "C" int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, in
   if (n > kPoolMaxN) {
     // device sort into the workspace, then the table path on those tables
     char* wsb = static_cast<char*>(workspace);
-    const WsLayout L = ws_layout(n, h_in, r, workspace_bytes);
+    const WsLayout L = ws_layout(n, h_in, r);
     const DevTabLayout D = dev_tab_layout(n);
     char* dt = wsb + L.dtab_off;
     SortOut o{};
@@ -637,7 +637,7 @@ extern "C" int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, in
     return hip_status(table_lora_add_device(
         stream, dtype, r, y, ld_y, x, ld_x, reinterpret_cast<const void* const*>(o.A_ptrs),
         reinterpret_cast<const void* const*>(o.B_ptrs), o.seg_starts, o.perm, o.meta, n, S_max,
-        h_in, h_out, scale, workspace, workspace_bytes));
+        h_in, h_out, scale, workspace));
   }
 
   PoolArgs p;

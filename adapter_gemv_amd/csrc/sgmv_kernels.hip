@@ -182,8 +182,6 @@ __global__ __launch_bounds__(64) void expand_gemv_kernel(
 // ------------------------------------------------------------------------------------
 // long-segment path (segments with >= kLongMin rows)
 // ------------------------------------------------------------------------------------
-constexpr int kCounterStride = kCounterInts;  // one tile counter per 256-byte line
-
 __device__ inline void store_coherent(float* q, float v) {
   __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -251,9 +249,9 @@ __device__ inline int next_run(const TileSegs<ROWS>& sh, int& q) {
 // in equal amounts; the waves take interleaved stages of UN k steps, with the loads of the next
 // stage in flight while the current one is multiplied, and are summed through LDS in a
 // fixed order.  Rows of several long segments in one tile are handled run by run with the
-// other rows' x set to zero.  With one chunk per tile v is written directly; otherwise the
-// chunks go out as agent-scope atomic stores and the last chunk of the tile (per a
-// counter on its own cache line) adds them in order, writes v and resets the counter.
+// other rows' x set to zero.  With one chunk per tile v is written directly; otherwise
+// each chunk writes its slice of partial sums and reduce_v_kernel, the next launch, adds
+// the slices in order (no wait on other workgroups inside this kernel).
 //
 // With a multiple of 8 chunks, workgroup b (on XCD b % 8) takes chunks = b mod 8, so each
 // XCD's L2 keeps one eighth of the K range of the adapters' A.
@@ -316,7 +314,7 @@ __global__ __launch_bounds__(256, ShrCfg<R>::WAVES_PER_SIMD) void shrink_mfma_ke
     const uint16_t* __restrict__ x, int64_t ld_x, const uint16_t* const* __restrict__ A_ptrs,
     const int32_t* __restrict__ seg_starts, int32_t S_host, const int32_t* __restrict__ perm,
     int32_t n, int32_t h_in, int32_t kcm, int32_t ks, float* __restrict__ part, int64_t slice,
-    int32_t* __restrict__ tile_cnt, float* __restrict__ v_out, int32_t* __restrict__ rowks,
+    float* __restrict__ v_out, int32_t* __restrict__ rowks,
     const int32_t* __restrict__ meta) {
   const int S = meta ? meta[0] : S_host;
   if (meta && meta[2] < kLongMin) return;  // no long segment at all
@@ -324,7 +322,6 @@ __global__ __launch_bounds__(256, ShrCfg<R>::WAVES_PER_SIMD) void shrink_mfma_ke
   constexpr int NB = C::NB, RB = C::RB, UN = C::UN, STAGE = C::STAGE, MT = C::MT;
   __shared__ TileSegs<MT> sh;
   __shared__ int s_prow[MT];
-  __shared__ int s_last;
   __shared__ f32x4_t red[2][RB][NB][64];
 
   const int b = blockIdx.x;
@@ -406,57 +403,13 @@ __global__ __launch_bounds__(256, ShrCfg<R>::WAVES_PER_SIMD) void shrink_mfma_ke
       if (ks == 1)
         v_out[o] = sum[c];
       else
-        store_coherent(part + kc * slice + o, sum[c]);
+        part[kc * slice + o] = sum[c];
     }
   }
+  // rows of long segments: final v (ks == 1) or ks slices for reduce_v_kernel
   if (kc == 0)
     for (int qr = tid; qr < r1 - r0; qr += 256)
-      if (sh.rseg[qr] >= 0) rowks[r0 + qr] = 0;  // v of long rows is final, not in slices
-  if (ks == 1) return;
-
-  // publish this chunk, then let the last chunk of the tile reduce and write v
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(&tile_cnt[tile * kCounterStride], 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (old == ks - 1);
-    if (s_last)
-      __hip_atomic_store(&tile_cnt[tile * kCounterStride], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  // The tile's part of each slice is contiguous (rows r0.. of R floats): thread t takes
-  // the 4-float groups t, t + 256, ..., reads up to 16 slices of them at once as 64-bit
-  // coherent loads and adds the slices in order.
-  constexpr int kSl = 16;
-  const int nq = (r1 - r0) * R / 4;
-  for (int qd = tid; qd < nq; qd += 256) {
-    if (sh.rseg[qd * 4 / R] < 0) continue;
-    const uint64_t* src = reinterpret_cast<const uint64_t*>(part + static_cast<int64_t>(r0) * R) + 2 * qd;
-    f32x4_t a = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < ks; k0 += kSl) {
-      uint64_t lo[kSl], hi[kSl];
-#pragma unroll
-      for (int u = 0; u < kSl; ++u) {
-        const bool in = k0 + u < ks;
-        const uint64_t* q = src + (in ? (k0 + u) : 0) * (slice / 2);
-        lo[u] = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        hi[u] = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-#pragma unroll
-      for (int u = 0; u < kSl; ++u) {
-        const bool in = k0 + u < ks;
-        a[0] += in ? __uint_as_float(static_cast<uint32_t>(lo[u])) : 0.f;
-        a[1] += in ? __uint_as_float(static_cast<uint32_t>(lo[u] >> 32)) : 0.f;
-        a[2] += in ? __uint_as_float(static_cast<uint32_t>(hi[u])) : 0.f;
-        a[3] += in ? __uint_as_float(static_cast<uint32_t>(hi[u] >> 32)) : 0.f;
-      }
-    }
-    *reinterpret_cast<f32x4_t*>(v_out + static_cast<int64_t>(r0) * R + 4 * qd) = a;
-  }
+      if (sh.rseg[qr] >= 0) rowks[r0 + qr] = (ks == 1) ? 0 : ks;
 }
 
 // Expand on MFMA 16x16x32 for a tile of TR sorted rows and TC columns, computed
@@ -476,6 +429,9 @@ __global__ __launch_bounds__(256, ShrCfg<R>::WAVES_PER_SIMD) void shrink_mfma_ke
 // of column strips, so its L2 holds only that part of every B[a]; within the range the
 // workgroups go row tile by row tile, so the y traffic in flight at any time covers whole
 // rows of a few consecutive tiles.
+// split-K slices of long rows that the MFMA expand adds itself (above: reduce_v_kernel)
+constexpr int kExpandSlices = 4;
+
 template <int R>
 struct ExpCfg {
   static constexpr int TR = (R == 16) ? 32 : 64;    // rows per tile
@@ -502,9 +458,11 @@ __device__ inline void exp_load_b(gptr<const uint16_t> B, int wc, int l16, int k
   }
 }
 
-template <int DT, int R>
+// VS: v comes as up to VS split-K slices (vks of them, vslice floats apart) that are added
+// here in slice order; VS == 1: v is final.
+template <int DT, int R, int VS>
 __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_kernel(
-    uint16_t* __restrict__ y, int64_t ld_y, const float* __restrict__ v,
+    uint16_t* __restrict__ y, int64_t ld_y, const float* __restrict__ v, int64_t vslice, int32_t vks,
     const uint16_t* const* __restrict__ B_ptrs, const int32_t* __restrict__ seg_starts,
     int32_t S_host, const int32_t* __restrict__ perm, int32_t n, int32_t h_out, float scale,
     int32_t tiles, int32_t strips, const int32_t* __restrict__ meta) {
@@ -559,10 +517,21 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
     yv[u] = (prow >= 0 && col < h_out) ? ld16(y + static_cast<int64_t>(prow) * ld_y + col) : zero4();
   }
   float vv[VPT];
+  {
+    float t[VS][VPT];
 #pragma unroll
-  for (int u = 0; u < VPT; ++u) {
-    const int idx = tid + 256 * u;
-    vv[u] = (g0 + idx / R < g1) ? v[static_cast<int64_t>(g0) * R + idx] : 0.f;
+    for (int k = 0; k < VS; ++k)
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        const int idx = tid + 256 * u;
+        t[k][u] = (k < vks && g0 + idx / R < g1) ? v[k * vslice + static_cast<int64_t>(g0) * R + idx] : 0.f;
+      }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      vv[u] = t[0][u];
+#pragma unroll
+      for (int k = 1; k < VS; ++k) vv[u] += t[k][u];  // slices past vks add exact zeros
+    }
   }
   if (tile_long_segments<TR, 256>(seg_starts, S, g0, g1, sh) == 0) return;  // uniform
 
@@ -652,18 +621,35 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
   }
 }
 
-// v[i, :] = sum of the split-K slices of sorted row i, in slice order, for rows whose
-// slice count is nonzero (rows of long segments already have their final v).
+// v[i, :] = sum of the split-K slices of sorted row i, for rows whose slice count is
+// nonzero (rows of long segments with one slice already have their final v).  A workgroup
+// takes 64 consecutive entries of v; wave q adds slices q, q + 4, q + 8, ... of each entry
+// in that order and the four waves' sums are added as (w0 + w1) + (w2 + w3).
 template <int R>
 __global__ __launch_bounds__(256) void reduce_v_kernel(float* __restrict__ v,
                                                       const float* __restrict__ part, int64_t slice,
                                                       const int32_t* __restrict__ rowks, int32_t n,
                                                       int32_t ks_max) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= static_cast<int64_t>(n) * R) return;
-  const int row = static_cast<int>(idx / R);
-  const int ks = min(rowks[row], ks_max);
-  if (ks > 0) v[idx] = sum_slices(part + idx, slice, ks);
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 64 + lane;
+  const bool in = idx < static_cast<int64_t>(n) * R;
+  const int ks = in ? min(rowks[idx / R], ks_max) : 0;
+  float acc = 0.f;
+  constexpr int kFly = 8;  // loads in flight per thread
+  for (int k0 = q; k0 < ks; k0 += 4 * kFly) {
+    float t[kFly];
+#pragma unroll
+    for (int u = 0; u < kFly; ++u) {
+      const int k = k0 + 4 * u;
+      t[u] = (k < ks) ? part[k * slice + idx] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kFly; ++u) acc += t[u];
+  }
+  red[q][lane] = acc;
+  __syncthreads();
+  if (q == 0 && ks > 0) v[idx] = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
 }
 
 // ------------------------------------------------------------------------------------
@@ -713,14 +699,17 @@ struct Tables {
   unsigned gemv_grid() const { return static_cast<unsigned>(meta ? (S < 256 ? S : 256) : S); }
 };
 
-// shrink kernels: short segments leave split-K slices (ks_gemv of them, counted in rowks),
-// long segments leave their final v in v_long
+// shrink kernels: short segments leave split-K slices (ks_gemv of them, counted in rowks);
+// long segments leave their final v in v_long (ks_long == 1) or ks_long slices, counted in
+// rowks, for reduce_v_kernel
 template <int DT, int R>
 hipError_t launch_shrink(hipStream_t st, const uint16_t* x, int64_t ld_x, const Tables& T,
-                         int32_t h_in, const WsLayout& L, char* ws, float* v_long, int* ks_gemv) {
+                         int32_t h_in, const WsLayout& L, char* ws, float* v_long, int* ks_gemv,
+                         int* ks_long) {
   float* part = reinterpret_cast<float*>(ws + L.part_off);
   int32_t* rowks = reinterpret_cast<int32_t*>(ws + L.rowks_off);
   *ks_gemv = 0;
+  *ks_long = 0;
   if (T.use_gemv()) {
     const int ks = (h_in + GemvCfg<R>::KC - 1) / GemvCfg<R>::KC;
     *ks_gemv = ks;
@@ -733,7 +722,8 @@ hipError_t launch_shrink(hipStream_t st, const uint16_t* x, int64_t ld_x, const 
     const int tiles = (T.n + ShrCfg<R>::MT - 1) / ShrCfg<R>::MT;
     hipLaunchKernelGGL((shrink_mfma_kernel<DT, R>), dim3(tiles * ks), dim3(256), 0, st, x, ld_x,
                        T.ptrs, T.seg_starts, T.S, T.perm, T.n, h_in, kcm, ks, part, L.slice,
-                       reinterpret_cast<int32_t*>(ws + L.tile_cnt_off), v_long, rowks, T.meta);
+                       v_long, rowks, T.meta);
+    *ks_long = ks;
   }
   return hipGetLastError();
 }
@@ -742,8 +732,8 @@ hipError_t launch_shrink(hipStream_t st, const uint16_t* x, int64_t ld_x, const 
 // segments read their final v from v_long
 template <int DT, int R>
 hipError_t launch_expand(hipStream_t st, uint16_t* y, int64_t ld_y, const float* vsrc,
-                         int64_t slice, int ks_gemv, const float* v_long, const Tables& T,
-                         int32_t h_out, float scale) {
+                         int64_t slice, int ks_gemv, const float* v_long, int64_t lslice,
+                         int ks_long, const Tables& T, int32_t h_out, float scale) {
   constexpr int CPL = 128 / R;
   if (T.use_gemv()) {
     const int chunks = (h_out + 64 * CPL - 1) / (64 * CPL);
@@ -757,43 +747,69 @@ hipError_t launch_expand(hipStream_t st, uint16_t* y, int64_t ld_y, const float*
     const int strips = (h_out + ExpCfg<R>::TC - 1) / ExpCfg<R>::TC;
     const int64_t share = static_cast<int64_t>(tiles) * ((strips + kXcds - 1) / kXcds);
     if (share * kXcds > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((expand_mfma_kernel<DT, R>), dim3(static_cast<unsigned>(share * kXcds)),
-                       dim3(256), 0, st, y, ld_y, v_long, T.ptrs, T.seg_starts, T.S, T.perm, T.n,
-                       h_out, scale, tiles, strips, T.meta);
+    const dim3 grid(static_cast<unsigned>(share * kXcds));
+    if (ks_long > 1) {
+      if constexpr (R <= 32) {
+        hipLaunchKernelGGL((expand_mfma_kernel<DT, R, kExpandSlices>), grid, dim3(256), 0, st, y,
+                           ld_y, v_long, lslice, ks_long, T.ptrs, T.seg_starts, T.S, T.perm, T.n,
+                           h_out, scale, tiles, strips, T.meta);
+      } else {
+        return hipErrorInvalidValue;  // r = 64: reduce_v_kernel runs first
+      }
+    } else {
+      hipLaunchKernelGGL((expand_mfma_kernel<DT, R, 1>), grid, dim3(256), 0, st, y, ld_y, v_long,
+                         lslice, 1, T.ptrs, T.seg_starts, T.S, T.perm, T.n, h_out, scale, tiles,
+                         strips, T.meta);
+    }
   }
   return hipGetLastError();
 }
 
-template <int DT, int R>
-hipError_t run_shrink(hipStream_t st, float* v, const uint16_t* x, int64_t ld_x, const Tables& T,
-                      int32_t h_in, const WsLayout& L, char* ws) {
-  int ksg;
-  hipError_t e = launch_shrink<DT, R>(st, x, ld_x, T, h_in, L, ws, v, &ksg);
-  if (e != hipSuccess) return e;
-  if (!T.use_gemv()) return hipSuccess;
+// v of every row whose slice count (rowks) is nonzero, summed in slice order
+template <int R>
+hipError_t launch_reduce(hipStream_t st, float* v, const Tables& T, const WsLayout& L, char* ws) {
   const int64_t total = static_cast<int64_t>(T.n) * R;
-  hipLaunchKernelGGL((reduce_v_kernel<R>), dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256),
+  hipLaunchKernelGGL((reduce_v_kernel<R>), dim3(static_cast<unsigned>((total + 63) / 64)), dim3(256),
                      0, st, v, reinterpret_cast<const float*>(ws + L.part_off), L.slice,
                      reinterpret_cast<const int32_t*>(ws + L.rowks_off), T.n, L.ks_max);
   return hipGetLastError();
 }
 
 template <int DT, int R>
+hipError_t run_shrink(hipStream_t st, float* v, const uint16_t* x, int64_t ld_x, const Tables& T,
+                      int32_t h_in, const WsLayout& L, char* ws) {
+  int ksg, ksl;
+  hipError_t e = launch_shrink<DT, R>(st, x, ld_x, T, h_in, L, ws, v, &ksg, &ksl);
+  if (e != hipSuccess) return e;
+  if (ksg == 0 && ksl <= 1) return hipSuccess;
+  return launch_reduce<R>(st, v, T, L, ws);
+}
+
+template <int DT, int R>
 hipError_t run_expand(hipStream_t st, uint16_t* y, int64_t ld_y, const float* v, const Tables& T,
                       int32_t h_out, float scale) {
-  return launch_expand<DT, R>(st, y, ld_y, v, 0, 1, v, T, h_out, scale);
+  return launch_expand<DT, R>(st, y, ld_y, v, 0, 1, v, 0, 1, T, h_out, scale);
 }
 
 template <int DT, int R>
 hipError_t run_lora_add(hipStream_t st, uint16_t* y, int64_t ld_y, const uint16_t* x, int64_t ld_x,
                         const Tables& TA, const Tables& TB, int32_t h_in, int32_t h_out, float scale,
                         const WsLayout& L, char* ws) {
-  int ksg;
+  int ksg, ksl;
   float* v_long = reinterpret_cast<float*>(ws + L.v_off);
-  hipError_t e = launch_shrink<DT, R>(st, x, ld_x, TA, h_in, L, ws, v_long, &ksg);
+  hipError_t e = launch_shrink<DT, R>(st, x, ld_x, TA, h_in, L, ws, v_long, &ksg, &ksl);
   if (e != hipSuccess) return e;
-  return launch_expand<DT, R>(st, y, ld_y, reinterpret_cast<const float*>(ws + L.part_off), L.slice,
-                              ksg, v_long, TB, h_out, scale);
+  const float* part = reinterpret_cast<const float*>(ws + L.part_off);
+  // A few slices of long rows are added by the MFMA expand itself (r <= 32), and up to 16
+  // slices of short rows by the GEMV expand.  Otherwise reduce_v_kernel sums every row's
+  // slices once instead of every column chunk of the expand kernels summing them again.
+  if ((ksl > 1 && (ksl > kExpandSlices || R > 32)) || ksg > 16) {
+    if ((e = launch_reduce<R>(st, v_long, TA, L, ws)) != hipSuccess) return e;
+    return launch_expand<DT, R>(st, y, ld_y, v_long, 0, 1, v_long, 0, 1, TB, h_out, scale);
+  }
+  if (ksl > 1)
+    return launch_expand<DT, R>(st, y, ld_y, part, L.slice, ksg, part, L.slice, ksl, TB, h_out, scale);
+  return launch_expand<DT, R>(st, y, ld_y, part, L.slice, ksg, v_long, 0, 1, TB, h_out, scale);
 }
 
 template <template <int, int> class F, typename... Args>
@@ -834,8 +850,8 @@ hipError_t table_lora_add_device(hipStream_t st, int32_t dtype, int32_t r, void*
                                  const void* const* B_ptrs, const int32_t* seg_starts,
                                  const int32_t* perm, const int32_t* meta, int32_t n,
                                  int32_t S_max, int32_t h_in, int32_t h_out, float scale,
-                                 void* workspace, size_t workspace_bytes) {
-  const WsLayout L = ws_layout(n, h_in, r, workspace_bytes);
+                                 void* workspace) {
+  const WsLayout L = ws_layout(n, h_in, r);
   Tables TA{reinterpret_cast<const uint16_t* const*>(A_ptrs), seg_starts, perm, n, S_max, 1, n};
   Tables TB{reinterpret_cast<const uint16_t* const*>(B_ptrs), seg_starts, perm, n, S_max, 1, n};
   TA.meta = meta;
@@ -867,7 +883,7 @@ extern "C" int sgmv_shrink(hipStream_t stream, int32_t dtype, float* v, const vo
   if (!aligned16(x) || !aligned16(v)) return SGMV_ERR_ALIGNMENT;
   if (ranges_overlap(v, sizeof(float) * static_cast<size_t>(n) * r, x, matrix_bytes(n, ld_x, h_in)))
     return SGMV_ERR_ALIAS;
-  const WsLayout L = ws_layout(n, h_in, r, workspace_bytes);
+  const WsLayout L = ws_layout(n, h_in, r);
   if (!workspace || workspace_bytes < L.total ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return SGMV_ERR_WORKSPACE;
@@ -916,7 +932,7 @@ extern "C" int sgmv_lora_add(hipStream_t stream, int32_t dtype, void* y, int64_t
   if (!aligned16(x) || !aligned16(y)) return SGMV_ERR_ALIGNMENT;
   if (ranges_overlap(x, matrix_bytes(n, ld_x, h_in), y, matrix_bytes(n, ld_y, h_out)))
     return SGMV_ERR_ALIAS;
-  const WsLayout L = ws_layout(n, h_in, r, workspace_bytes);
+  const WsLayout L = ws_layout(n, h_in, r);
   if (!workspace || workspace_bytes < L.total ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return SGMV_ERR_WORKSPACE;
@@ -971,7 +987,7 @@ extern "C" int sgmv_lora_add_ranked(hipStream_t stream, int32_t dtype, void* y, 
                     G.max_seg_len};
     const Tables TB{B, seg_starts + G.starts0, perm + G.row0, G.n, G.n_segments, G.min_seg_len,
                     G.max_seg_len};
-    const WsLayout L = ws_layout(G.n, h_in, G.r, workspace_bytes);
+    const WsLayout L = ws_layout(G.n, h_in, G.r);
     const hipError_t e = dispatch<LoraOp>(dtype, G.r, stream, static_cast<uint16_t*>(y), ld_y,
                                           static_cast<const uint16_t*>(x), ld_x, TA, TB, h_in,
                                           h_out, G.scale, L, static_cast<char*>(workspace));

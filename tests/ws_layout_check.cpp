@@ -1,6 +1,7 @@
 // Host check of the workspace layout rule: in a buffer sized for the largest of a set of
-// shapes, no call of any smaller shape writes scratch over the counters or tagged partials
-// of any other such call, and every region stays inside the buffer.  Built and run by
+// shapes, no call of any smaller shape writes scratch over the tagged partials of any
+// other such call (the counters sit at a fixed place before all scratch), and every
+// region stays inside the buffer.  Built and run by
 // tests/test_host_abi.py; prints "ok" and exits 0 when the rule holds.
 #include <cstdio>
 #include <vector>
@@ -25,12 +26,10 @@ int main() {
             if (h > H) continue;
             for (int r : rs) {
               if (r > R) continue;
-              const WsLayout Li = ws_layout(n, h, r, W);
-              const size_t cnt = sizeof(int32_t) * kCounterInts * ((n + 15) / 16);
+              const WsLayout Li = ws_layout(n, h, r);
               const size_t pool = pool_offset(W, h, r);
-              if (Li.rowks_off < front_zero_end || Li.table_end > Li.tile_cnt_off ||
-                  Li.tile_cnt_off + cnt != pool || pool + pool_bytes(h, r) > W ||
-                  pool % 256 != 0 || Li.tile_cnt_off % 256 != 0) {
+              if (Li.rowks_off < front_zero_end || Li.table_end > pool ||
+                  pool + pool_bytes(h, r) > W || pool % 256 != 0) {
                 std::printf("bad layout: call (%d,%d,%d) in buffer for (%d,%d,%d)\n", n, h, r, N, H, R);
                 return 1;
               }
@@ -42,8 +41,8 @@ int main() {
                   for (int r2 : rs) {
                     if (r2 > R) continue;
                     ++checks;
-                    if (Li.table_end > ws_layout(n2, h2, r2, W).tile_cnt_off) {
-                      std::printf("overlap: scratch of (%d,%d,%d) reaches the counters of (%d,%d,%d) "
+                    if (Li.table_end > pool_offset(W, h2, r2)) {
+                      std::printf("overlap: scratch of (%d,%d,%d) reaches the tagged partials of (%d,%d,%d) "
                                   "in a buffer for (%d,%d,%d)\n", n, h, r, n2, h2, r2, N, H, R);
                       return 1;
                     }
