@@ -257,26 +257,28 @@ __device__ inline int next_run(const TileSegs<ROWS>& sh, int& q) {
 // XCD's L2 keeps one eighth of the K range of the adapters' A.
 constexpr int kXcds = 8;
 
-template <int R>
+template <int R, int RB_ = R / 16>
 struct ShrCfg {
   static constexpr int NB = R / 16;                 // column blocks of v
-  static constexpr int RB = R / 16;                 // row blocks
+  static constexpr int RB = RB_;                    // row blocks
   static constexpr int MT = 16 * RB;                // rows per tile
-  static constexpr int UN = (R == 16) ? 2 : 1;      // k steps per stage
+  static constexpr int UN = (R == 16 && RB == 1) ? 2 : 1;  // k steps per stage
   static constexpr int STAGE = 32 * UN;             // k per stage
   static constexpr int WAVES_PER_SIMD = (R == 64) ? 2 : 3;
-  static constexpr int TARGET_WGS = (R == 16) ? 256 : (R == 32 ? 384 : 512);
+  static constexpr int TARGET_WGS = (R == 16) ? (RB == 1 ? 256 : 512) : (R == 32 ? 384 : 512);
 };
 
+// r = 16: tiles of 16 rows, except for long rows of x (h_in > 16384), where 64-row tiles
+// read each k range of A once for four times as many rows (measured on MI355X: 70B down
+// projection 120 -> 93 us per call; 16-row tiles stay faster up to h_in = 13824)
+inline bool shrink_tall(int r, int32_t h_in) { return r == 16 && h_in > 16384; }
 // Loads of one stage.  They are unconditional (out-of-range k reads offset 0 of the same
 // row, rows outside the current run read a row that exists) so that the compiler can count
 // them exactly and keep the next stage in flight; shr_mul zeroes what does not belong.
-template <int DT, int R>
-__device__ inline void shr_load(const gptr<const uint16_t> (&xr)[ShrCfg<R>::RB],
-                                const gptr<const uint16_t> (&ar)[ShrCfg<R>::NB], int k0, int k_hi, int kq,
-                                uint4 (&xv)[ShrCfg<R>::UN][ShrCfg<R>::RB],
-                                uint4 (&av)[ShrCfg<R>::UN][ShrCfg<R>::NB]) {
-  using C = ShrCfg<R>;
+template <int DT, class C>
+__device__ inline void shr_load(const gptr<const uint16_t> (&xr)[C::RB],
+                                const gptr<const uint16_t> (&ar)[C::NB], int k0, int k_hi, int kq,
+                                uint4 (&xv)[C::UN][C::RB], uint4 (&av)[C::UN][C::NB]) {
 #pragma unroll
   for (int u = 0; u < C::UN; ++u) {
     const int kk = k0 + 32 * u + 8 * kq;
@@ -288,12 +290,10 @@ __device__ inline void shr_load(const gptr<const uint16_t> (&xr)[ShrCfg<R>::RB],
   }
 }
 
-template <int DT, int R>
-__device__ inline void shr_mul(const uint4 (&xv)[ShrCfg<R>::UN][ShrCfg<R>::RB],
-                               const uint4 (&av)[ShrCfg<R>::UN][ShrCfg<R>::NB], int k0, int k_hi,
-                               int kq, const bool (&xin)[ShrCfg<R>::RB],
-                               f32x4_t (&acc)[ShrCfg<R>::RB][ShrCfg<R>::NB]) {
-  using C = ShrCfg<R>;
+template <int DT, class C>
+__device__ inline void shr_mul(const uint4 (&xv)[C::UN][C::RB], const uint4 (&av)[C::UN][C::NB],
+                               int k0, int k_hi, int kq, const bool (&xin)[C::RB],
+                               f32x4_t (&acc)[C::RB][C::NB]) {
 #pragma unroll
   for (int u = 0; u < C::UN; ++u) {
     const bool in = k0 + 32 * u + 8 * kq < k_hi;
@@ -309,8 +309,8 @@ __device__ inline void shr_mul(const uint4 (&xv)[ShrCfg<R>::UN][ShrCfg<R>::RB],
   }
 }
 
-template <int DT, int R>
-__global__ __launch_bounds__(256, ShrCfg<R>::WAVES_PER_SIMD) void shrink_mfma_kernel(
+template <int DT, int R, int RB_>
+__global__ __launch_bounds__(256, (ShrCfg<R, RB_>::WAVES_PER_SIMD)) void shrink_mfma_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, const uint16_t* const* __restrict__ A_ptrs,
     const int32_t* __restrict__ seg_starts, int32_t S_host, const int32_t* __restrict__ perm,
     int32_t n, int32_t h_in, int32_t kcm, int32_t ks, float* __restrict__ part, int64_t slice,
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(256, ShrCfg<R>::WAVES_PER_SIMD) void shrink_mfma_ke
     const int32_t* __restrict__ meta) {
   const int S = meta ? meta[0] : S_host;
   if (meta && meta[2] < kLongMin) return;  // no long segment at all
-  using C = ShrCfg<R>;
+  using C = ShrCfg<R, RB_>;
   constexpr int NB = C::NB, RB = C::RB, UN = C::UN, STAGE = C::STAGE, MT = C::MT;
   __shared__ TileSegs<MT> sh;
   __shared__ int s_prow[MT];
@@ -366,12 +366,12 @@ __global__ __launch_bounds__(256, ShrCfg<R>::WAVES_PER_SIMD) void shrink_mfma_ke
     for (int nb = 0; nb < NB; ++nb) ar[nb] = A + static_cast<int64_t>(nb * 16 + mrow) * h_in;
     uint4 x0[UN][RB], a0[UN][NB], x1[UN][RB], a1[UN][NB];
     int k0 = k_lo + w * STAGE;
-    shr_load<DT, R>(xr, ar, k0, k_hi, kq, x0, a0);
+    shr_load<DT, C>(xr, ar, k0, k_hi, kq, x0, a0);
     for (int g = w; g < nst; g += 8) {
-      shr_load<DT, R>(xr, ar, k0 + 4 * STAGE, k_hi, kq, x1, a1);
-      shr_mul<DT, R>(x0, a0, k0, k_hi, kq, xin, acc);
-      shr_load<DT, R>(xr, ar, k0 + 8 * STAGE, k_hi, kq, x0, a0);
-      shr_mul<DT, R>(x1, a1, k0 + 4 * STAGE, k_hi, kq, xin, acc);
+      shr_load<DT, C>(xr, ar, k0 + 4 * STAGE, k_hi, kq, x1, a1);
+      shr_mul<DT, C>(x0, a0, k0, k_hi, kq, xin, acc);
+      shr_load<DT, C>(xr, ar, k0 + 8 * STAGE, k_hi, kq, x0, a0);
+      shr_mul<DT, C>(x1, a1, k0 + 4 * STAGE, k_hi, kq, xin, acc);
       k0 += 8 * STAGE;
     }
   }
@@ -671,10 +671,10 @@ static_assert(GemvCfg<16>::KC == 512 && GemvCfg<32>::KC == 256 && GemvCfg<64>::K
 // sweeps on MI355X: fewer, longer chunks win for r = 16, more for r = 64), chunks of at
 // least 256 k, a multiple of 8 chunks where there are 8 or more (XCD-owned chunks), and
 // no more slices than the workspace holds
-template <int R>
+template <class C>
 inline void mfma_split(int32_t n, int32_t h_in, int ks_cap, int* kcm, int* ks) {
-  const int tiles = (n + ShrCfg<R>::MT - 1) / ShrCfg<R>::MT;
-  const int target = ShrCfg<R>::TARGET_WGS;
+  const int tiles = (n + C::MT - 1) / C::MT;
+  const int target = C::TARGET_WGS;
   int k = (target + tiles - 1) / tiles;
   k = min(k, max(1, h_in / 256));
   k = max(1, min(k, ks_cap));
@@ -699,6 +699,21 @@ struct Tables {
   unsigned gemv_grid() const { return static_cast<unsigned>(meta ? (S < 256 ? S : 256) : S); }
 };
 
+template <int DT, int R, int RB>
+hipError_t launch_shrink_mfma(hipStream_t st, const uint16_t* x, int64_t ld_x, const Tables& T,
+                              int32_t h_in, const WsLayout& L, float* part, float* v_long,
+                              int32_t* rowks, int* ks_long) {
+  using C = ShrCfg<R, RB>;
+  int kcm, ks;
+  mfma_split<C>(T.n, h_in, L.ks_max, &kcm, &ks);
+  const int tiles = (T.n + C::MT - 1) / C::MT;
+  hipLaunchKernelGGL((shrink_mfma_kernel<DT, R, RB>), dim3(tiles * ks), dim3(256), 0, st, x, ld_x,
+                     T.ptrs, T.seg_starts, T.S, T.perm, T.n, h_in, kcm, ks, part, L.slice,
+                     v_long, rowks, T.meta);
+  *ks_long = ks;
+  return hipGetLastError();
+}
+
 // shrink kernels: short segments leave split-K slices (ks_gemv of them, counted in rowks);
 // long segments leave their final v in v_long (ks_long == 1) or ks_long slices, counted in
 // rowks, for reduce_v_kernel
@@ -717,13 +732,11 @@ hipError_t launch_shrink(hipStream_t st, const uint16_t* x, int64_t ld_x, const 
                        ld_x, T.ptrs, T.seg_starts, T.perm, h_in, part, L.slice, rowks, ks, T.meta);
   }
   if (T.use_long()) {
-    int kcm, ks;
-    mfma_split<R>(T.n, h_in, L.ks_max, &kcm, &ks);
-    const int tiles = (T.n + ShrCfg<R>::MT - 1) / ShrCfg<R>::MT;
-    hipLaunchKernelGGL((shrink_mfma_kernel<DT, R>), dim3(tiles * ks), dim3(256), 0, st, x, ld_x,
-                       T.ptrs, T.seg_starts, T.S, T.perm, T.n, h_in, kcm, ks, part, L.slice,
-                       v_long, rowks, T.meta);
-    *ks_long = ks;
+    if constexpr (R == 16) {
+      if (shrink_tall(R, h_in))
+        return launch_shrink_mfma<DT, R, 4>(st, x, ld_x, T, h_in, L, part, v_long, rowks, ks_long);
+    }
+    return launch_shrink_mfma<DT, R, R / 16>(st, x, ld_x, T, h_in, L, part, v_long, rowks, ks_long);
   }
   return hipGetLastError();
 }

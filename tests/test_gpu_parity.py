@@ -103,6 +103,7 @@ EXACT_CASES = [
     ("r64_mixed", 90, 1024, 776, 64, 5, "mixed"),
     ("r64_decode", 12, 8192, 1024, 64, 12, "perm"),
     ("deep_k", 40, 28672, 264, 16, 3, "mixed"),
+    ("deep_k_long", 150, 20480, 264, 16, 3, "mixed"),  # r = 16 with 64-row shrink tiles
 ]
 
 
@@ -168,6 +169,7 @@ RAGGED = [
     (2048, 264, 264, 16, 1, "blocks", 0, True),     # one very long segment
     (300, 1032, 1160, 32, 3, "mixed", 8, False),    # r = 32 tiles, ragged last strip
     (129, 2056, 200, 64, 2, "blocks", 0, False),    # r = 64 tiles, narrow h_out
+    (130, 16392, 1032, 16, 3, "mixed", 8, False),   # r = 16, 64-row shrink tiles, ragged
 ]
 
 
