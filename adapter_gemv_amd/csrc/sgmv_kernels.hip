@@ -182,39 +182,38 @@ __global__ __launch_bounds__(64) void expand_gemv_kernel(
 // ------------------------------------------------------------------------------------
 // long-segment path (segments with >= kLongMin rows)
 // ------------------------------------------------------------------------------------
-__device__ inline void store_coherent(float* q, float v) {
-  __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline float load_coherent(const float* q) {
-  return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Long segments overlapping the sorted rows [g0, g1) of a tile (at most ROWS rows), found
-// in one parallel pass over seg_starts: sh.rseg[q] = segment of row g0 + q if that segment
-// has at least kLongMin rows, else -1.  Returns the number of such segments (uniform).
-// A tile of ROWS rows meets at most ROWS / kLongMin + 2 long segments.
+// in one parallel pass over seg_starts that also reads each segment's weight pointer (so
+// that the pointer needs no load of its own once the segment is known): sh.seg[k],
+// sh.ptr[k] for the tile's long segments k, and sh.rseg[q] = k for row g0 + q if its
+// segment has at least kLongMin rows, else -1.  Returns the number of such segments
+// (uniform).  A tile of ROWS rows meets at most ROWS / kLongMin + 2 long segments.
 template <int ROWS>
 struct TileSegs {
   static constexpr int kMax = ROWS / kLongMin + 2;
   int nseg;
   int seg[kMax], st[kMax], en[kMax];
+  const uint16_t* ptr[kMax];
   int rseg[ROWS];
 };
 
 template <int ROWS, int THREADS>
-__device__ inline int tile_long_segments(const int32_t* __restrict__ seg_starts, int S, int g0,
+__device__ inline int tile_long_segments(const int32_t* __restrict__ seg_starts,
+                                         const uint16_t* const* __restrict__ ptrs, int S, int g0,
                                          int g1, TileSegs<ROWS>& sh) {
   const int tid = threadIdx.x;
   if (tid == 0) sh.nseg = 0;
   __syncthreads();
   for (int s = tid; s < S; s += THREADS) {
     const int st = seg_starts[s], en = seg_starts[s + 1];
+    const uint16_t* const pp = ptrs[s];
     if (en - st >= kLongMin && st < g1 && en > g0) {
       const int k = atomicAdd(&sh.nseg, 1);
       if (k < TileSegs<ROWS>::kMax) {
         sh.seg[k] = s;
         sh.st[k] = st;
         sh.en[k] = en;
+        sh.ptr[k] = pp;
       }
     }
   }
@@ -222,24 +221,24 @@ __device__ inline int tile_long_segments(const int32_t* __restrict__ seg_starts,
   const int nseg = min(sh.nseg, TileSegs<ROWS>::kMax);
   for (int q = tid; q < ROWS; q += THREADS) {
     const int row = g0 + q;
-    int sg = -1;
+    int slot = -1;
     for (int k = 0; k < nseg; ++k)
-      if (sh.st[k] <= row && row < sh.en[k]) sg = sh.seg[k];
-    sh.rseg[q] = sg;
+      if (sh.st[k] <= row && row < sh.en[k]) slot = k;
+    sh.rseg[q] = slot;
   }
   __syncthreads();
   return nseg;
 }
 
-// Next long segment of a tile at or after row q (rows are in segment order); returns -1
-// when there is none and leaves q after the segment's last row in the tile.
+// Next long run of a tile at or after row q (rows are in segment order): its slot k in
+// TileSegs, or -1 when there is none; leaves q after the run's last row in the tile.
 template <int ROWS>
 __device__ inline int next_run(const TileSegs<ROWS>& sh, int& q) {
   while (q < ROWS && sh.rseg[q] < 0) ++q;
   if (q >= ROWS) return -1;
-  const int sg = sh.rseg[q];
-  while (q < ROWS && sh.rseg[q] == sg) ++q;
-  return sg;
+  const int k = sh.rseg[q];
+  while (q < ROWS && sh.rseg[q] == k) ++q;
+  return k;
 }
 
 // Shrink on MFMA 16x16x32 for a tile of r sorted rows and one K chunk.  The x rows are
@@ -340,7 +339,7 @@ __global__ __launch_bounds__(256, (ShrCfg<R, RB_>::WAVES_PER_SIMD)) void shrink_
   const int lane = tid & 63, w = tid >> 6;
   const int mrow = lane & 15, kq = lane >> 4;
   if (tid < MT) s_prow[tid] = (r0 + tid < r1) ? (perm ? perm[r0 + tid] : r0 + tid) : 0;
-  if (tile_long_segments<MT, 256>(seg_starts, S, r0, r1, sh) == 0) return;  // uniform
+  if (tile_long_segments<MT, 256>(seg_starts, A_ptrs, S, r0, r1, sh) == 0) return;  // uniform
   const int k_lo = kc * kcm;
   const int k_hi = min(h_in, k_lo + kcm);
   const int nst = (k_hi - k_lo + STAGE - 1) / STAGE;
@@ -360,7 +359,7 @@ __global__ __launch_bounds__(256, (ShrCfg<R, RB_>::WAVES_PER_SIMD)) void shrink_
       xin[rb] = sh.rseg[16 * rb + mrow] == sg;
       xr[rb] = global_ptr(x) + static_cast<int64_t>(s_prow[xin[rb] ? 16 * rb + mrow : 0]) * ld_x;
     }
-    const gptr<const uint16_t> A = global_ptr(A_ptrs[sg]);
+    const gptr<const uint16_t> A = global_ptr(sh.ptr[sg]);
     gptr<const uint16_t> ar[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) ar[nb] = A + static_cast<int64_t>(nb * 16 + mrow) * h_in;
@@ -533,16 +532,16 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
       for (int k = 1; k < VS; ++k) vv[u] += t[k][u];  // slices past vks add exact zeros
     }
   }
-  if (tile_long_segments<TR, 256>(seg_starts, S, g0, g1, sh) == 0) return;  // uniform
+  if (tile_long_segments<TR, 256>(seg_starts, B_ptrs, S, g0, g1, sh) == 0) return;  // uniform
 
-  // B of the tile's first long run goes out now, so that its latency (a dependent pointer
-  // load, then the B rows) overlaps the wait for v.  B row c holds the r values of column
+  // B of the tile's first long run goes out now, so that its latency overlaps the wait
+  // for v.  B row c holds the r values of column
   // c; the product's k runs over the hi halves, then the lo halves, so the k-steps past r
   // reuse the same B bytes: only NKU = r / 32 distinct loads per column block.
   int q = 0;
   int sg = next_run(sh, q);  // the tile meets a long segment, so there is a first run
   uint4 bop[CB][NKU];
-  exp_load_b<R, CB, NKU>(global_ptr(B_ptrs[sg]), wc, l16, kq, h_out, bop);
+  exp_load_b<R, CB, NKU>(global_ptr(sh.ptr[sg]), wc, l16, kq, h_out, bop);
 
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
@@ -587,7 +586,7 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
         for (int s = 0; s < NK; ++s) acc[rb][cb] = E::mfma(bop[cb][s % NKU], vop[s], acc[rb][cb]);
     }
     if ((sg = next_run(sh, q)) < 0) break;
-    exp_load_b<R, CB, NKU>(global_ptr(B_ptrs[sg]), wc, l16, kq, h_out, bop);
+    exp_load_b<R, CB, NKU>(global_ptr(sh.ptr[sg]), wc, l16, kq, h_out, bop);
   }
   __syncthreads();  // every wave is done reading vlds before dl overwrites it
   // lane: D rows 4*kq .. +3 of column block cb = tile columns (TC/4)w + 16cb + 4kq .. +3,
