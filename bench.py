@@ -739,7 +739,7 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; multi-GPU runs are not supported "
+        print("bench.py: measures one GPU only; multi-GPU runs are not supported "
               "(--gpus 1)", file=sys.stderr)
         return 2
 
