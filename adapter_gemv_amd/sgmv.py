@@ -158,6 +158,8 @@ class Batch:
     table: SegmentTable
     n_adapters: int
     rank: int
+    h_in: int
+    h_out: int
     dev: object
     A_ptrs_addr: int
     B_ptrs_addr: int
@@ -177,8 +179,13 @@ class Batch:
         torch = _torch()
         if isinstance(A_pool, (list, tuple)):
             n_adapters, rank = len(A_pool), int(A_pool[0].shape[0])
+            h_in, h_out = int(A_pool[0].shape[1]), int(B_pool[0].shape[0])
+            As, Bs = list(A_pool), list(B_pool)
         else:
             n_adapters, rank = int(A_pool.shape[0]), int(A_pool.shape[1])
+            h_in, h_out = int(A_pool.shape[2]), int(B_pool.shape[1])
+            As, Bs = [A_pool[0]], [B_pool[0]]
+        _check_adapters(As, Bs, rank, h_in, h_out, n_adapters, len(B_pool))
         tab = sgmv_build_segments(adapter_ids, n_adapters)
         if identity_perm and not np.array_equal(tab.perm, np.arange(tab.n, dtype=np.int32)):
             raise ValueError("identity_perm requires adapter_ids to be sorted")
@@ -193,7 +200,7 @@ class Batch:
         off_b = 8 * S
         off_s = 16 * S
         off_p = off_s + 4 * (S + 1)
-        return cls(tab, n_adapters, rank, dev, base, base + off_b, base + off_s,
+        return cls(tab, n_adapters, rank, h_in, h_out, dev, base, base + off_b, base + off_s,
                    0 if identity_perm else base + off_p)
 
     @staticmethod
@@ -206,6 +213,25 @@ class Batch:
         buf[16 * S: 16 * S + 4 * (S + 1)] = tab.seg_starts.view(np.uint8)
         buf[16 * S + 4 * (S + 1): nbytes] = tab.perm.view(np.uint8)
         return buf
+
+
+def _check_adapters(As, Bs, r: int, h_in: int, h_out: int, n_a: int, n_b: int):
+    """Every adapter's A is a dense [r, h_in] and B a dense [h_out, r] array (the kernels
+    read them with these strides)."""
+    if n_a != n_b:
+        raise ValueError("A and B pools hold different numbers of adapters")
+    for A, B in zip(As, Bs):
+        if tuple(A.shape[-2:]) != (r, h_in) or tuple(B.shape[-2:]) != (h_out, r):
+            raise ValueError(f"adapter shapes {tuple(A.shape)} / {tuple(B.shape)} do not match "
+                             f"A [{r}, {h_in}] and B [{h_out}, {r}]")
+        if A.stride(-1) != 1 or A.stride(-2) != h_in or B.stride(-1) != 1 or B.stride(-2) != r:
+            raise ValueError("each adapter's A and B must be dense row-major arrays")
+
+
+def _check_io(x, y, h_in: int, h_out: int):
+    if x.shape[1] != h_in or y.shape[1] != h_out:
+        raise ValueError(f"x [n, {x.shape[1]}] / y [n, {y.shape[1]}] do not match the adapters' "
+                         f"h_in = {h_in}, h_out = {h_out}")
 
 
 def make_workspace(n: int, h_in: int, r: int, device):
@@ -231,6 +257,7 @@ def lora_add(y, x, batch: Batch, scale: float, workspace=None, stream=None):
     _check_rows(y, n, "y")
     if x.dtype != y.dtype:
         raise TypeError("x and y must share a dtype")
+    _check_io(x, y, batch.h_in, batch.h_out)
     r = _infer_rank(batch)
     if workspace is None:
         workspace = make_workspace(n, x.shape[1], r, x.device)
@@ -249,6 +276,8 @@ def shrink(x, batch: Batch, r: Optional[int] = None, workspace=None, stream=None
     torch = _torch()
     n = batch.n
     _check_rows(x, n, "x")
+    if x.shape[1] != batch.h_in:
+        raise ValueError(f"x [n, {x.shape[1]}] does not match the adapters' h_in = {batch.h_in}")
     r = r or _infer_rank(batch)
     v = torch.empty((n, r), dtype=torch.float32, device=x.device)
     if workspace is None:
@@ -266,6 +295,8 @@ def expand(y, v, batch: Batch, scale: float, stream=None):
     """y[perm[i]] += scale * v[i] @ B[segment of i] in place."""
     n = batch.n
     _check_rows(y, n, "y")
+    if y.shape[1] != batch.h_out or tuple(v.shape) != (n, batch.rank):
+        raise ValueError("y or v does not match the batch's h_out and rank")
     t = batch.table
     st = sgmv_expand(_stream_handle(stream), dtype_code(y), y.data_ptr(), y.stride(0),
                      v.data_ptr(), batch.B_ptrs_addr, batch.seg_starts_addr,
@@ -329,6 +360,8 @@ class RankedBatch:
     """Segment metadata of a mixed-rank batch on the device.  Adapter ids index the
     concatenation of the pools: pool k holds ids offset_k .. offset_k + P_k - 1."""
     table: RankedTable
+    h_in: int
+    h_out: int
     dev: object
     A_ptrs_addr: int
     B_ptrs_addr: int
@@ -348,6 +381,10 @@ class RankedBatch:
         """``pools`` is a list of (A_pool [P_k, r_k, h_in], B_pool [P_k, h_out, r_k]) device
         tensors."""
         torch = _torch()
+        h_in, h_out = int(pools[0][0].shape[2]), int(pools[0][1].shape[1])
+        for A, B in pools:
+            _check_adapters([A[0]], [B[0]], int(A.shape[1]), h_in, h_out, int(A.shape[0]),
+                            int(B.shape[0]))
         rank = np.concatenate([np.full(int(A.shape[0]), int(A.shape[1]), np.int32)
                                for A, _ in pools])
         tab = sgmv_build_segments_ranked(adapter_ids, rank)
@@ -365,7 +402,8 @@ class RankedBatch:
         buf[16 * S + 4 * ns: nbytes] = tab.perm.view(np.uint8)
         dev = torch.from_numpy(buf).to(pools[0][0].device)
         base = int(dev.data_ptr())
-        return cls(tab, dev, base, base + 8 * S, base + 16 * S, base + 16 * S + 4 * ns)
+        return cls(tab, h_in, h_out, dev, base, base + 8 * S, base + 16 * S,
+                   base + 16 * S + 4 * ns)
 
 
 def lora_add_ranked(y, x, batch: RankedBatch, scales, workspace=None, stream=None):
@@ -376,6 +414,7 @@ def lora_add_ranked(y, x, batch: RankedBatch, scales, workspace=None, stream=Non
     _check_rows(y, n, "y")
     if x.dtype != y.dtype:
         raise TypeError("x and y must share a dtype")
+    _check_io(x, y, batch.h_in, batch.h_out)
     gs = batch.table.groups
     arr = (_lib.RankGroup * max(len(gs), 1))()
     for i, g in enumerate(gs):
@@ -441,10 +480,10 @@ def lora_add_pool(y, x, ids, A_pool, B_pool, scale: float, workspace=None, strea
     _check_rows(x, n, "x")
     _check_rows(y, n, "y")
     r = int(A_pool.shape[1])
-    if A_pool.stride(1) != A_pool.shape[2] or A_pool.stride(2) != 1:
-        raise ValueError("each A_pool[a] must be a dense [r, h_in] array")
-    if B_pool.stride(1) != B_pool.shape[2] or B_pool.stride(2) != 1:
-        raise ValueError("each B_pool[a] must be a dense [h_out, r] array")
+    _check_adapters([A_pool[0]], [B_pool[0]], r, int(x.shape[1]), int(y.shape[1]),
+                    int(A_pool.shape[0]), int(B_pool.shape[0]))
+    if ids.dtype != _torch().int32 or ids.dim() != 1 or int(ids.shape[0]) != n:
+        raise ValueError("ids must be a device int32 tensor [n]")
     if workspace is None:
         workspace = make_workspace(n, x.shape[1], r, x.device)
     st = sgmv_lora_add_pool(_stream_handle(stream), dtype_code(y), y.data_ptr(), y.stride(0),

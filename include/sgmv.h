@@ -156,10 +156,10 @@ int sgmv_build_ptr_table(const uint64_t* adapter_base, int32_t n_adapters,
                          const int32_t* seg_adapter, int32_t n_segments, uint64_t* seg_ptrs);
 
 /*
- * Bytes of device workspace that sgmv_shrink, sgmv_lora_add and sgmv_lora_add_pool need
- * for calls of up to n rows, h_in and rank r: float32 split-K partial sums, a few
- * counters, and the decode path's tagged partial sums, which sit at the end of the
- * buffer.  The workspace must be 256-byte aligned and zero-filled once before its first
+ * Bytes of device workspace that sgmv_shrink, sgmv_lora_add, sgmv_lora_add_ranked and
+ * sgmv_lora_add_pool need for calls of up to n rows, h_in and rank r: float32 split-K
+ * partial sums, device-built segment tables, a few counters, and the decode path's
+ * tagged partial sums, which sit at the end of the buffer.  The workspace must be 256-byte aligned and zero-filled once before its first
  * use; every call leaves it ready for the next one.  One workspace may serve any mix of
  * calls (either path, any shapes) if it is sized with the largest n, h_in and r among
  * them and the calls are stream-ordered.  Returns 0 for invalid sizes.
@@ -210,7 +210,8 @@ int sgmv_lora_add(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
  *   n               rows of the batch (x and y have n rows; perm entries are < n)
  *   workspace       at least sgmv_workspace_bytes(n, h_in, largest r of the groups)
  * Every group is checked before anything is launched.  Rows that belong to no group are
- * left unchanged.  Returns SGMV_ERR_SHAPE if a group's rows or segment bounds do not fit.
+ * left unchanged; x and y must not overlap.  Returns SGMV_ERR_SHAPE if a group's rows or
+ * segment bounds do not fit, SGMV_ERR_UNSUPPORTED for a group rank outside {16, 32, 64}.
  */
 int sgmv_lora_add_ranked(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
                          const void* x, int64_t ld_x, const void* const* A_ptrs,

@@ -329,3 +329,26 @@ def test_lora_add_ranked_rejects(name, gs, kw, code):
 def test_lora_add_ranked_empty_is_ok():
     assert _ranked([], n_groups=0, x=None, y=None) == _lib.OK
     assert _ranked([G16[:2] + (0, 0, 0, 0, 0, 0, 1.0)], n=0) == _lib.OK
+
+
+def test_binding_rejects_mismatched_adapters():
+    """The binding checks adapter shapes against x and y before anything reaches the GPU
+    (the kernels read A and B with strides taken from h_in and h_out)."""
+    import torch
+    x = torch.zeros((4, 64), dtype=torch.bfloat16)
+    y = torch.zeros((4, 32), dtype=torch.bfloat16)
+    ids = torch.zeros(4, dtype=torch.int32)
+    A = torch.zeros((3, 16, 64), dtype=torch.bfloat16)
+    B = torch.zeros((3, 32, 16), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):   # h_in of A differs from x
+        sgmv.lora_add_pool(y, x, ids, torch.zeros((3, 16, 72), dtype=torch.bfloat16), B, 1.0)
+    with pytest.raises(ValueError):   # h_out of B differs from y
+        sgmv.lora_add_pool(y, x, ids, A, torch.zeros((3, 40, 16), dtype=torch.bfloat16), 1.0)
+    with pytest.raises(ValueError):   # rank of B differs from A
+        sgmv.lora_add_pool(y, x, ids, A, torch.zeros((3, 32, 32), dtype=torch.bfloat16), 1.0)
+    with pytest.raises(ValueError):   # A not dense
+        sgmv.lora_add_pool(y, x, ids, torch.zeros((3, 64, 16), dtype=torch.bfloat16).transpose(1, 2), B, 1.0)
+    with pytest.raises(ValueError):   # pools of different sizes
+        sgmv.lora_add_pool(y, x, ids, A, B[:2], 1.0)
+    with pytest.raises(ValueError):   # ids of the wrong type
+        sgmv.lora_add_pool(y, x, ids.long(), A, B, 1.0)
