@@ -304,6 +304,159 @@ __global__ __launch_bounds__(kTabThreads) void tables_kernel(const int32_t* __re
   }
 }
 
+// Grouping for the fused call (sgmv_lora_add_pool, 64 < n <= 4096), one workgroup: rows
+// of one adapter are made contiguous, which is all the paper summary's idea I2 needs; the
+// order of the groups and of the rows inside a group is not the sorted one (the results
+// do not depend on it: every row's sums are formed alone, in a fixed order).  Each id goes
+// into an LDS hash table of 2 * kDevSortMax slots (open addressing), which counts its rows;
+// a scan over the slots gives every group its first row and its segment number, and each
+// row then takes the next free position of its group.  Writes the same tables as the
+// sort (perm, seg_starts, seg_adapter, pointer tables, meta, n_segments, flag).
+constexpr int kGroupThreads = 1024;
+constexpr int kGroupSlots = 2 * kDevSortMax;
+constexpr int kGroupPer = kDevSortMax / kGroupThreads;     // rows per thread
+constexpr int kSlotsPer = kGroupSlots / kGroupThreads;     // slots per thread
+static_assert(kGroupSlots == 1 << 13, "the slot hash keeps 13 bits");
+
+__global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __restrict__ ids,
+                                                              int32_t n, int32_t n_adapters,
+                                                              SortOut o) {
+  constexpr int T = kGroupThreads, W = T / 64;
+  __shared__ int key[kGroupSlots];  // adapter id of the slot, -1 = empty
+  __shared__ int cnt[kGroupSlots];  // rows of the slot, then its next free position
+  __shared__ int wrows[W], wsegs[W];
+  __shared__ int s_bad, s_min, s_max, s_rows, s_segs;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+#pragma unroll
+  for (int u = 0; u < kSlotsPer; ++u) {
+    key[tid + T * u] = -1;
+    cnt[tid + T * u] = 0;
+  }
+  if (tid == 0) {
+    s_bad = 0;
+    s_min = 0x7fffffff;
+    s_max = 0;
+  }
+  __syncthreads();
+  // insert: thread t takes rows t, t + T, ...  Consecutive lanes with the same id (a
+  // request's rows) form a run whose first lane does the table work for the whole run, so
+  // that a batch of few adapters does not serialise on a few LDS addresses.
+  int slot[kGroupPer], rank[kGroupPer], head_lane[kGroupPer], run_len[kGroupPer];
+#pragma unroll
+  for (int u = 0; u < kGroupPer; ++u) {
+    const int i = tid + T * u;
+    int id = (i < n) ? ids[i] : -1;
+    if (i < n && (id < 0 || id >= n_adapters)) {
+      s_bad = 1;
+      id = -1;
+    }
+    const bool valid = id >= 0;
+    const int prev = __shfl_up(id, 1);
+    const bool head = valid && (lane == 0 || prev != id);
+    const uint64_t heads = __ballot(head);
+    const uint64_t bounds = heads | __ballot(!valid);
+    const uint64_t upto = (lane == 63) ? ~0ull : ((2ull << lane) - 1);
+    const uint64_t below = heads & upto;
+    const int hl = below ? 63 - __clzll(below) : lane;
+    const uint64_t above = bounds & ~upto;
+    const int len = (above ? __ffsll(static_cast<long long>(above)) - 1 : 64) - lane;
+    int h = -1;
+    if (head) {
+      h = static_cast<int>((static_cast<uint32_t>(id) * 2654435761u) >> 19);  // 13 bits
+      for (int probe = 0; probe < kGroupSlots; ++probe) {
+        const int old = atomicCAS(&key[h], -1, id);
+        if (old == -1 || old == id) break;
+        h = (h + 1) & (kGroupSlots - 1);
+      }
+      atomicAdd(&cnt[h], len);
+    }
+    const int hs = __shfl(h, hl);
+    slot[u] = valid ? hs : -1;
+    rank[u] = lane - hl;
+    head_lane[u] = hl;
+    run_len[u] = head ? len : 0;
+  }
+  __syncthreads();
+  // scan over the slots: thread t owns slots kSlotsPer*t .. +kSlotsPer-1
+  int rows = 0, segs = 0;
+#pragma unroll
+  for (int u = 0; u < kSlotsPer; ++u) {
+    const int c = cnt[kSlotsPer * tid + u];
+    rows += c;
+    segs += (c > 0);
+  }
+  int ir = rows, is = segs;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int ur = __shfl_up(ir, d), us = __shfl_up(is, d);
+    if (lane >= d) {
+      ir += ur;
+      is += us;
+    }
+  }
+  if (lane == 63) {
+    wrows[wv] = ir;
+    wsegs[wv] = is;
+  }
+  __syncthreads();
+  int row0 = ir - rows, seg0 = is - segs;
+  for (int q = 0; q < wv; ++q) {
+    row0 += wrows[q];
+    seg0 += wsegs[q];
+  }
+  if (tid == T - 1) {
+    s_rows = row0 + rows;
+    s_segs = seg0 + segs;
+  }
+  int mn = 0x7fffffff, mx = 0;
+#pragma unroll
+  for (int u = 0; u < kSlotsPer; ++u) {
+    const int sl = kSlotsPer * tid + u;
+    const int c = cnt[sl];
+    if (c > 0) {
+      const int a = key[sl];
+      o.seg_starts[seg0] = row0;
+      o.seg_adapter[seg0] = a;
+      if (o.A_ptrs) {
+        o.A_ptrs[seg0] = o.A_pool + static_cast<int64_t>(a) * o.A_stride;
+        o.B_ptrs[seg0] = o.B_pool + static_cast<int64_t>(a) * o.B_stride;
+      }
+      mn = min(mn, c);
+      mx = max(mx, c);
+      cnt[sl] = row0;  // from now on: the group's next free position
+      row0 += c;
+      ++seg0;
+    }
+  }
+  if (mx > 0) {
+    atomicMin(&s_min, mn);
+    atomicMax(&s_max, mx);
+  }
+  __syncthreads();
+  // every run takes the next positions of its group, in row order inside the run
+#pragma unroll
+  for (int u = 0; u < kGroupPer; ++u) {
+    int base = 0;
+    if (run_len[u] > 0) base = atomicAdd(&cnt[slot[u]], run_len[u]);
+    base = __shfl(base, head_lane[u]);
+    if (slot[u] >= 0) o.perm[base + rank[u]] = tid + T * u;
+  }
+  const int n_valid = s_rows, S = s_segs;
+  for (int p = n_valid + tid; p < n; p += T) o.perm[p] = -1;
+  if (tid == 0) {
+    o.seg_starts[S] = n_valid;
+    o.n_segments[0] = s_bad ? -1 : S;
+    if (o.meta) {
+      o.meta[0] = S;
+      o.meta[1] = S ? s_min : 0;
+      o.meta[2] = s_max;
+      o.meta[3] = n_valid;
+    }
+    if (s_bad && o.ws_flag)
+      __hip_atomic_store(o.ws_flag, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 inline hipError_t launch_device_sort(hipStream_t st, const int32_t* ids, int32_t n,
                                      int32_t n_adapters, const SortOut& o) {
   hipLaunchKernelGGL(rank_kernel, dim3((n + kRankRows - 1) / kRankRows), dim3(kRankThreads), 0, st,
@@ -612,7 +765,7 @@ extern "C" int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, in
   if ((st = check_device())) return st;
 
   if (n > kPoolMaxN) {
-    // device sort into the workspace, then the table path on those tables
+    // device grouping into the workspace, then the table path on those tables
     char* wsb = static_cast<char*>(workspace);
     const WsLayout L = ws_layout(n, h_in, r);
     const DevTabLayout D = dev_tab_layout(n);
@@ -631,7 +784,9 @@ extern "C" int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, in
     o.B_stride = B_stride;
     o.ws_flag = reinterpret_cast<int32_t*>(wsb);
     o.sorted_ids = reinterpret_cast<int32_t*>(dt + D.sorted_ids);
-    hipError_t e = launch_device_sort(stream, adapter_ids, n, n_adapters, o);
+    hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupThreads), 0, stream, adapter_ids, n,
+                       n_adapters, o);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_status(e);
     const int32_t S_max = n < n_adapters ? n : n_adapters;
     return hip_status(table_lora_add_device(

@@ -244,9 +244,11 @@ int sgmv_build_segments_device(hipStream_t stream, const int32_t* adapter_ids, i
  * y[t] += scale * (x[t] @ A[a_t]) @ B[a_t], with no host work that depends on the ids
  * (the call can be captured in a HIP graph and replayed with new ids):
  *   n <= 64:        one kernel launch: segment metadata, shrink and expand (decode);
- *   64 < n <= 4096: the device sort of sgmv_build_segments_device writes the segment
- *                   tables and pointer tables into the workspace, then the kernels of
- *                   sgmv_lora_add run on them (prefill and mixed batches).
+ *   64 < n <= 4096: one workgroup groups the rows by adapter (a hash table in LDS; the
+ *                   groups are contiguous but, unlike sgmv_build_segments_device, not in
+ *                   id order) and writes the segment and pointer tables into the
+ *                   workspace, then the kernels of sgmv_lora_add run on them (prefill and
+ *                   mixed batches).
  *   adapter_ids  device int32[n]: adapter of caller row t (device memory, so a HIP
  *                graph can capture the call and replay it with new ids)
  *   A_pool       device: adapter a's A ([r, h_in] row-major) starts at
