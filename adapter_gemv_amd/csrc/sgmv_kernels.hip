@@ -197,16 +197,47 @@ struct TileSegs {
   int rseg[ROWS];
 };
 
-template <int ROWS, int THREADS>
-__device__ inline int tile_long_segments(const int32_t* __restrict__ seg_starts,
+// Segment s = threadIdx.x's bounds and weight pointer, read ahead of the scan so that they
+// share a round of loads with the caller rows (sh.nseg must be cleared before the caller's
+// barrier; see tile_long_segments_pre).
+struct SegPre {
+  int st, en;
+  const uint16_t* ptr;
+};
+
+__device__ inline SegPre seg_preload(const int32_t* __restrict__ seg_starts,
+                                     const uint16_t* const* __restrict__ ptrs, int S) {
+  SegPre p{0, 0, nullptr};
+  const int s = threadIdx.x;
+  if (s < S) {
+    p.st = seg_starts[s];
+    p.en = seg_starts[s + 1];
+    p.ptr = ptrs[s];
+  }
+  return p;
+}
+
+template <int ROWS, int THREADS, bool PRE>
+__device__ inline int tile_segments_impl(const int32_t* __restrict__ seg_starts,
                                          const uint16_t* const* __restrict__ ptrs, int S, int g0,
-                                         int g1, TileSegs<ROWS>& sh) {
+                                         int g1, TileSegs<ROWS>& sh, const SegPre& pre) {
   const int tid = threadIdx.x;
-  if (tid == 0) sh.nseg = 0;
-  __syncthreads();
+  if constexpr (!PRE) {
+    if (tid == 0) sh.nseg = 0;
+    __syncthreads();
+  }
   for (int s = tid; s < S; s += THREADS) {
-    const int st = seg_starts[s], en = seg_starts[s + 1];
-    const uint16_t* const pp = ptrs[s];
+    int st, en;
+    const uint16_t* pp;
+    if (PRE && s == tid) {
+      st = pre.st;
+      en = pre.en;
+      pp = pre.ptr;
+    } else {
+      st = seg_starts[s];
+      en = seg_starts[s + 1];
+      pp = ptrs[s];
+    }
     if (en - st >= kLongMin && st < g1 && en > g0) {
       const int k = atomicAdd(&sh.nseg, 1);
       if (k < TileSegs<ROWS>::kMax) {
@@ -228,6 +259,23 @@ __device__ inline int tile_long_segments(const int32_t* __restrict__ seg_starts,
   }
   __syncthreads();
   return nseg;
+}
+
+template <int ROWS, int THREADS>
+__device__ inline int tile_long_segments(const int32_t* __restrict__ seg_starts,
+                                         const uint16_t* const* __restrict__ ptrs, int S, int g0,
+                                         int g1, TileSegs<ROWS>& sh) {
+  return tile_segments_impl<ROWS, THREADS, false>(seg_starts, ptrs, S, g0, g1, sh, SegPre{});
+}
+
+// As tile_long_segments, with segment threadIdx.x already read by seg_preload and sh.nseg
+// cleared before a barrier that all threads have passed.
+template <int ROWS, int THREADS>
+__device__ inline int tile_long_segments_pre(const int32_t* __restrict__ seg_starts,
+                                             const uint16_t* const* __restrict__ ptrs, int S,
+                                             int g0, int g1, TileSegs<ROWS>& sh,
+                                             const SegPre& pre) {
+  return tile_segments_impl<ROWS, THREADS, true>(seg_starts, ptrs, S, g0, g1, sh, pre);
 }
 
 // Next long run of a tile at or after row q (rows are in segment order): its slot k in
@@ -338,8 +386,12 @@ __global__ __launch_bounds__(256, (ShrCfg<R, RB_>::WAVES_PER_SIMD)) void shrink_
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int mrow = lane & 15, kq = lane >> 4;
+  // one round of loads for the caller rows, the segment bounds and the A pointers
+  const SegPre pre = seg_preload(seg_starts, A_ptrs, S);
   if (tid < MT) s_prow[tid] = (r0 + tid < r1) ? (perm ? perm[r0 + tid] : r0 + tid) : 0;
-  if (tile_long_segments<MT, 256>(seg_starts, A_ptrs, S, r0, r1, sh) == 0) return;  // uniform
+  if (tid == 0) sh.nseg = 0;
+  __syncthreads();
+  if (tile_long_segments_pre<MT, 256>(seg_starts, A_ptrs, S, r0, r1, sh, pre) == 0) return;  // uniform
   const int k_lo = kc * kcm;
   const int k_hi = min(h_in, k_lo + kcm);
   const int nst = (k_hi - k_lo + STAGE - 1) / STAGE;
@@ -504,8 +556,11 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
   const int kq = lane >> 4, l16 = lane & 15;
   const int wc = c0 + (TC / 4) * w;  // first column of this wave
 
-  // caller rows first, so that y is in flight while the segments are found
+  // one round of loads for the caller rows, the segment bounds and the B pointers; then y
+  // and v go out, the segments are found from registers, and B follows without waiting
+  const SegPre pre = seg_preload(seg_starts, B_ptrs, S);
   if (tid < TR) s_prow[tid] = (g0 + tid < g1) ? (perm ? perm[g0 + tid] : g0 + tid) : -1;
+  if (tid == 0) sh.nseg = 0;
   __syncthreads();
   // y: thread vector e = tid + 256u covers row e / VPR, columns c0 + 8 * (e % VPR) .. +7
   uint4 yv[YPT];
@@ -532,7 +587,7 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
       for (int k = 1; k < VS; ++k) vv[u] += t[k][u];  // slices past vks add exact zeros
     }
   }
-  if (tile_long_segments<TR, 256>(seg_starts, B_ptrs, S, g0, g1, sh) == 0) return;  // uniform
+  if (tile_long_segments_pre<TR, 256>(seg_starts, B_ptrs, S, g0, g1, sh, pre) == 0) return;  // uniform
 
   // B of the tile's first long run goes out now, so that its latency overlaps the wait
   // for v.  B row c holds the r values of column
