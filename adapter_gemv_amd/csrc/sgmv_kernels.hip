@@ -470,11 +470,12 @@ __global__ __launch_bounds__(256, (ShrCfg<R, RB_>::WAVES_PER_SIMD)) void shrink_
 // exact and summed in float32; hi + lo carries 16 (bf16) or 22 (fp16) significant bits of
 // scale*v.  For fp16 each row of scale*v is first multiplied by a power of two that puts
 // its largest magnitude in [2^14, 2^15), and the row's sums are multiplied back by the
-// inverse power (both exact), so any float32 v fits fp16's range.  The float32 sums go
-// through LDS so that y is read and written with whole
-// 16-byte vectors (TC/8 lanes per row): y is loaded as soon as the caller rows are known,
-// then updated as y + sum in float32 and rounded once.  The tile shape keeps the B bytes
-// a tile reads (TC x r) no larger than its y bytes (TR x TC).
+// inverse power (both exact), so any float32 v fits fp16's range.  B's columns are taken
+// in an order that leaves every lane with 8 consecutive columns of one row (exp_load_b),
+// so y is read and written with 16-byte vectors straight from the accumulators, with no
+// pass through LDS: y is loaded as soon as the caller rows are known, then updated as
+// y + sum in float32 and rounded once.  The tile shape keeps the B bytes a tile reads
+// (TC x r) no larger than its y bytes (TR x TC).
 //
 // Workgroup b runs on XCD b % 8 (round-robin dispatch).  Each XCD owns a contiguous range
 // of column strips, so its L2 holds only that part of every B[a]; within the range the
@@ -488,19 +489,21 @@ struct ExpCfg {
   static constexpr int TR = (R == 16) ? 32 : 64;    // rows per tile
   static constexpr int TC = (R == 16) ? 256 : 128;  // columns per tile (TC/4 per wave)
   static constexpr int RB = TR / 16, CB = TC / 64;  // 16 x 16 blocks per wave
-  static constexpr int PAD = 4;                     // floats of padding per LDS row of sums
-  // waves per SIMD the register budget is set for
-  static constexpr int WAVES_PER_SIMD = 4;
+  // waves per SIMD the register budget is set for (five spill at r = 64)
+  static constexpr int WAVES_PER_SIMD = (R == 64) ? 4 : 5;
 };
 
-// The B operand of one run for a wave's CB column blocks: lane (l16, kq) takes column
-// wc + 16cb + l16 and B values 32s + 8kq .. +7 (mod r) of it, s < NKU.
+// The B operand of one run for a wave's CB column blocks.  The blocks come in pairs whose
+// 16 columns are interleaved in groups of 4: block 2p + h, lane (l16, kq) takes column
+// wc + 32p + 8(l16/4) + 4h + l16%4 and B values 32s + 8kq .. +7 (mod r) of it, s < NKU.
+// The products then leave lane (kq, l16) with the 8 consecutive columns
+// wc + 32p + 8kq .. +7 of one row in blocks 2p and 2p + 1: 16 bytes of y.
 template <int R, int CB, int NKU>
 __device__ inline void exp_load_b(gptr<const uint16_t> B, int wc, int l16, int kq, int h_out,
                                   uint4 (&bop)[CB][NKU]) {
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    const int col = wc + 16 * cb + l16;
+    const int col = wc + 32 * (cb >> 1) + 8 * (l16 >> 2) + 4 * (cb & 1) + (l16 & 3);
 #pragma unroll
     for (int s = 0; s < NKU; ++s) {
       const int j0 = (32 * s + 8 * kq) % R;
@@ -526,18 +529,12 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
   constexpr int NK = KT / 32;        // MFMA k-steps
   constexpr int NKU = (R >= 32) ? R / 32 : 1;  // distinct B loads per column block
   constexpr int VPT = TR * R / 256;  // v values per thread
-  constexpr int VPR = TC / 8;        // 16-byte vectors per tile row
-  constexpr int YPT = TR * VPR / 256;  // 16-byte vectors of y per thread
+  static_assert(CB % 2 == 0, "column blocks come in pairs");
   __shared__ TileSegs<TR> sh;
   __shared__ int s_prow[TR];  // caller row of each tile row
-  // The hi/lo halves of scale * v (vlds) and, after the products, the float32 sums (dl)
-  // share one LDS buffer.  vlds rows are padded by 16 bytes: the 16 lanes that read one k
-  // range of 16 different rows then fall on 16 different bank groups instead of one.
-  typedef uint16_t VRows[TR][KT + 8];
-  typedef float DRows[TR][TC + C::PAD];
-  __shared__ __attribute__((aligned(16))) char smem[sizeof(DRows) > sizeof(VRows) ? sizeof(DRows) : sizeof(VRows)];
-  VRows& vlds = *reinterpret_cast<VRows*>(smem);
-  DRows& dl = *reinterpret_cast<DRows*>(smem);
+  // The hi/lo halves of scale * v.  Rows are padded by 16 bytes: the 16 lanes that read one
+  // k range of 16 different rows then fall on 16 different bank groups instead of one.
+  __shared__ __attribute__((aligned(16))) uint16_t vlds[TR][KT + 8];
   __shared__ int s_exp[TR];  // fp16: the row's sums are multiplied by 2^s_exp[row]
 
   // XCD x owns strips [sx0, sx1) and walks them tile-major
@@ -562,13 +559,18 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
   if (tid < TR) s_prow[tid] = (g0 + tid < g1) ? (perm ? perm[g0 + tid] : g0 + tid) : -1;
   if (tid == 0) sh.nseg = 0;
   __syncthreads();
-  // y: thread vector e = tid + 256u covers row e / VPR, columns c0 + 8 * (e % VPR) .. +7
-  uint4 yv[YPT];
+  // y in the products' layout: lane (kq, l16) holds row 16rb + l16, columns
+  // wc + 32p + 8kq .. +7
+  uint4 yv[RB][CB / 2];
+  int yrow[RB];
 #pragma unroll
-  for (int u = 0; u < YPT; ++u) {
-    const int e = tid + 256 * u, q = e / VPR, col = c0 + 8 * (e % VPR);
-    const int prow = s_prow[q];
-    yv[u] = (prow >= 0 && col < h_out) ? ld16(y + static_cast<int64_t>(prow) * ld_y + col) : zero4();
+  for (int rb = 0; rb < RB; ++rb) {
+    yrow[rb] = s_prow[16 * rb + l16];
+#pragma unroll
+    for (int p = 0; p < CB / 2; ++p) {
+      const int col = wc + 32 * p + 8 * kq;
+      yv[rb][p] = (yrow[rb] >= 0 && col < h_out) ? ld16(y + static_cast<int64_t>(yrow[rb]) * ld_y + col) : zero4();
+    }
   }
   float vv[VPT];
   {
@@ -643,11 +645,11 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
     if ((sg = next_run(sh, q)) < 0) break;
     exp_load_b<R, CB, NKU>(global_ptr(sh.ptr[sg]), wc, l16, kq, h_out, bop);
   }
-  __syncthreads();  // every wave is done reading vlds before dl overwrites it
-  // lane: D rows 4*kq .. +3 of column block cb = tile columns (TC/4)w + 16cb + 4kq .. +3,
-  // D column l16 = tile row 16rb + l16
+  // y + sum, rounded once, straight from the accumulators: lane (kq, l16) owns 16 bytes
+  // of row 16rb + l16 per block pair
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
+    if (rs[rb] < 0) continue;
     if constexpr (DT == SGMV_F16) {
       const int ex = s_exp[16 * rb + l16];
 #pragma unroll
@@ -656,22 +658,18 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
         for (int i = 0; i < 4; ++i) acc[rb][cb][i] = ldexpf(acc[rb][cb][i], ex);
     }
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-      *reinterpret_cast<f32x4_t*>(&dl[16 * rb + l16][(TC / 4) * w + 16 * cb + 4 * kq]) = acc[rb][cb];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < YPT; ++u) {
-    const int e = tid + 256 * u, q2 = e / VPR, cc = 8 * (e % VPR), col = c0 + cc;
-    if (sh.rseg[q2] < 0 || col >= h_out) continue;
-    const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(&dl[q2][cc]);
-    const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(&dl[q2][cc + 4]);
-    uint4 o;
-    o.x = E::pack(E::lo(yv[u].x) + d0[0], E::hi(yv[u].x) + d0[1]);
-    o.y = E::pack(E::lo(yv[u].y) + d0[2], E::hi(yv[u].y) + d0[3]);
-    o.z = E::pack(E::lo(yv[u].z) + d1[0], E::hi(yv[u].z) + d1[1]);
-    o.w = E::pack(E::lo(yv[u].w) + d1[2], E::hi(yv[u].w) + d1[3]);
-    *reinterpret_cast<uint4*>(y + static_cast<int64_t>(s_prow[q2]) * ld_y + col) = o;
+    for (int p = 0; p < CB / 2; ++p) {
+      const int col = wc + 32 * p + 8 * kq;
+      if (col >= h_out) continue;
+      const f32x4_t d0 = acc[rb][2 * p], d1 = acc[rb][2 * p + 1];
+      const uint4 yy = yv[rb][p];
+      uint4 o;
+      o.x = E::pack(E::lo(yy.x) + d0[0], E::hi(yy.x) + d0[1]);
+      o.y = E::pack(E::lo(yy.y) + d0[2], E::hi(yy.y) + d0[3]);
+      o.z = E::pack(E::lo(yy.z) + d1[0], E::hi(yy.z) + d1[1]);
+      o.w = E::pack(E::lo(yy.w) + d1[2], E::hi(yy.w) + d1[3]);
+      *reinterpret_cast<uint4*>(y + static_cast<int64_t>(yrow[rb]) * ld_y + col) = o;
+    }
   }
 }
 
