@@ -474,8 +474,9 @@ __global__ __launch_bounds__(256, (ShrCfg<R, RB_>::WAVES_PER_SIMD)) void shrink_
 // in an order that leaves every lane with 8 consecutive columns of one row (exp_load_b),
 // so y is read and written with 16-byte vectors straight from the accumulators, with no
 // pass through LDS: y is loaded as soon as the caller rows are known, then updated as
-// y + sum in float32 and rounded once.  The tile shape keeps the B bytes a tile reads
-// (TC x r) no larger than its y bytes (TR x TC).
+// y + sum in float32 and rounded once.  Tiles are 32 x 256 (64 x 128 at r = 32); at
+// r = 64 a tile then reads twice as many B bytes (from L2) as y bytes, which measured
+// faster than the squarer 64 x 128 tiles.
 //
 // Workgroup b runs on XCD b % 8 (round-robin dispatch).  Each XCD owns a contiguous range
 // of column strips, so its L2 holds only that part of every B[a]; within the range the
@@ -486,8 +487,9 @@ constexpr int kExpandSlices = 4;
 
 template <int R>
 struct ExpCfg {
-  static constexpr int TR = (R == 16) ? 32 : 64;    // rows per tile
-  static constexpr int TC = (R == 16) ? 256 : 128;  // columns per tile (TC/4 per wave)
+  // rows and columns per tile (TC/4 columns per wave); measured on MI355X
+  static constexpr int TR = (R == 32) ? 64 : 32;
+  static constexpr int TC = (R == 32) ? 128 : 256;
   static constexpr int RB = TR / 16, CB = TC / 64;  // 16 x 16 blocks per wave
   // waves per SIMD the register budget is set for (five spill at r = 64)
   static constexpr int WAVES_PER_SIMD = (R == 64) ? 4 : 5;
