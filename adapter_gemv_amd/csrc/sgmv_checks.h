@@ -13,6 +13,7 @@
 namespace sgmv_host {
 
 constexpr int64_t kMaxDim = int64_t(1) << 22;
+constexpr int kLongMin = 16;  // segments with at least this many rows use the MFMA kernels
 
 inline bool rank_ok(int32_t r) { return r == 16 || r == 32 || r == 64; }
 

@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __r
   constexpr int T = kGroupThreads, W = T / 64;
   __shared__ int key[kGroupSlots];  // adapter id of the slot, -1 = empty
   __shared__ int cnt[kGroupSlots];  // rows of the slot, then its next free position
-  __shared__ int wrows[W], wsegs[W];
+  __shared__ int wrows[W], wsegs[W], wsrows[W], wssegs[W];
   __shared__ int s_bad, s_min, s_max, s_rows, s_segs;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 #pragma unroll
@@ -377,36 +377,59 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __r
     run_len[u] = head ? len : 0;
   }
   __syncthreads();
-  // scan over the slots: thread t owns slots kSlotsPer*t .. +kSlotsPer-1
-  int rows = 0, segs = 0;
+  // scan over the slots: thread t owns slots kSlotsPer*t .. +kSlotsPer-1.  Groups of at
+  // least kLongMin rows come first, then the short ones, so that the long segments start
+  // at row 0 and the MFMA tiles meet as few short rows as a sorted batch does.
+  int lr = 0, ls = 0, sr = 0, ss = 0;  // long rows / segments, short rows / segments
 #pragma unroll
   for (int u = 0; u < kSlotsPer; ++u) {
     const int c = cnt[kSlotsPer * tid + u];
-    rows += c;
-    segs += (c > 0);
+    if (c >= kLongMin) {
+      lr += c;
+      ++ls;
+    } else if (c > 0) {
+      sr += c;
+      ++ss;
+    }
   }
-  int ir = rows, is = segs;
+  int ilr = lr, ils = ls, isr = sr, iss = ss;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const int ur = __shfl_up(ir, d), us = __shfl_up(is, d);
+    const int a0 = __shfl_up(ilr, d), a1 = __shfl_up(ils, d), a2 = __shfl_up(isr, d),
+              a3 = __shfl_up(iss, d);
     if (lane >= d) {
-      ir += ur;
-      is += us;
+      ilr += a0;
+      ils += a1;
+      isr += a2;
+      iss += a3;
     }
   }
   if (lane == 63) {
-    wrows[wv] = ir;
-    wsegs[wv] = is;
+    wrows[wv] = ilr;
+    wsegs[wv] = ils;
+    wsrows[wv] = isr;
+    wssegs[wv] = iss;
   }
   __syncthreads();
-  int row0 = ir - rows, seg0 = is - segs;
-  for (int q = 0; q < wv; ++q) {
-    row0 += wrows[q];
-    seg0 += wsegs[q];
+  int lrow = ilr - lr, lseg = ils - ls, srow = isr - sr, sseg = iss - ss;
+  int tlr = 0, tls = 0, tsr = 0, tss = 0;  // totals
+  for (int q = 0; q < W; ++q) {
+    if (q < wv) {
+      lrow += wrows[q];
+      lseg += wsegs[q];
+      srow += wsrows[q];
+      sseg += wssegs[q];
+    }
+    tlr += wrows[q];
+    tls += wsegs[q];
+    tsr += wsrows[q];
+    tss += wssegs[q];
   }
-  if (tid == T - 1) {
-    s_rows = row0 + rows;
-    s_segs = seg0 + segs;
+  srow += tlr;  // short groups after all long ones
+  sseg += tls;
+  if (tid == 0) {
+    s_rows = tlr + tsr;
+    s_segs = tls + tss;
   }
   int mn = 0x7fffffff, mx = 0;
 #pragma unroll
@@ -414,18 +437,26 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __r
     const int sl = kSlotsPer * tid + u;
     const int c = cnt[sl];
     if (c > 0) {
+      const bool lng = c >= kLongMin;
+      const int seg = lng ? lseg : sseg;
+      const int row0 = lng ? lrow : srow;
       const int a = key[sl];
-      o.seg_starts[seg0] = row0;
-      o.seg_adapter[seg0] = a;
+      o.seg_starts[seg] = row0;
+      o.seg_adapter[seg] = a;
       if (o.A_ptrs) {
-        o.A_ptrs[seg0] = o.A_pool + static_cast<int64_t>(a) * o.A_stride;
-        o.B_ptrs[seg0] = o.B_pool + static_cast<int64_t>(a) * o.B_stride;
+        o.A_ptrs[seg] = o.A_pool + static_cast<int64_t>(a) * o.A_stride;
+        o.B_ptrs[seg] = o.B_pool + static_cast<int64_t>(a) * o.B_stride;
       }
       mn = min(mn, c);
       mx = max(mx, c);
       cnt[sl] = row0;  // from now on: the group's next free position
-      row0 += c;
-      ++seg0;
+      if (lng) {
+        lrow += c;
+        ++lseg;
+      } else {
+        srow += c;
+        ++sseg;
+      }
     }
   }
   if (mx > 0) {

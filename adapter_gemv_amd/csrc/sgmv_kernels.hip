@@ -28,7 +28,6 @@ namespace {
 using namespace sgmv_dev;
 using namespace sgmv_host;
 
-constexpr int kLongMin = 16;   // segments with at least this many rows use MFMA tiles
 constexpr int kShortMax = kLongMin - 1;
 
 // ------------------------------------------------------------------------------------
@@ -54,12 +53,14 @@ __global__ __launch_bounds__(256) void shrink_gemv_kernel(
     const int32_t* __restrict__ meta) {
   using C = GemvCfg<R>;
   __shared__ float red[4][kShortMax][R];
-  const int kc = blockIdx.y;
-  // segments blockIdx.x, + gridDim.x, ... (the count comes from the device tables' meta
-  // word when the tables were built on the device)
+  // items (segment s, chunk kc) = (i % S, i / S): one per workgroup of a (S, ks) grid with
+  // host tables; strided over a 1-D grid when the segment count comes from the device
+  // tables' meta word
   const int S = meta ? meta[0] : static_cast<int>(gridDim.x);
   if (meta && meta[1] >= kLongMin) return;  // no short segment at all
-  for (int s = blockIdx.x; s < S; s += gridDim.x) {
+  const int items = S * ks;
+  for (int item = blockIdx.x + gridDim.x * blockIdx.y; item < items; item += gridDim.x * gridDim.y) {
+  const int s = item % S, kc = item / S;
   const int seg0 = seg_starts[s];
   const int m = seg_starts[s + 1] - seg0;
   if (m <= 0 || m >= kLongMin) continue;  // uniform
@@ -115,21 +116,24 @@ template <int DT, int R>
 __global__ __launch_bounds__(64) void expand_gemv_kernel(
     uint16_t* __restrict__ y, int64_t ld_y, const float* __restrict__ vsrc, int64_t slice,
     int32_t ks, const uint16_t* const* __restrict__ B_ptrs, const int32_t* __restrict__ seg_starts,
-    const int32_t* __restrict__ perm, int32_t h_out, float scale,
+    const int32_t* __restrict__ perm, int32_t h_out, float scale, int32_t chunks,
     const int32_t* __restrict__ meta) {
   using E = Elem<DT>;
   constexpr int CPL = 128 / R;
   constexpr int NV = 16;  // CPL * R / 8
   constexpr int YW = CPL / 2;  // 32-bit words of y per lane and row
   __shared__ float vs[kShortMax][R];
+  // items (segment s, column chunk ch) = (i % S, i / S), as in shrink_gemv_kernel
   const int S = meta ? meta[0] : static_cast<int>(gridDim.x);
   if (meta && meta[1] >= kLongMin) return;  // no short segment at all
-  for (int s = blockIdx.x; s < S; s += gridDim.x) {
+  const int items = S * chunks;
+  for (int item = blockIdx.x + gridDim.x * blockIdx.y; item < items; item += gridDim.x * gridDim.y) {
+  const int s = item % S, ch = item / S;
   const int seg0 = seg_starts[s];
   const int m = seg_starts[s + 1] - seg0;
   if (m <= 0 || m >= kLongMin) continue;  // uniform
   const int lane = threadIdx.x;
-  const int c0 = (blockIdx.y * 64 + lane) * CPL;
+  const int c0 = (ch * 64 + lane) * CPL;
   const bool cin = c0 < h_out;
 
   uint4 b[NV];
@@ -749,8 +753,14 @@ struct Tables {
   const int32_t* meta = nullptr;
   bool use_gemv() const { return meta || min_len < kLongMin; }
   bool use_long() const { return meta || max_len >= kLongMin; }
-  // grid width of the GEMV kernels (they loop over the segments beyond it)
-  unsigned gemv_grid() const { return static_cast<unsigned>(meta ? (S < 256 ? S : 256) : S); }
+  // grid of a GEMV kernel with `per` items per segment: one workgroup per item with host
+  // tables; with device tables at most max_wgs workgroups striding over S_max * per items
+  // (the real count is only known on the device)
+  dim3 gemv_grid(int per, int max_wgs) const {
+    if (!meta) return dim3(static_cast<unsigned>(S), static_cast<unsigned>(per));
+    const int64_t items = static_cast<int64_t>(S) * per;
+    return dim3(static_cast<unsigned>(items < max_wgs ? items : max_wgs), 1);
+  }
 };
 
 template <int DT, int R, int RB>
@@ -782,7 +792,7 @@ hipError_t launch_shrink(hipStream_t st, const uint16_t* x, int64_t ld_x, const 
   if (T.use_gemv()) {
     const int ks = (h_in + GemvCfg<R>::KC - 1) / GemvCfg<R>::KC;
     *ks_gemv = ks;
-    hipLaunchKernelGGL((shrink_gemv_kernel<DT, R>), dim3(T.gemv_grid(), ks), dim3(256), 0, st, x,
+    hipLaunchKernelGGL((shrink_gemv_kernel<DT, R>), T.gemv_grid(ks, 2048), dim3(256), 0, st, x,
                        ld_x, T.ptrs, T.seg_starts, T.perm, h_in, part, L.slice, rowks, ks, T.meta);
   }
   if (T.use_long()) {
@@ -804,9 +814,9 @@ hipError_t launch_expand(hipStream_t st, uint16_t* y, int64_t ld_y, const float*
   constexpr int CPL = 128 / R;
   if (T.use_gemv()) {
     const int chunks = (h_out + 64 * CPL - 1) / (64 * CPL);
-    hipLaunchKernelGGL((expand_gemv_kernel<DT, R>), dim3(T.gemv_grid(), chunks), dim3(64), 0, st,
+    hipLaunchKernelGGL((expand_gemv_kernel<DT, R>), T.gemv_grid(chunks, 8192), dim3(64), 0, st,
                        y, ld_y, vsrc, slice, ks_gemv, T.ptrs, T.seg_starts, T.perm, h_out, scale,
-                       T.meta);
+                       chunks, T.meta);
   }
   if (T.use_long()) {
     // each XCD takes ceil(strips / 8) strips at most: pad the grid to 8 equal shares
