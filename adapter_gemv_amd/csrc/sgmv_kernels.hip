@@ -18,6 +18,7 @@
 
 #include <climits>
 #include <cstdint>
+#include <type_traits>
 
 #include "../../include/sgmv.h"
 #include "sgmv_checks.h"
@@ -293,7 +294,7 @@ __device__ inline int next_run(const TileSegs<ROWS>& sh, int& q) {
   return k;
 }
 
-// Shrink on MFMA 16x16x32 for a tile of r sorted rows and one K chunk.  The x rows are
+// Shrink on MFMA 16x16x32 for a tile of r sorted rows and one K chunk (r = 16 and 32).  The x rows are
 // the A operand and the adapter's stored A rows the B operand; lane l supplies row (or
 // column) l%16 and k = k0 + 8*(l/16) .. +7 of each 32-wide k step.  Each of the 4 waves
 // covers all r rows and r columns (r/16 x r/16 accumulator blocks), so A and x are read
@@ -308,21 +309,26 @@ __device__ inline int next_run(const TileSegs<ROWS>& sh, int& q) {
 // XCD's L2 keeps one eighth of the K range of the adapters' A.
 constexpr int kXcds = 8;
 
-template <int R, int RB_ = R / 16>
+template <int R>
 struct ShrCfg {
+  static_assert(R == 16 || R == 32, "r = 64 takes shrink_lds_kernel");
   static constexpr int NB = R / 16;                 // column blocks of v
-  static constexpr int RB = RB_;                    // row blocks
+  static constexpr int RB = R / 16;                 // row blocks
   static constexpr int MT = 16 * RB;                // rows per tile
-  static constexpr int UN = (R == 16 && RB == 1) ? 2 : 1;  // k steps per stage
+  static constexpr int UN = (R == 16) ? 2 : 1;      // k steps per stage
   static constexpr int STAGE = 32 * UN;             // k per stage
-  static constexpr int WAVES_PER_SIMD = (R == 64) ? 2 : 3;
-  static constexpr int TARGET_WGS = (R == 16) ? (RB == 1 ? 256 : 512) : (R == 32 ? 384 : 512);
+  static constexpr int WAVES_PER_SIMD = 3;
+  static constexpr int TARGET_WGS = (R == 16) ? 256 : 384;
 };
 
-// r = 16: tiles of 16 rows, except for long rows of x (h_in > 16384), where 64-row tiles
-// read each k range of A once for four times as many rows (measured on MI355X: 70B down
-// projection 120 -> 93 us per call; 16-row tiles stay faster up to h_in = 13824)
-inline bool shrink_tall(int r, int32_t h_in) { return r == 16 && h_in > 16384; }
+// The LDS-staged shrink (shrink_lds_kernel, 64-row tiles) takes r = 64, and r = 16 when
+// the rows of x are long (h_in > 16384).  Measured on MI355X for the 70B batch: r = 64
+// gate/up shrink 27.6 -> 21.0 us, down 57.6 -> 49.3 us, r = 16 down 41.6 -> 35.6 us; for
+// r = 16 at h_in <= 13824 it is slower than 16-row tiles of shrink_mfma_kernel.
+inline bool shrink_lds_long_rows(int32_t h_in) { return h_in > 16384; }
+template <int R> constexpr int kLdsD = (R == 16) ? 3 : 6;  // stage buffers
+constexpr int kLdsMT = 64;                                  // rows per tile
+constexpr int kLdsWgs = 512;                                // workgroup target
 // Loads of one stage.  They are unconditional (out-of-range k reads offset 0 of the same
 // row, rows outside the current run read a row that exists) so that the compiler can count
 // them exactly and keep the next stage in flight; shr_mul zeroes what does not belong.
@@ -360,8 +366,8 @@ __device__ inline void shr_mul(const uint4 (&xv)[C::UN][C::RB], const uint4 (&av
   }
 }
 
-template <int DT, int R, int RB_>
-__global__ __launch_bounds__(256, (ShrCfg<R, RB_>::WAVES_PER_SIMD)) void shrink_mfma_kernel(
+template <int DT, int R>
+__global__ __launch_bounds__(256, ShrCfg<R>::WAVES_PER_SIMD) void shrink_mfma_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, const uint16_t* const* __restrict__ A_ptrs,
     const int32_t* __restrict__ seg_starts, int32_t S_host, const int32_t* __restrict__ perm,
     int32_t n, int32_t h_in, int32_t kcm, int32_t ks, float* __restrict__ part, int64_t slice,
@@ -369,7 +375,7 @@ __global__ __launch_bounds__(256, (ShrCfg<R, RB_>::WAVES_PER_SIMD)) void shrink_
     const int32_t* __restrict__ meta) {
   const int S = meta ? meta[0] : S_host;
   if (meta && meta[2] < kLongMin) return;  // no long segment at all
-  using C = ShrCfg<R, RB_>;
+  using C = ShrCfg<R>;
   constexpr int NB = C::NB, RB = C::RB, UN = C::UN, STAGE = C::STAGE, MT = C::MT;
   __shared__ TileSegs<MT> sh;
   __shared__ int s_prow[MT];
@@ -462,6 +468,212 @@ __global__ __launch_bounds__(256, (ShrCfg<R, RB_>::WAVES_PER_SIMD)) void shrink_
     }
   }
   // rows of long segments: final v (ks == 1) or ks slices for reduce_v_kernel
+  if (kc == 0)
+    for (int qr = tid; qr < r1 - r0; qr += 256)
+      if (sh.rseg[qr] >= 0) rowks[r0 + qr] = (ks == 1) ? 0 : ks;
+}
+
+// Shrink on MFMA with the operands staged in LDS by direct global-to-LDS loads.  Same
+// product and outputs as shrink_mfma_kernel, organised to keep many bytes in flight at a
+// small register cost: every 1 KB operand block (64 lanes x 16 bytes, fetched in the
+// MFMA's lane order) goes straight from global memory into a ring of D stage buffers, so
+// D - 1 stages are in flight while one is multiplied.  The four waves split the tile's
+// rows (each owns MT / 4 rows over the whole chunk) and share the stage's A blocks, so A
+// is fetched once per tile and chunk for all MT rows, and no cross-wave sum is needed.  A
+// stage covers k = 32 * UN with NB * UN = 4 A blocks, one fetched by each wave.  A wave
+// waits for its own loads of a stage (vmcnt), then a barrier makes every wave's loads
+// visible; the same barrier tells each wave that all waves have finished reading the
+// buffer it refills next.  The stage buffers are separate LDS variables addressed with
+// compile-time indices, so that the compiler can tell which loads a read depends on.
+template <int R, int MT_, int D_>
+struct ShrLdsCfg {
+  static constexpr int NB = R / 16;     // column blocks of v
+  static constexpr int MT = MT_;        // rows per tile
+  static constexpr int RBW = MT / 64;   // 16-row blocks per wave
+  static constexpr int UN = 4 / NB;     // k steps of 32 per stage
+  static constexpr int STAGE = 32 * UN;
+  static constexpr int XPW = RBW * UN;  // x blocks per wave and stage
+  static constexpr int LPS = 1 + XPW;   // 1 KB loads per wave and stage
+  static constexpr int D = D_;          // stage buffers
+  static_assert(NB * UN == 4 && RBW >= 1 && MT <= 256, "tile shape");
+  static_assert(D >= 3 && D <= 8 && (D - 2) * LPS < 64, "ring depth");
+};
+
+template <class C>
+struct ShrStage {
+  uint4 a[4][64];          // A block j: k step j / NB, columns 16 * (j % NB) ..
+  uint4 x[4][C::XPW][64];  // wave w's x block i: k step i / RBW, rows 16 * (i % RBW) ..
+};
+
+// wait until at most N vector-memory loads of this wave are in flight (gfx9 s_waitcnt:
+// vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ inline void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
+
+// 16 bytes per lane from src into LDS at dst + 16 * lane (dst is the same for the wave)
+__device__ inline void load_to_lds(gptr<const uint16_t> src, uint4* dst) {
+  __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)dst, 16, 0, 0);
+}
+
+// workgroup barrier with no memory fence (so no wait for the loads in flight); the
+// signal fences keep the compiler from moving LDS accesses across it
+__device__ inline void barrier_no_fence() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int I, int N, class F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+template <int DT, int R, int MT, int D>
+__global__ __launch_bounds__(256) void shrink_lds_kernel(
+    const uint16_t* __restrict__ x, int64_t ld_x, const uint16_t* const* __restrict__ A_ptrs,
+    const int32_t* __restrict__ seg_starts, int32_t S_host, const int32_t* __restrict__ perm,
+    int32_t n, int32_t h_in, int32_t kcm, int32_t ks, float* __restrict__ part, int64_t slice,
+    float* __restrict__ v_out, int32_t* __restrict__ rowks,
+    const int32_t* __restrict__ meta) {
+  using C = ShrLdsCfg<R, MT, D>;
+  constexpr int NB = C::NB, RBW = C::RBW, UN = C::UN, STAGE = C::STAGE, XPW = C::XPW;
+  constexpr int LPS = C::LPS;
+  const int S = meta ? meta[0] : S_host;
+  if (meta && meta[2] < kLongMin) return;  // no long segment at all
+  __shared__ TileSegs<MT> sh;
+  __shared__ int s_prow[MT];
+  __shared__ ShrStage<C> b0, b1, b2, b3, b4, b5, b6, b7;
+  auto buf = [&](auto J) -> ShrStage<C>& {
+    constexpr int j = decltype(J)::value;
+    if constexpr (j == 0) return b0;
+    else if constexpr (j == 1) return b1;
+    else if constexpr (j == 2) return b2;
+    else if constexpr (j == 3) return b3;
+    else if constexpr (j == 4) return b4;
+    else if constexpr (j == 5) return b5;
+    else if constexpr (j == 6) return b6;
+    else return b7;
+  };
+
+  const int b = blockIdx.x;
+  int tile, kc;
+  if (ks % kXcds == 0) {
+    const int m = ks / kXcds, j = b / kXcds;
+    tile = j / m;
+    kc = b % kXcds + kXcds * (j % m);
+  } else {
+    tile = b / ks;
+    kc = b % ks;
+  }
+  const int r0 = tile * MT;
+  const int r1 = min(n, r0 + MT);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int mrow = lane & 15, kq = lane >> 4;
+  const SegPre pre = seg_preload(seg_starts, A_ptrs, S);
+  if (tid < MT) s_prow[tid] = (r0 + tid < r1) ? (perm ? perm[r0 + tid] : r0 + tid) : 0;
+  if (tid == 0) sh.nseg = 0;
+  __syncthreads();
+  if (tile_long_segments_pre<MT, 256>(seg_starts, A_ptrs, S, r0, r1, sh, pre) == 0) return;  // uniform
+  const int k_lo = kc * kcm;
+  const int k_hi = min(h_in, k_lo + kcm);
+  // stages of the chunk, padded to a multiple of D (padding stages load in-range
+  // addresses and multiply zeros)
+  const int nst = ((k_hi - k_lo + STAGE - 1) / STAGE + D - 1) / D * D;
+  const int qw = w * 16 * RBW;  // this wave's first row in the tile
+  const int au = w / NB, anb = w % NB;  // the A block this wave fetches
+
+  f32x4_t acc[RBW][NB];
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int q = 0;
+  for (int sg; (sg = next_run(sh, q)) >= 0;) {
+    // rows outside the run fetch row r0 of the tile (it exists) and are zeroed below
+    gptr<const uint16_t> xr[RBW];
+    bool xin[RBW];
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      const int qr = qw + 16 * rb + mrow;
+      xin[rb] = sh.rseg[qr] == sg;
+      xr[rb] = global_ptr(x) + static_cast<int64_t>(s_prow[xin[rb] ? qr : 0]) * ld_x;
+    }
+    const gptr<const uint16_t> ar =
+        global_ptr(sh.ptr[sg]) + static_cast<int64_t>(anb * 16 + mrow) * h_in;
+    auto issue = [&](auto J, int s) {
+      ShrStage<C>& st = buf(J);
+      const int k0 = k_lo + s * STAGE + 8 * kq;
+      const int ka = k0 + 32 * au;
+      load_to_lds(ar + (ka < k_hi ? ka : 0), &st.a[w][0]);
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const int kk = k0 + 32 * u;
+        const int off = kk < k_hi ? kk : 0;
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) load_to_lds(xr[rb] + off, &st.x[w][u * RBW + rb][0]);
+      }
+    };
+    auto compute = [&](auto J, int s) {
+      const ShrStage<C>& st = buf(J);
+      const int k0 = k_lo + s * STAGE + 8 * kq;
+      uint4 av[4], xv[XPW];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) av[j] = st.a[j][lane];
+#pragma unroll
+      for (int i = 0; i < XPW; ++i) xv[i] = st.x[w][i][lane];
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const bool in = k0 + 32 * u < k_hi;
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) {
+          const uint4 xa = (in && xin[rb]) ? xv[u * RBW + rb] : zero4();
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            acc[rb][nb] = Elem<DT>::mfma(xa, in ? av[u * NB + nb] : zero4(), acc[rb][nb]);
+        }
+      }
+    };
+    auto step = [&](auto J, int s) {
+      wait_vmem<(D - 2) * LPS>();
+      barrier_no_fence();
+      issue(std::integral_constant<int, (decltype(J)::value + D - 1) % D>{}, s + D - 1);
+      compute(J, s);
+    };
+    static_for<0, D - 1>([&](auto J) { issue(J, J); });
+    int s = 0;
+    for (; s < nst - D; s += D) static_for<0, D>([&](auto J) { step(J, s + J); });
+    step(std::integral_constant<int, 0>{}, s);  // fetches the last stage, nst - 1
+    wait_vmem<0>();
+    barrier_no_fence();
+    static_for<1, D>([&](auto J) { compute(J, s + J); });
+    barrier_no_fence();  // the next run refills the buffers
+  }
+  // rows qw + 16rb + 4(lane/16) + c, column nb*16 + lane%16
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int qr = qw + 16 * rb + 4 * kq + c;
+      if (sh.rseg[qr] < 0) continue;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int64_t o = static_cast<int64_t>(r0 + qr) * R + nb * 16 + mrow;
+        if (ks == 1)
+          v_out[o] = acc[rb][nb][c];
+        else
+          part[kc * slice + o] = acc[rb][nb][c];
+      }
+    }
   if (kc == 0)
     for (int qr = tid; qr < r1 - r0; qr += 256)
       if (sh.rseg[qr] >= 0) rowks[r0 + qr] = (ks == 1) ? 0 : ks;
@@ -729,17 +941,21 @@ static_assert(GemvCfg<16>::KC == 512 && GemvCfg<32>::KC == 256 && GemvCfg<64>::K
 // sweeps on MI355X: fewer, longer chunks win for r = 16, more for r = 64), chunks of at
 // least 256 k, a multiple of 8 chunks where there are 8 or more (XCD-owned chunks), and
 // no more slices than the workspace holds
-template <class C>
-inline void mfma_split(int32_t n, int32_t h_in, int ks_cap, int* kcm, int* ks) {
-  const int tiles = (n + C::MT - 1) / C::MT;
-  const int target = C::TARGET_WGS;
+inline void split_k(int32_t n, int32_t h_in, int ks_cap, int mt, int target, int granule,
+                    int* kcm, int* ks) {
+  const int tiles = (n + mt - 1) / mt;
   int k = (target + tiles - 1) / tiles;
   k = min(k, max(1, h_in / 256));
   k = max(1, min(k, ks_cap));
   if (k >= 8) k -= k % 8;
-  const int c = ((h_in + k - 1) / k + 63) / 64 * 64;
+  const int c = ((h_in + k - 1) / k + granule - 1) / granule * granule;
   *kcm = c;
   *ks = (h_in + c - 1) / c;
+}
+
+template <class C>
+inline void mfma_split(int32_t n, int32_t h_in, int ks_cap, int* kcm, int* ks) {
+  split_k(n, h_in, ks_cap, C::MT, C::TARGET_WGS, 64, kcm, ks);
 }
 
 // Segment tables of one call.  With host tables S, min_len and max_len are exact.  With
@@ -763,16 +979,33 @@ struct Tables {
   }
 };
 
-template <int DT, int R, int RB>
+template <int DT, int R>
 hipError_t launch_shrink_mfma(hipStream_t st, const uint16_t* x, int64_t ld_x, const Tables& T,
                               int32_t h_in, const WsLayout& L, float* part, float* v_long,
                               int32_t* rowks, int* ks_long) {
-  using C = ShrCfg<R, RB>;
+  using C = ShrCfg<R>;
   int kcm, ks;
   mfma_split<C>(T.n, h_in, L.ks_max, &kcm, &ks);
   const int tiles = (T.n + C::MT - 1) / C::MT;
-  hipLaunchKernelGGL((shrink_mfma_kernel<DT, R, RB>), dim3(tiles * ks), dim3(256), 0, st, x, ld_x,
+  hipLaunchKernelGGL((shrink_mfma_kernel<DT, R>), dim3(tiles * ks), dim3(256), 0, st, x, ld_x,
                      T.ptrs, T.seg_starts, T.S, T.perm, T.n, h_in, kcm, ks, part, L.slice,
+                     v_long, rowks, T.meta);
+  *ks_long = ks;
+  return hipGetLastError();
+}
+
+// LDS-staged shrink: tiles of MT rows, D stage buffers, about `target` workgroups; chunks
+// are whole multiples of D stages where the split allows (the kernel pads the last)
+template <int DT, int R, int MT, int D>
+hipError_t launch_shrink_lds(hipStream_t st, const uint16_t* x, int64_t ld_x, const Tables& T,
+                             int32_t h_in, const WsLayout& L, float* part, float* v_long,
+                             int32_t* rowks, int* ks_long, int target) {
+  using C = ShrLdsCfg<R, MT, D>;
+  int kcm, ks;
+  split_k(T.n, h_in, L.ks_max, MT, target, C::STAGE * D, &kcm, &ks);
+  const int tiles = (T.n + MT - 1) / MT;
+  hipLaunchKernelGGL((shrink_lds_kernel<DT, R, MT, D>), dim3(tiles * ks), dim3(256), 0, st, x,
+                     ld_x, T.ptrs, T.seg_starts, T.S, T.perm, T.n, h_in, kcm, ks, part, L.slice,
                      v_long, rowks, T.meta);
   *ks_long = ks;
   return hipGetLastError();
@@ -796,11 +1029,15 @@ hipError_t launch_shrink(hipStream_t st, const uint16_t* x, int64_t ld_x, const 
                        ld_x, T.ptrs, T.seg_starts, T.perm, h_in, part, L.slice, rowks, ks, T.meta);
   }
   if (T.use_long()) {
-    if constexpr (R == 16) {
-      if (shrink_tall(R, h_in))
-        return launch_shrink_mfma<DT, R, 4>(st, x, ld_x, T, h_in, L, part, v_long, rowks, ks_long);
+    if constexpr (R == 64) {
+      return launch_shrink_lds<DT, R, kLdsMT, kLdsD<R>>(st, x, ld_x, T, h_in, L, part, v_long,
+                                                        rowks, ks_long, kLdsWgs);
+    } else {
+      if (R == 16 && shrink_lds_long_rows(h_in))
+        return launch_shrink_lds<DT, 16, kLdsMT, kLdsD<16>>(st, x, ld_x, T, h_in, L, part, v_long,
+                                                            rowks, ks_long, kLdsWgs);
+      return launch_shrink_mfma<DT, R>(st, x, ld_x, T, h_in, L, part, v_long, rowks, ks_long);
     }
-    return launch_shrink_mfma<DT, R, R / 16>(st, x, ld_x, T, h_in, L, part, v_long, rowks, ks_long);
   }
   return hipGetLastError();
 }
