@@ -150,17 +150,19 @@ __device__ inline float dot8(const uint4& a, const uint4& b, float acc) {
   return acc;
 }
 
-// sum of ks float slices src[0], src[stride], ... in slice order, 8 loads in flight
+// Sum of ks float slices src[0], src[stride], ... in the one order every table-path kernel
+// uses for split-K slices: four partial sums p_q over slices q, q + 4, q + 8, ... (each
+// from 0, in increasing slice order), then (p0 + p1) + (p2 + p3).  8 loads in flight.
 __device__ inline float sum_slices(const float* __restrict__ src, int64_t stride, int ks) {
-  float acc = 0.f;
+  float p[4] = {0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < ks; k0 += 8) {
     float v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) v[u] = (k0 + u < ks) ? src[(k0 + u) * stride] : 0.f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc += v[u];
+    for (int u = 0; u < 8; ++u) p[u & 3] += v[u];
   }
-  return acc;
+  return (p[0] + p[1]) + (p[2] + p[3]);
 }
 
 }  // namespace sgmv_dev

@@ -342,3 +342,60 @@ def test_lora_layer_table_path(torch_cuda):
     _say(f"[layer] table: {r}")
     assert r["path"].startswith("table")
     assert r["parity"]["ok"], r["parity"]
+
+
+# --------------------------------------------------------------------------------------
+# short and long segments in one call: eager (one stream) against graph replay (the short
+# chain on a forked second stream), bit for bit
+# --------------------------------------------------------------------------------------
+def _mixed_ids(n_long, n_short_each, n_short_adapters, seed):
+    """Two long segments (adapters 0 and 1) and short segments on adapters 2 .., interleaved
+    in caller order."""
+    rng = np.random.default_rng(seed)
+    ids = np.concatenate([np.zeros(n_long, np.int32), np.ones(n_long, np.int32),
+                          np.repeat(np.arange(2, 2 + n_short_adapters, dtype=np.int32), n_short_each)])
+    return rng.permutation(ids).astype(np.int32)
+
+
+# (r, h_in, h_out, long rows per segment, short rows per segment, short segments):
+#   r = 16, h_in = 8200: 17 GEMV slices (a reduce pass for the short rows) while the long
+#   rows' 4 slices are added by the MFMA expand itself;
+#   r = 32: few GEMV slices summed by the GEMV expand; r = 64: reduce passes on both sides
+GRAPH_MIXED = [(16, 8200, 1032, 520, 3, 9), (32, 1032, 2056, 40, 5, 4), (64, 2056, 1032, 70, 15, 3)]
+
+
+@pytest.mark.parametrize("r,h_in,h_out,n_long,n_short,n_sa", GRAPH_MIXED)
+def test_mixed_batch_graph_equals_eager(torch_cuda, r, h_in, h_out, n_long, n_short, n_sa):
+    torch = torch_cuda
+    from adapter_gemv_amd import sgmv
+    _say(f"[graph mixed] r={r} h_in={h_in} h_out={h_out}")
+    ids = _mixed_ids(n_long, n_short, n_sa, 7 + r)
+    p = synth.random_problem((93, r), n=len(ids), h_in=h_in, h_out=h_out, r=r,
+                             n_adapters=2 + n_sa, dtype="bf16", ids=ids)
+    dp = _upload(p)
+    ws = sgmv.make_workspace(p.n, p.h_in, r, dp.x.device)
+    y_eager = dp.lora_add(workspace=ws)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.nonzero(ids >= 2)[0],
+                           np.random.default_rng(3).choice(np.nonzero(ids < 2)[0], 64, replace=False)])
+    ref = oracle.lora_add(p.y[rows], p.x[rows], p.ids[rows], p.A, p.B, p.scale, p.dtype)
+    _assert_close(_y_f64(y_eager, p.dtype)[rows], ref, f"mixed r={r} eager")
+    y = dp.fresh_y()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dp.lora_add(y, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dp.lora_add(y, workspace=ws)
+    for rep in range(3):
+        y.copy_(dp.y0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _say(f"[graph mixed] r={r} replay {rep}")
+        assert torch.equal(y, y_eager), f"replay {rep} differs from the eager call"
+        _ = (dp.x.float() * 2).sum()
+        torch.cuda.synchronize()
