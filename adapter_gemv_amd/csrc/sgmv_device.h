@@ -151,18 +151,25 @@ __device__ inline float dot8(const uint4& a, const uint4& b, float acc) {
 }
 
 // Sum of ks float slices src[0], src[stride], ... in the one order every table-path kernel
-// uses for split-K slices: four partial sums p_q over slices q, q + 4, q + 8, ... (each
-// from 0, in increasing slice order), then (p0 + p1) + (p2 + p3).  8 loads in flight.
+// uses for split-K slices: four partial sums p_q over slices q, q + 4, q + 8, ... (in
+// increasing slice order), then ((p0 + p1) + (p2 + p3)) + 0.  reduce_v_kernel starts each
+// p_q from +0 instead; the two differ at most in the sign of a zero along the way, which
+// the final + 0 removes, so both give the same bits.  8 loads in flight.
 __device__ inline float sum_slices(const float* __restrict__ src, int64_t stride, int ks) {
-  float p[4] = {0.f, 0.f, 0.f, 0.f};
+  float p[4];
   for (int k0 = 0; k0 < ks; k0 += 8) {
     float v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) v[u] = (k0 + u < ks) ? src[(k0 + u) * stride] : 0.f;
+    if (k0 == 0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) p[u & 3] += v[u];
+      for (int q = 0; q < 4; ++q) p[q] = v[q] + v[q + 4];
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) p[u & 3] += v[u];
+    }
   }
-  return (p[0] + p[1]) + (p[2] + p[3]);
+  return ks > 0 ? ((p[0] + p[1]) + (p[2] + p[3])) + 0.f : 0.f;
 }
 
 }  // namespace sgmv_dev

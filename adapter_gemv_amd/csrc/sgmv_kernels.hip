@@ -805,17 +805,15 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
         const int idx = tid + 256 * u;
         t[k][u] = (k < vks && g0 + idx / R < g1) ? v[k * vslice + static_cast<int64_t>(g0) * R + idx] : 0.f;
       }
-    // the slices' fixed order (sum_slices): partial sums 0 + s_q, then (p0 + p1) + (p2 + p3);
-    // slices past vks are zeros
+    // the slices' fixed order (sum_slices): (s0 + s1) + (s2 + s3), then + 0 (slices past
+    // vks are zeros)
     static_assert(VS == 1 || VS == 4, "slice sum order");
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-      if constexpr (VS == 1) {
+      if constexpr (VS == 1)
         vv[u] = t[0][u];
-      } else {
-        const float p0 = 0.f + t[0][u], p1 = 0.f + t[1][u], p2 = 0.f + t[2][u], p3 = 0.f + t[3][u];
-        vv[u] = (p0 + p1) + (p2 + p3);
-      }
+      else
+        vv[u] = ((t[0][u] + t[1][u]) + (t[2][u] + t[3][u])) + 0.f;
     }
   }
   if (tile_long_segments_pre<TR, 256>(seg_starts, B_ptrs, S, g0, g1, sh, pre) == 0) return;  // uniform
