@@ -39,9 +39,16 @@
  *     16 rows use wavefront-reduction (GEMV) kernels, longer ones MFMA tiles.
  *
  * Memory ownership: every pointer passed to a device call is device memory owned by
- * the caller, except where a comment says "host".  The library allocates nothing,
- * keeps no per-call state and never synchronises: device calls are enqueued on
+ * the caller, except where a comment says "host".  The library allocates no device
+ * memory, keeps no per-call state and never synchronises: device calls are enqueued on
  * `stream` and return.  Calls that share a workspace must be ordered (same stream).
+ * Streams: a fused call (sgmv_lora_add, sgmv_lora_add_ranked, sgmv_lora_add_pool above
+ * 64 rows) whose batch has segments both shorter and longer than 16 rows, made while
+ * `stream` is being captured into a HIP graph, runs its short-segment kernels on a
+ * second stream that the library creates once per device (default priority, on the
+ * first such call that is not captured) and joins it back into `stream` before
+ * returning: the captured graph orders everything after the call exactly as `stream`
+ * alone would, and its two branches overlap on the GPU.  Eager calls use `stream` only.
  *
  * Errors: every argument check is done on the host before any HIP call, so a
  * rejected call has no effect.  The contents of device tables (seg_starts, perm,
