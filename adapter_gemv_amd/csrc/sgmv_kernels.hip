@@ -1160,13 +1160,21 @@ class SideStream {
 
   hipError_t fork(hipStream_t st) {
     lock_ = std::unique_lock<std::mutex>(g_side_mu);
+    // a stream whose device or capture state cannot be queried gets no fork (and the
+    // query's error is cleared, so that it is not taken for a launch error later)
     int dev = 0;
     hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return hipSuccess;
+    }
     if (dev < 0 || dev >= kSideDevices) return hipSuccess;
     SideSlot& slot = g_side[dev];
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if ((e = hipStreamIsCapturing(st, &cap)) != hipSuccess) return e;
+    if (hipStreamIsCapturing(st, &cap) != hipSuccess) {
+      (void)hipGetLastError();
+      return hipSuccess;
+    }
     if (!slot.stream) {
       if (cap != hipStreamCaptureStatusNone) return hipSuccess;
       int cur = 0;
