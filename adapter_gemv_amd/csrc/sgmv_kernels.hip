@@ -299,13 +299,13 @@ __device__ inline int next_run(const TileSegs<ROWS>& sh, int& q) {
   return k;
 }
 
-// Shrink on MFMA 16x16x32 for a tile of r sorted rows and one K chunk (r = 16 and 32).  The x rows are
-// the A operand and the adapter's stored A rows the B operand; lane l supplies row (or
-// column) l%16 and k = k0 + 8*(l/16) .. +7 of each 32-wide k step.  Each of the 4 waves
-// covers all r rows and r columns (r/16 x r/16 accumulator blocks), so A and x are read
-// in equal amounts; the waves take interleaved stages of UN k steps, with the loads of the next
-// stage in flight while the current one is multiplied, and are summed through LDS in a
-// fixed order.  Rows of several long segments in one tile are handled run by run with the
+// Shrink on MFMA 16x16x32 for a tile of r sorted rows and one K chunk (r = 16 and 32).
+// The x rows are the A operand and the adapter's stored A rows the B operand; lane l
+// supplies row (or column) l%16 and k = k0 + 8*(l/16) .. +7 of each 32-wide k step.  Each
+// of the 4 waves covers all r rows and r columns (r/16 x r/16 accumulator blocks), so A
+// and x are read in equal amounts; the waves take interleaved stages of UN k steps, with
+// the loads of the next stage in flight while the current one is multiplied, and are
+// summed through LDS in a fixed order.  Rows of several long segments in one tile are handled run by run with the
 // other rows' x set to zero.  With one chunk per tile v is written directly; otherwise
 // each chunk writes its slice of partial sums and reduce_v_kernel, the next launch, adds
 // the slices in order (no wait on other workgroups inside this kernel).
@@ -951,10 +951,10 @@ inline int gemv_kc(int r) {
 static_assert(GemvCfg<16>::KC == 512 && GemvCfg<32>::KC == 256 && GemvCfg<64>::KC == 256,
               "table_gemv_kc in sgmv_checks.h must match the GEMV shrink's chunk");
 
-// split-K of the MFMA shrink: about TARGET_WGS workgroups (set per rank from measured
-// sweeps on MI355X: fewer, longer chunks win for r = 16, more for r = 64), chunks of at
-// least 256 k, a multiple of 8 chunks where there are 8 or more (XCD-owned chunks), and
-// no more slices than the workspace holds
+// split-K of the MFMA shrinks: about `target` workgroups (set per kernel and rank from
+// measured sweeps on MI355X), chunks of at least 256 k rounded up to `granule`, a multiple
+// of 8 chunks where there are 8 or more before the rounding (XCD-owned chunks), and no
+// more slices than the workspace holds
 inline void split_k(int32_t n, int32_t h_in, int ks_cap, int mt, int target, int granule,
                     int* kcm, int* ks) {
   const int tiles = (n + mt - 1) / mt;

@@ -170,6 +170,10 @@ RAGGED = [
     (300, 1032, 1160, 32, 3, "mixed", 8, False),    # r = 32 tiles, ragged last strip
     (129, 2056, 200, 64, 2, "blocks", 0, False),    # r = 64 tiles, narrow h_out
     (130, 16392, 1032, 16, 3, "mixed", 8, False),   # r = 16, 64-row shrink tiles, ragged
+    (80, 264, 136, 64, 2, "blocks", 0, False),      # r = 64 LDS-staged shrink: one chunk,
+                                                    # v written directly, padded stages
+    (70, 16648, 520, 16, 2, "blocks", 8, False),    # r = 16 LDS-staged shrink, last chunk
+                                                    # padded to a whole ring turn
 ]
 
 
