@@ -149,6 +149,26 @@ inline WsLayout ws_layout(int32_t n, int32_t h_in, int32_t r) {
   return L;
 }
 
+// Rank groups of a mixed-rank call with their scratch side by side (so that their chains
+// can run concurrently): group g (ns[g] rows, rank rs[g]) uses the workspace from
+// offsets[g] on, with the layout ws_layout(ns[g], h_in, rs[g]) relative to it, whose scratch
+// [rowks_off, table_end) then follows the previous group's.  Groups of no rows get the
+// previous offset and no room.  Returns the end of the last group's scratch, which must
+// not pass the buffer's end.
+inline size_t ranked_side_by_side(const int32_t* ns, const int32_t* rs, int count, int32_t h_in,
+                                  size_t* offsets) {
+  size_t off = 0, end = 0;
+  for (int g = 0; g < count; ++g) {
+    off = align_up(off, 256);
+    if (offsets) offsets[g] = off;
+    if (ns[g] <= 0) continue;
+    const WsLayout L = ws_layout(ns[g], h_in, rs[g]);
+    end = off + L.table_end;
+    off += L.table_end - L.rowks_off;
+  }
+  return end;
+}
+
 // The table path on segment tables that live on the device (sgmv_kernels.hip): the
 // tables and their meta word [S, min_len, max_len, n_valid] as written by the device sort;
 // S_max bounds S.

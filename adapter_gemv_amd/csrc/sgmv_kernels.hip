@@ -20,6 +20,7 @@
 #include <cstdint>
 #include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "../../include/sgmv.h"
 #include "sgmv_checks.h"
@@ -1137,29 +1138,34 @@ hipError_t run_expand(hipStream_t st, uint16_t* y, int64_t ld_y, const float* v,
   return hipSuccess;
 }
 
-// A second stream per device for the short-segment chain of a fused call, and the two
-// events that fork it from the caller's stream and join it back.  The fork is taken only
-// while the caller's stream is being captured into a graph: replayed, the two chains
-// overlap; called eagerly, the cross-stream event pair costs more host time than the
-// overlap saves (measured on MI355X), so eager calls run both chains on the caller's
-// stream.  The stream and events are created by the first fused call on a device that is
-// not being captured (a capture before that runs both chains on the caller's stream).
-// One mutex keeps each call's record-wait-launch-record-wait sequence whole when host
-// threads call concurrently.  Default stream priority.
+// Side streams per device for independent chains of launches in a fused call (the
+// short- and long-segment chains of sgmv_lora_add, the rank groups of
+// sgmv_lora_add_ranked), with one event that forks them from the caller's stream and one
+// per stream that joins them back.  Forks are taken only while the caller's stream is
+// being captured into a graph: replayed, the chains overlap; called eagerly, the
+// cross-stream event pairs cost more host time than the overlap saves (measured on
+// MI355X), so eager calls run every chain on the caller's stream.  The streams and events
+// are created by the first fused call on a device that is not being captured (a capture
+// before that runs every chain on the caller's stream).  One mutex keeps each call's
+// record-wait-launch-record-wait sequence whole when host threads call concurrently.
+// Default stream priority.
 constexpr int kSideDevices = 64;
+constexpr int kSideStreams = 4;
 struct SideSlot {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipStream_t stream[kSideStreams] = {};
+  hipEvent_t join[kSideStreams] = {};
+  hipEvent_t fork = nullptr;
 };
 std::mutex g_side_mu;
 SideSlot g_side[kSideDevices];
 
 class SideStream {
  public:
-  hipStream_t stream = nullptr;  // null: no side stream, run everything on the caller's
-
-  hipError_t fork(hipStream_t st) {
+  // Up to `want` side streams forked from st; count() of them are available (0: eager
+  // call, capture before the streams exist, or a stream that cannot be queried).
+  hipError_t fork(hipStream_t st, int want = 1) {
     lock_ = std::unique_lock<std::mutex>(g_side_mu);
+    if (want <= 0) return hipSuccess;
     // a stream whose device or capture state cannot be queried gets no fork (and the
     // query's error is cleared, so that it is not taken for a launch error later)
     int dev = 0;
@@ -1175,41 +1181,56 @@ class SideStream {
       (void)hipGetLastError();
       return hipSuccess;
     }
-    if (!slot.stream) {
+    if (!slot.fork) {
       if (cap != hipStreamCaptureStatusNone) return hipSuccess;
       int cur = 0;
       if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
       if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
       SideSlot made;
-      e = hipStreamCreateWithFlags(&made.stream, hipStreamNonBlocking);
+      for (int i = 0; i < kSideStreams && e == hipSuccess; ++i) {
+        e = hipStreamCreateWithFlags(&made.stream[i], hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&made.join[i], hipEventDisableTiming);
+      }
       if (e == hipSuccess) e = hipEventCreateWithFlags(&made.fork, hipEventDisableTiming);
-      if (e == hipSuccess) e = hipEventCreateWithFlags(&made.join, hipEventDisableTiming);
       if (cur != dev) hipSetDevice(cur);
       if (e != hipSuccess) return e;
       slot = made;
     }
     if (cap != hipStreamCaptureStatusActive) return hipSuccess;
+    const int k = want < kSideStreams ? want : kSideStreams;
     if ((e = hipEventRecord(slot.fork, st)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(slot.stream, slot.fork, 0)) != hipSuccess) return e;
     slot_ = &slot;
-    stream = slot.stream;
+    for (int i = 0; i < k; ++i) {
+      if ((e = hipStreamWaitEvent(slot.stream[i], slot.fork, 0)) != hipSuccess) return e;
+      n_ = i + 1;  // joined back even if a later wait fails
+    }
     return hipSuccess;
   }
 
+  int count() const { return n_; }
+  hipStream_t stream(int i) const { return slot_->stream[i % n_]; }
+
   hipError_t join(hipStream_t st) {
     hipError_t e = hipSuccess;
-    if (slot_) {
-      e = hipEventRecord(slot_->join, slot_->stream);
-      if (e == hipSuccess) e = hipStreamWaitEvent(st, slot_->join, 0);
-      slot_ = nullptr;
+    for (int i = 0; i < n_; ++i) {
+      hipError_t ei = hipEventRecord(slot_->join[i], slot_->stream[i]);
+      if (ei == hipSuccess) ei = hipStreamWaitEvent(st, slot_->join[i], 0);
+      if (e == hipSuccess) e = ei;
     }
+    n_ = 0;
+    slot_ = nullptr;
     if (lock_.owns_lock()) lock_.unlock();
     return e;
+  }
+
+  ~SideStream() {
+    if (lock_.owns_lock()) lock_.unlock();
   }
 
  private:
   std::unique_lock<std::mutex> lock_;
   SideSlot* slot_ = nullptr;
+  int n_ = 0;
 };
 
 // The short segments of a fused call (decode rows: GEMV kernels) and its long segments
@@ -1265,10 +1286,13 @@ hipError_t run_lora_add(hipStream_t st, uint16_t* y, int64_t ld_y, const uint16_
     return run_long_chain<DT, R>(st, y, ld_y, x, ld_x, TA, TB, h_in, h_out, scale, L, ws);
   }
   SideStream side;
-  hipError_t e = side.fork(st);
-  if (e != hipSuccess) return e;
-  if (side.stream) {
-    e = run_short_chain<DT, R>(side.stream, y, ld_y, x, ld_x, TA, TB, h_in, h_out, scale, L, ws);
+  hipError_t e = side.fork(st, 1);
+  if (e != hipSuccess) {
+    side.join(st);
+    return e;
+  }
+  if (side.count() > 0) {
+    e = run_short_chain<DT, R>(side.stream(0), y, ld_y, x, ld_x, TA, TB, h_in, h_out, scale, L, ws);
     const hipError_t e2 =
         run_long_chain<DT, R>(st, y, ld_y, x, ld_x, TA, TB, h_in, h_out, scale, L, ws);
     const hipError_t e3 = side.join(st);
@@ -1316,6 +1340,16 @@ template <int DT, int R>
 struct ExpandOp {
   template <typename... A>
   static hipError_t run(A... a) { return run_expand<DT, R>(a...); }
+};
+template <int DT, int R>
+struct ShortChainOp {
+  template <typename... A>
+  static hipError_t run(A... a) { return run_short_chain<DT, R>(a...); }
+};
+template <int DT, int R>
+struct LongChainOp {
+  template <typename... A>
+  static hipError_t run(A... a) { return run_long_chain<DT, R>(a...); }
 };
 template <int DT, int R>
 struct LoraOp {
@@ -1461,19 +1495,68 @@ extern "C" int sgmv_lora_add_ranked(hipStream_t stream, int32_t dtype, void* y, 
       (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return SGMV_ERR_WORKSPACE;
   if ((st = check_device())) return st;
+  auto tables = [&](const sgmv_rank_group& G, const void* const* P) {
+    return Tables{reinterpret_cast<const uint16_t* const*>(P) + G.seg0, seg_starts + G.starts0,
+                  perm + G.row0, G.n, G.n_segments, G.min_seg_len, G.max_seg_len};
+  };
+  // The groups touch disjoint rows.  Under graph capture, with room for every group's
+  // scratch side by side in the workspace, each group's short and long chains run on
+  // streams of their own and all of them overlap; otherwise the groups run one after
+  // another (each as sgmv_lora_add, whose own chains overlap under capture).
+  int chains = 0;
+  std::vector<int32_t> gn(n_groups), gr(n_groups);
+  std::vector<size_t> goff(n_groups);
+  for (int32_t g = 0; g < n_groups; ++g) {
+    const sgmv_rank_group& G = groups[g];
+    gn[g] = G.n;
+    gr[g] = G.r;
+    if (G.n > 0) chains += (G.min_seg_len < kLongMin) + (G.max_seg_len >= kLongMin);
+  }
+  const bool fits =
+      ranked_side_by_side(gn.data(), gr.data(), n_groups, h_in, goff.data()) <= workspace_bytes;
+  SideStream side;
+  if (fits && chains > 1) {
+    if (side.fork(stream, chains - 1) != hipSuccess) {
+      side.join(stream);
+      return SGMV_ERR_HIP;
+    }
+  }
+  if (side.count() > 0) {
+    hipError_t e = hipSuccess;
+    int k = 0;
+    for (int32_t g = 0; g < n_groups; ++g) {
+      const sgmv_rank_group& G = groups[g];
+      if (G.n == 0) continue;
+      const Tables TA = tables(G, A_ptrs), TB = tables(G, B_ptrs);
+      const WsLayout L = ws_layout(G.n, h_in, G.r);
+      char* ws = static_cast<char*>(workspace) + goff[g];
+      const bool kinds[2] = {TA.min_len < kLongMin, TA.max_len >= kLongMin};
+      for (int c = 0; c < 2; ++c) {
+        if (!kinds[c]) continue;
+        const hipStream_t s = (k == 0) ? stream : side.stream(k - 1);
+        ++k;
+        const hipError_t ec =
+            c == 0 ? dispatch<ShortChainOp>(dtype, G.r, s, static_cast<uint16_t*>(y), ld_y,
+                                            static_cast<const uint16_t*>(x), ld_x, TA, TB, h_in,
+                                            h_out, G.scale, L, ws)
+                   : dispatch<LongChainOp>(dtype, G.r, s, static_cast<uint16_t*>(y), ld_y,
+                                           static_cast<const uint16_t*>(x), ld_x, TA, TB, h_in,
+                                           h_out, G.scale, L, ws);
+        if (e == hipSuccess) e = ec;
+      }
+    }
+    const hipError_t ej = side.join(stream);
+    return (e == hipSuccess && ej == hipSuccess) ? SGMV_OK : SGMV_ERR_HIP;
+  }
+  side.join(stream);
   for (int32_t g = 0; g < n_groups; ++g) {
     const sgmv_rank_group& G = groups[g];
     if (G.n == 0) continue;
-    const auto A = reinterpret_cast<const uint16_t* const*>(A_ptrs) + G.seg0;
-    const auto B = reinterpret_cast<const uint16_t* const*>(B_ptrs) + G.seg0;
-    const Tables TA{A, seg_starts + G.starts0, perm + G.row0, G.n, G.n_segments, G.min_seg_len,
-                    G.max_seg_len};
-    const Tables TB{B, seg_starts + G.starts0, perm + G.row0, G.n, G.n_segments, G.min_seg_len,
-                    G.max_seg_len};
     const WsLayout L = ws_layout(G.n, h_in, G.r);
     const hipError_t e = dispatch<LoraOp>(dtype, G.r, stream, static_cast<uint16_t*>(y), ld_y,
-                                          static_cast<const uint16_t*>(x), ld_x, TA, TB, h_in,
-                                          h_out, G.scale, L, static_cast<char*>(workspace));
+                                          static_cast<const uint16_t*>(x), ld_x,
+                                          tables(G, A_ptrs), tables(G, B_ptrs), h_in, h_out,
+                                          G.scale, L, static_cast<char*>(workspace));
     if (e != hipSuccess) return SGMV_ERR_HIP;
   }
   return SGMV_OK;

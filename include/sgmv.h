@@ -209,8 +209,12 @@ int sgmv_lora_add(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
 /*
  * Fused LoRA add-on for a mixed-rank batch: for every group g of `groups` (host array,
  * as written by sgmv_build_segments_ranked, with the scales filled in), the rows of g get
- * y[t] += g.scale * (x[t] @ A[a_t]) @ B[a_t] with A[a_t] of g.r columns.  The groups run
- * one after another on `stream`, each as sgmv_lora_add on its part of the tables:
+ * y[t] += g.scale * (x[t] @ A[a_t]) @ B[a_t] with A[a_t] of g.r columns.  Called eagerly,
+ * the groups run one after another on `stream`, each as sgmv_lora_add on its part of the
+ * tables.  Captured into a graph, with a workspace that holds every group's scratch side
+ * by side (a buffer of sgmv_workspace_bytes(n, h_in, largest r) does), each
+ * group's short- and long-segment kernels run on streams of their own, forked from and
+ * joined back into `stream` (see "Streams" above), and overlap:
  *   A_ptrs, B_ptrs  device per-segment pointer tables over all groups' segments
  *   seg_starts      device int32: the builder's seg_starts array
  *   perm            device int32[n]: the builder's perm (required)

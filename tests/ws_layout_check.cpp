@@ -1,8 +1,10 @@
 // Host check of the workspace layout rule: in a buffer sized for the largest of a set of
 // shapes, no call of any smaller shape writes scratch over the tagged partials of any
 // other such call (the counters sit at a fixed place before all scratch), and every
-// region stays inside the buffer.  Built and run by
+// region stays inside the buffer; and the rank groups of a mixed-rank call fit side by
+// side in the buffer sized for all their rows at the largest rank.  Built and run by
 // tests/test_host_abi.py; prints "ok" and exits 0 when the rule holds.
+#include <algorithm>
 #include <cstdio>
 #include <vector>
 
@@ -52,6 +54,44 @@ int main() {
             }
           }
         }
+      }
+  // mixed-rank calls: in a buffer sized for all rows at the largest rank (as the Python
+  // binding allocates), the groups' scratch fits side by side, each group's scratch starts
+  // after the counters and after the previous group's, and none passes the buffer's end
+  const std::vector<int> Ns = {2, 65, 300, 2112, 4096};
+  for (int N : Ns)
+    for (int H : hs)
+      for (int R : rs) {
+        const size_t W = ws_layout(N, H, R).total;
+        for (int parts = 2; parts <= 3; ++parts)
+          for (int cut = 1; cut < 8; ++cut) {
+            int32_t gn[3], gr[3];
+            size_t off[3];
+            int left = N;
+            for (int g = 0; g < parts; ++g) {
+              gn[g] = (g == parts - 1) ? left : std::min(left, (N * cut) / (8 * (parts - 1)) + g);
+              left -= gn[g];
+              gr[g] = rs[(g + cut) % rs.size()];
+              if (gr[g] > R) gr[g] = R;
+            }
+            const size_t end = ranked_side_by_side(gn, gr, parts, H, off);
+            ++checks;
+            if (end > W) {
+              std::printf("ranked: groups of %d rows (H %d, R %d, %d parts, cut %d) need %zu > %zu\n",
+                          N, H, R, parts, cut, end, W);
+              return 1;
+            }
+            size_t prev_end = front_zero_end;
+            for (int g = 0; g < parts; ++g) {
+              if (gn[g] <= 0) continue;
+              const WsLayout L = ws_layout(gn[g], H, gr[g]);
+              if (off[g] % 256 != 0 || off[g] + L.rowks_off < prev_end) {
+                std::printf("ranked: group %d overlaps (N %d, H %d, R %d)\n", g, N, H, R);
+                return 1;
+              }
+              prev_end = off[g] + L.table_end;
+            }
+          }
       }
   std::printf("ok %ld\n", checks);
   return 0;
