@@ -710,10 +710,14 @@ constexpr int kExpandSlices = 4;
 
 template <int R>
 struct ExpCfg {
-  // rows and columns per tile (TC/4 columns per wave); measured on MI355X
-  static constexpr int TR = (R == 32) ? 64 : 32;
+  // rows per pass and columns per tile (TC/4 columns per wave); measured on MI355X
+  static constexpr int TRP = 32;
   static constexpr int TC = (R == 32) ? 128 : 256;
-  static constexpr int RB = TR / 16, CB = TC / 64;  // 16 x 16 blocks per wave
+  // passes over the tile's rows, one after another with the same B registers: B is read
+  // once for PASSES * TRP rows
+  static constexpr int PASSES = 2;
+  static constexpr int TR = TRP * PASSES;            // rows per tile
+  static constexpr int RB = TRP / 16, CB = TC / 64;  // 16 x 16 blocks per wave and pass
   // waves per SIMD the register budget is set for (five spill at r = 64)
   static constexpr int WAVES_PER_SIMD = (R == 64) ? 4 : 5;
 };
@@ -749,7 +753,7 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
   if (meta && meta[2] < kLongMin) return;  // no long segment at all
   using E = Elem<DT>;
   using C = ExpCfg<R>;
-  constexpr int TR = C::TR, TC = C::TC, RB = C::RB, CB = C::CB;
+  constexpr int TR = C::TR, TRP = C::TRP, TC = C::TC, RB = C::RB, CB = C::CB;
   constexpr int KT = 2 * R;          // k of the hi/lo product
   constexpr int NK = KT / 32;        // MFMA k-steps
   constexpr int NKU = (R >= 32) ? R / 32 : 1;  // distinct B loads per column block
@@ -784,19 +788,22 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
   if (tid < TR) s_prow[tid] = (g0 + tid < g1) ? (perm ? perm[g0 + tid] : g0 + tid) : -1;
   if (tid == 0) sh.nseg = 0;
   __syncthreads();
-  // y in the products' layout: lane (kq, l16) holds row 16rb + l16, columns
-  // wc + 32p + 8kq .. +7
+  // y in the products' layout: lane (kq, l16) holds row ro + 16rb + l16 of the pass that
+  // starts at tile row ro, columns wc + 32p + 8kq .. +7
   uint4 yv[RB][CB / 2];
   int yrow[RB];
+  auto load_y = [&](int ro) {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    yrow[rb] = s_prow[16 * rb + l16];
+    for (int rb = 0; rb < RB; ++rb) {
+      yrow[rb] = s_prow[ro + 16 * rb + l16];
 #pragma unroll
-    for (int p = 0; p < CB / 2; ++p) {
-      const int col = wc + 32 * p + 8 * kq;
-      yv[rb][p] = (yrow[rb] >= 0 && col < h_out) ? ld16(y + static_cast<int64_t>(yrow[rb]) * ld_y + col) : zero4();
+      for (int p = 0; p < CB / 2; ++p) {
+        const int col = wc + 32 * p + 8 * kq;
+        yv[rb][p] = (yrow[rb] >= 0 && col < h_out) ? ld16(y + static_cast<int64_t>(yrow[rb]) * ld_y + col) : zero4();
+      }
     }
-  }
+  };
+  load_y(0);
   float vv[VPT];
   {
     float t[VS][VPT];
@@ -825,7 +832,7 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
   // c; the product's k runs over the hi halves, then the lo halves, so the k-steps past r
   // reuse the same B bytes: only NKU = r / 32 distinct loads per column block.
   int q = 0;
-  int sg = next_run(sh, q);  // the tile meets a long segment, so there is a first run
+  const int sg = next_run(sh, q);  // the tile meets a long segment, so there is a first run
   uint4 bop[CB][NKU];
   exp_load_b<R, CB, NKU>(global_ptr(sh.ptr[sg]), wc, l16, kq, h_out, bop);
 
@@ -849,55 +856,66 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
   }
   __syncthreads();
 
-  int rs[RB];
+  int cur = sg;  // the run whose B is in bop
+  for (int pass = 0; pass < C::PASSES; ++pass) {
+    const int ro = pass * TRP;
+    if (pass > 0) load_y(ro);
+    int rs[RB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) rs[rb] = sh.rseg[16 * rb + l16];
-  f32x4_t acc[RB][CB];
+    for (int rb = 0; rb < RB; ++rb) rs[rb] = sh.rseg[ro + 16 * rb + l16];
+    f32x4_t acc[RB][CB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // the long segments of the tile, in increasing order (the reads are uniform)
-  for (;;) {
+      for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // the long runs that meet this pass's rows, in increasing order (the reads are uniform)
+    for (int qq = ro;;) {
+      while (qq < ro + TRP && sh.rseg[qq] < 0) ++qq;
+      if (qq >= ro + TRP) break;
+      const int run = sh.rseg[qq];
+      while (qq < ro + TRP && sh.rseg[qq] == run) ++qq;
+      if (run != cur) {
+        exp_load_b<R, CB, NKU>(global_ptr(sh.ptr[run]), wc, l16, kq, h_out, bop);
+        cur = run;
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int lq = ro + 16 * rb + l16;
+        uint4 vop[NK];
+#pragma unroll
+        for (int s = 0; s < NK; ++s)
+          vop[s] = (rs[rb] == run) ? *reinterpret_cast<const uint4*>(&vlds[lq][32 * s + 8 * kq]) : zero4();
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int s = 0; s < NK; ++s) acc[rb][cb] = E::mfma(bop[cb][s % NKU], vop[s], acc[rb][cb]);
+      }
+    }
+    // y + sum, rounded once, straight from the accumulators: lane (kq, l16) owns 16 bytes
+    // of row ro + 16rb + l16 per block pair
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const int lq = 16 * rb + l16;
-      uint4 vop[NK];
+      if (rs[rb] < 0) continue;
+      if constexpr (DT == SGMV_F16) {
+        const int ex = s_exp[ro + 16 * rb + l16];
 #pragma unroll
-      for (int s = 0; s < NK; ++s)
-        vop[s] = (rs[rb] == sg) ? *reinterpret_cast<const uint4*>(&vlds[lq][32 * s + 8 * kq]) : zero4();
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
+          for (int i = 0; i < 4; ++i) acc[rb][cb][i] = ldexpf(acc[rb][cb][i], ex);
+      }
 #pragma unroll
-        for (int s = 0; s < NK; ++s) acc[rb][cb] = E::mfma(bop[cb][s % NKU], vop[s], acc[rb][cb]);
-    }
-    if ((sg = next_run(sh, q)) < 0) break;
-    exp_load_b<R, CB, NKU>(global_ptr(sh.ptr[sg]), wc, l16, kq, h_out, bop);
-  }
-  // y + sum, rounded once, straight from the accumulators: lane (kq, l16) owns 16 bytes
-  // of row 16rb + l16 per block pair
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    if (rs[rb] < 0) continue;
-    if constexpr (DT == SGMV_F16) {
-      const int ex = s_exp[16 * rb + l16];
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[rb][cb][i] = ldexpf(acc[rb][cb][i], ex);
-    }
-#pragma unroll
-    for (int p = 0; p < CB / 2; ++p) {
-      const int col = wc + 32 * p + 8 * kq;
-      if (col >= h_out) continue;
-      const f32x4_t d0 = acc[rb][2 * p], d1 = acc[rb][2 * p + 1];
-      const uint4 yy = yv[rb][p];
-      uint4 o;
-      o.x = E::pack(E::lo(yy.x) + d0[0], E::hi(yy.x) + d0[1]);
-      o.y = E::pack(E::lo(yy.y) + d0[2], E::hi(yy.y) + d0[3]);
-      o.z = E::pack(E::lo(yy.z) + d1[0], E::hi(yy.z) + d1[1]);
-      o.w = E::pack(E::lo(yy.w) + d1[2], E::hi(yy.w) + d1[3]);
-      *reinterpret_cast<uint4*>(y + static_cast<int64_t>(yrow[rb]) * ld_y + col) = o;
+      for (int p = 0; p < CB / 2; ++p) {
+        const int col = wc + 32 * p + 8 * kq;
+        if (col >= h_out) continue;
+        const f32x4_t d0 = acc[rb][2 * p], d1 = acc[rb][2 * p + 1];
+        const uint4 yy = yv[rb][p];
+        uint4 o;
+        o.x = E::pack(E::lo(yy.x) + d0[0], E::hi(yy.x) + d0[1]);
+        o.y = E::pack(E::lo(yy.y) + d0[2], E::hi(yy.y) + d0[3]);
+        o.z = E::pack(E::lo(yy.z) + d1[0], E::hi(yy.z) + d1[1]);
+        o.w = E::pack(E::lo(yy.w) + d1[2], E::hi(yy.w) + d1[3]);
+        *reinterpret_cast<uint4*>(y + static_cast<int64_t>(yrow[rb]) * ld_y + col) = o;
+      }
     }
   }
 }
