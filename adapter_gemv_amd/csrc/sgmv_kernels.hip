@@ -40,16 +40,19 @@ enum ReduceRows : int32_t { kReduceAll = 0, kReduceShort = 1, kReduceLong = 2 };
 // ------------------------------------------------------------------------------------
 // GEMV path (segments with 1 .. kShortMax rows)
 // ------------------------------------------------------------------------------------
-// Lane (j, g) of a wave reads row j of A[a] (= column j of A) over its own contiguous
-// run of 8*KV k values, so the only cross-lane sum is over the G = 64/R lanes that
-// share j.  Four waves cover consecutive k ranges and are summed through LDS.
+// A wave covers WAVE_K values of k in 64-k segments.  Lane (t0 = lane / 8, c = lane % 8)
+// reads 16 bytes (k values 8c .. 8c + 7 of a segment) of rows t0, t0 + 8, t0 + 16, ... of
+// A[a]: one load instruction covers 8 rows × 128 contiguous bytes, whole cache lines.
+// The same 16 bytes of a token row's x serve all of the lane's A rows.  The 8 lanes of a
+// row add their partial sums by shuffles; four waves cover consecutive k ranges and are
+// summed through LDS.
 template <int R>
 struct GemvCfg {
-  static constexpr int G = 64 / R;               // k groups per wave
-  static constexpr int KV = (R == 64) ? 8 : 4;   // 16-byte vectors per lane and row
-  static constexpr int WAVE_K = G * 8 * KV;      // k values per wave
-  static constexpr int KC = 4 * WAVE_K;          // k values per workgroup (split-K chunk)
-  static constexpr int MR = 16 / KV;             // token rows loaded per pass
+  static constexpr int WAVE_K = (R == 16) ? 128 : 64;  // k values per wave
+  static constexpr int KC = 4 * WAVE_K;                // k values per workgroup (split-K chunk)
+  static constexpr int SEG = WAVE_K / 64;              // 64-k segments per wave
+  static constexpr int RT = R / 8;                     // A rows per lane
+  static constexpr int MR = 4;                         // token rows loaded per pass
 };
 
 template <int DT, int R>
@@ -72,37 +75,50 @@ __global__ __launch_bounds__(256) void shrink_gemv_kernel(
   const int m = seg_starts[s + 1] - seg0;
   if (m <= 0 || m >= kLongMin) continue;  // uniform
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int j = lane % R, g = lane / R;
-  const int kbase = kc * C::KC + w * C::WAVE_K + g * 8 * C::KV;
+  const int t0 = lane >> 3, c = lane & 7;
+  const int kbase = kc * C::KC + w * C::WAVE_K + 8 * c;
 
-  const gptr<const uint16_t> Arow = global_ptr(A_ptrs[s]) + static_cast<int64_t>(j) * h_in;
-  uint4 a[C::KV];
+  const gptr<const uint16_t> Ab = global_ptr(A_ptrs[s]) + static_cast<int64_t>(t0) * h_in;
+  uint4 a[C::SEG][C::RT];
 #pragma unroll
-  for (int v = 0; v < C::KV; ++v) {
-    const int k = kbase + 8 * v;
-    a[v] = (k < h_in) ? ld16(Arow + k) : zero4();
+  for (int sk = 0; sk < C::SEG; ++sk) {
+    const int k = kbase + 64 * sk;
+#pragma unroll
+    for (int t = 0; t < C::RT; ++t)
+      a[sk][t] = (k < h_in) ? ld16(Ab + static_cast<int64_t>(8 * t) * h_in + k) : zero4();
   }
   for (int i0 = 0; i0 < m; i0 += C::MR) {
-    uint4 xv[C::MR][C::KV];
+    uint4 xv[C::MR][C::SEG];
 #pragma unroll
     for (int r = 0; r < C::MR; ++r) {
       const int i = i0 + r;
       gptr<const uint16_t> xr = nullptr;
       if (i < m) xr = global_ptr(x) + static_cast<int64_t>(perm ? perm[seg0 + i] : seg0 + i) * ld_x;
 #pragma unroll
-      for (int v = 0; v < C::KV; ++v) {
-        const int k = kbase + 8 * v;
-        xv[r][v] = (xr && k < h_in) ? ld16(xr + k) : zero4();
+      for (int sk = 0; sk < C::SEG; ++sk) {
+        const int k = kbase + 64 * sk;
+        xv[r][sk] = (xr && k < h_in) ? ld16(xr + k) : zero4();
       }
     }
 #pragma unroll
     for (int r = 0; r < C::MR; ++r) {
-      float acc = 0.f;
+      float acc[C::RT];
 #pragma unroll
-      for (int v = 0; v < C::KV; ++v) acc = dot8<DT>(xv[r][v], a[v], acc);
+      for (int t = 0; t < C::RT; ++t) {
+        acc[t] = 0.f;
 #pragma unroll
-      for (int msk = R; msk < 64; msk <<= 1) acc += __shfl_xor(acc, msk);
-      if (g == 0 && i0 + r < m) red[w][i0 + r][j] = acc;
+        for (int sk = 0; sk < C::SEG; ++sk) acc[t] = dot8<DT>(xv[r][sk], a[sk][t], acc[t]);
+        // the 8 lanes of row 8t + t0, in a fixed butterfly
+#pragma unroll
+        for (int msk = 1; msk < 8; msk <<= 1) acc[t] += __shfl_xor(acc[t], msk);
+      }
+      // lane (t0, c) stores row 8c + t0 (every lane of the row holds its sum)
+      if (i0 + r < m && c < C::RT) {
+        float mine = acc[0];
+#pragma unroll
+        for (int t = 1; t < C::RT; ++t) mine = (c == t) ? acc[t] : mine;
+        red[w][i0 + r][8 * c + t0] = mine;
+      }
     }
   }
   __syncthreads();
@@ -1226,6 +1242,24 @@ class SideStream {
   }
 
   int count() const { return n_; }
+
+  // whether a fork from st would be taken now: st's device has its side streams and st is
+  // being captured
+  static bool ready(hipStream_t st) {
+    std::lock_guard<std::mutex> g(g_side_mu);
+    int dev = 0;
+    if ((st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev)) != hipSuccess) {
+      (void)hipGetLastError();
+      return false;
+    }
+    if (dev < 0 || dev >= kSideDevices || !g_side[dev].fork) return false;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cap) != hipSuccess) {
+      (void)hipGetLastError();
+      return false;
+    }
+    return cap == hipStreamCaptureStatusActive;
+  }
   hipStream_t stream(int i) const { return slot_->stream[i % n_]; }
 
   hipError_t join(hipStream_t st) {
@@ -1275,14 +1309,13 @@ hipError_t run_short_chain(hipStream_t st, uint16_t* y, int64_t ld_y, const uint
   return launch_expand_short<DT, R>(st, y, ld_y, part, L.slice, ksg, TB, h_out, scale);
 }
 
+// the long chain after its shrink (which left ksl slices)
 template <int DT, int R>
-hipError_t run_long_chain(hipStream_t st, uint16_t* y, int64_t ld_y, const uint16_t* x,
-                          int64_t ld_x, const Tables& TA, const Tables& TB, int32_t h_in,
-                          int32_t h_out, float scale, const WsLayout& L, char* ws) {
-  int ksl = 0;
+hipError_t run_long_tail(hipStream_t st, uint16_t* y, int64_t ld_y, const Tables& TA,
+                         const Tables& TB, int32_t h_out, float scale, const WsLayout& L,
+                         char* ws, int ksl) {
+  hipError_t e;
   float* v_long = reinterpret_cast<float*>(ws + L.v_off);
-  hipError_t e = launch_shrink_long<DT, R>(st, x, ld_x, TA, h_in, L, ws, v_long, &ksl);
-  if (e != hipSuccess) return e;
   const float* part = reinterpret_cast<const float*>(ws + L.part_off);
   // a few slices are added by the MFMA expand itself (r <= 32); more are summed once per row
   if (ksl > 1 && (ksl > kExpandSlices || R > 32)) {
@@ -1294,6 +1327,27 @@ hipError_t run_long_chain(hipStream_t st, uint16_t* y, int64_t ld_y, const uint1
 }
 
 template <int DT, int R>
+hipError_t run_long_chain(hipStream_t st, uint16_t* y, int64_t ld_y, const uint16_t* x,
+                          int64_t ld_x, const Tables& TA, const Tables& TB, int32_t h_in,
+                          int32_t h_out, float scale, const WsLayout& L, char* ws) {
+  int ksl = 0;
+  float* v_long = reinterpret_cast<float*>(ws + L.v_off);
+  const hipError_t e = launch_shrink_long<DT, R>(st, x, ld_x, TA, h_in, L, ws, v_long, &ksl);
+  if (e != hipSuccess) return e;
+  return run_long_tail<DT, R>(st, y, ld_y, TA, TB, h_out, scale, L, ws, ksl);
+}
+
+// Where the short chain starts under capture.  Started with the long chain, the GEMV
+// shrink (which reads every short segment's A) competes with the long shrink for memory;
+// forked after the long shrink, it overlaps the long chain's reduce and expand instead.
+// Measured on MI355X (70B mixed batch, graph replay), the later start wins only at r = 64
+// with h_in > h_out and a wide expand (down projection 116 -> 107 us); elsewhere the
+// early start is as fast or faster (r = 64 k/v 48 vs 52 us, r = 16 down 71 vs 75 us).
+inline bool short_after_long_shrink(int r, int32_t h_in, int32_t h_out) {
+  return r == 64 && h_in > h_out && h_out >= 4096;
+}
+
+template <int DT, int R>
 hipError_t run_lora_add(hipStream_t st, uint16_t* y, int64_t ld_y, const uint16_t* x, int64_t ld_x,
                         const Tables& TA, const Tables& TB, int32_t h_in, int32_t h_out, float scale,
                         const WsLayout& L, char* ws) {
@@ -1302,6 +1356,22 @@ hipError_t run_lora_add(hipStream_t st, uint16_t* y, int64_t ld_y, const uint16_
     if (TA.use_gemv())
       return run_short_chain<DT, R>(st, y, ld_y, x, ld_x, TA, TB, h_in, h_out, scale, L, ws);
     return run_long_chain<DT, R>(st, y, ld_y, x, ld_x, TA, TB, h_in, h_out, scale, L, ws);
+  }
+  if (short_after_long_shrink(R, h_in, h_out) && SideStream::ready(st)) {
+    // the long shrink first; the short chain, forked after it, overlaps the long chain's
+    // reduce and expand instead of competing with its shrink
+    int ksl = 0;
+    float* v_long = reinterpret_cast<float*>(ws + L.v_off);
+    hipError_t e = launch_shrink_long<DT, R>(st, x, ld_x, TA, h_in, L, ws, v_long, &ksl);
+    if (e != hipSuccess) return e;
+    SideStream side;
+    e = side.fork(st, 1);
+    const hipStream_t ss = (e == hipSuccess && side.count() > 0) ? side.stream(0) : st;
+    const hipError_t e1 =
+        run_short_chain<DT, R>(ss, y, ld_y, x, ld_x, TA, TB, h_in, h_out, scale, L, ws);
+    const hipError_t e2 = run_long_tail<DT, R>(st, y, ld_y, TA, TB, h_out, scale, L, ws, ksl);
+    const hipError_t e3 = side.join(st);
+    return e != hipSuccess ? e : (e1 != hipSuccess ? e1 : (e2 != hipSuccess ? e2 : e3));
   }
   SideStream side;
   hipError_t e = side.fork(st, 1);
