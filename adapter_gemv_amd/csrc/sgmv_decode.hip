@@ -538,9 +538,10 @@ __device__ inline uint64_t load_partial(const uint64_t* q) {
 }
 
 // shrink item: partial v over k in [kc*KC, (kc+1)*KC) for the adapter's rows within
-// one block of 16 caller rows (blk).  MFMA 16x16x32; lane l supplies MFMA row/column
-// l%16 and the k group l/16, reading its own contiguous 8*U-element run of k for both
-// operands.
+// one block of 16 caller rows (blk).  MFMA 16x16x32; in k step u, lane l supplies MFMA
+// row/column l%16 with k values 32u + 8(l/16) .. +7 of both operands, so one load
+// instruction reads 64 contiguous bytes of each of 16 rows and two consecutive steps
+// fill whole cache lines.
 template <int DT, int R>
 __device__ inline void shrink_item(const PoolArgs& p, const Leader& L, int blk, int kc) {
   using E = Elem<DT>;
@@ -550,13 +551,13 @@ __device__ inline void shrink_item(const PoolArgs& p, const Leader& L, int blk, 
   const int lane = threadIdx.x & 63;
   const int mrow = lane & 15, kq = lane >> 4;
   const gptr<const uint16_t> A = global_ptr(p.A) + static_cast<int64_t>(L.a) * p.A_stride;
-  const int kbase = kc * KC + kq * 8 * U;
+  const int kbase = kc * KC + kq * 8;
   uint4 av[NB][U];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int kk = kbase + 8 * u;
+      const int kk = kbase + 32 * u;
       av[nb][u] = (kk < p.h_in) ? ld16(A + static_cast<int64_t>(nb * 16 + mrow) * p.h_in + kk)
                                 : zero4();
     }
@@ -568,7 +569,7 @@ __device__ inline void shrink_item(const PoolArgs& p, const Leader& L, int blk, 
   uint4 xv[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int kk = kbase + 8 * u;
+    const int kk = kbase + 32 * u;
     xv[u] = (xr && kk < p.h_in) ? ld16(xr + kk) : zero4();
   }
   f32x4_t acc[NB];
