@@ -47,6 +47,9 @@ SIGNATURES = {
     "sgmv_build_segments_device": (ctypes.c_int, [_p, _p, _i32, _i32, _p, _p, _p, _p]),
     "sgmv_lora_add_pool": (ctypes.c_int, [_p, _i32, _p, _i64, _p, _i64, _p, _i32, _p, _i64, _p,
                                           _i64, _i32, _i32, _i32, _i32, ctypes.c_float, _p, _sz]),
+    "sgmv_lora_add_host_ids": (ctypes.c_int, [_p, _i32, _p, _i64, _p, _i64, _p, _i32, _p, _i64,
+                                              _p, _i64, _i32, _i32, _i32, _i32, ctypes.c_float,
+                                              _p, _sz]),
 }
 
 

@@ -697,10 +697,10 @@ __device__ inline void expand_item(const PoolArgs& p, const Leader& L, int r, in
 // (caller row r = i % n, column chunk i / n), kItemsPerWg items per workgroup (one per
 // wave).
 // Every shrink item an expand item waits for sits in a lower-numbered workgroup.
+// The kernel body, given lane's adapter id (the id of caller row `lane`, -1 past n).
 template <int DT, int R>
-__global__ __launch_bounds__(64 * kItemsPerWg) void lora_add_pool_kernel(PoolArgs p) {
+__device__ inline void pool_items(const PoolArgs& p, int id) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int id = lane < p.n ? p.ids[lane] : -1;
   const int n_shrink = p.n * p.KS;
   const int shrink_wgs = (n_shrink + kItemsPerWg - 1) / kItemsPerWg;
   const int b = blockIdx.x;
@@ -734,11 +734,41 @@ __global__ __launch_bounds__(64 * kItemsPerWg) void lora_add_pool_kernel(PoolArg
   }
 }
 
+// Adapter ids in device memory: every wave starts with one coalesced load of them.
+template <int DT, int R>
+__global__ __launch_bounds__(64 * kItemsPerWg) void lora_add_pool_kernel(PoolArgs p) {
+  const int lane = threadIdx.x & 63;
+  pool_items<DT, R>(p, lane < p.n ? p.ids[lane] : -1);
+}
+
+// Adapter ids carried in the kernel arguments (checked on the host before the launch).
+// They reach the waves with the rest of the arguments, so the loads of A and B are the
+// first memory accesses that depend on them: no global load of the ids precedes them.
+struct PoolIds {
+  int32_t id[kPoolMaxN];
+};
+
+template <int DT, int R>
+__global__ __launch_bounds__(64 * kItemsPerWg) void lora_add_ids_kernel(PoolArgs p, PoolIds ids) {
+  const int lane = threadIdx.x & 63;
+  const int raw = ids.id[lane];  // every lane loads: the load need not wait for p.n
+  pool_items<DT, R>(p, lane < p.n ? raw : -1);
+}
+
 template <int DT, int R>
 hipError_t launch_pool(hipStream_t st, const PoolArgs& p) {
   const int grid = (p.n * p.KS + kItemsPerWg - 1) / kItemsPerWg +
                    (p.n * p.NS + kItemsPerWg - 1) / kItemsPerWg;
   hipLaunchKernelGGL((lora_add_pool_kernel<DT, R>), dim3(grid), dim3(64 * kItemsPerWg), 0, st, p);
+  return hipGetLastError();
+}
+
+template <int DT, int R>
+hipError_t launch_ids(hipStream_t st, const PoolArgs& p, const PoolIds& ids) {
+  const int grid = (p.n * p.KS + kItemsPerWg - 1) / kItemsPerWg +
+                   (p.n * p.NS + kItemsPerWg - 1) / kItemsPerWg;
+  hipLaunchKernelGGL((lora_add_ids_kernel<DT, R>), dim3(grid), dim3(64 * kItemsPerWg), 0, st, p,
+                     ids);
   return hipGetLastError();
 }
 
@@ -770,12 +800,13 @@ extern "C" int sgmv_build_segments_device(hipStream_t stream, const int32_t* ada
   return hip_status(hipGetLastError());
 }
 
-extern "C" int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
-                                  const void* x, int64_t ld_x, const int32_t* adapter_ids,
-                                  int32_t n, const void* A_pool, int64_t A_stride,
-                                  const void* B_pool, int64_t B_stride, int32_t n_adapters,
-                                  int32_t h_in, int32_t h_out, int32_t r, float scale,
-                                  void* workspace, size_t workspace_bytes) {
+namespace {
+
+// Host checks shared by the pool entry points (no HIP call).
+int check_pool_call(int32_t dtype, void* y, int64_t ld_y, const void* x, int64_t ld_x,
+                    const int32_t* adapter_ids, int32_t n, const void* A_pool, int64_t A_stride,
+                    const void* B_pool, int64_t B_stride, int32_t n_adapters, int32_t h_in,
+                    int32_t h_out, int32_t r, void* workspace, size_t workspace_bytes) {
   if (dtype != SGMV_F16 && dtype != SGMV_BF16) return SGMV_ERR_UNSUPPORTED;
   if (!rank_ok(r)) return SGMV_ERR_UNSUPPORTED;
   if (n < 0 || n > kDevSortMax || n_adapters <= 0 || n_adapters > (1 << 24)) return SGMV_ERR_SHAPE;
@@ -794,6 +825,49 @@ extern "C" int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, in
   if (!workspace || workspace_bytes < sgmv_workspace_bytes(n, h_in, r) ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return SGMV_ERR_WORKSPACE;
+  return SGMV_OK;
+}
+
+// Arguments of the one-launch kernels (n <= 64).
+PoolArgs pool_args(void* y, int64_t ld_y, const void* x, int64_t ld_x, const int32_t* adapter_ids,
+                   int32_t n, const void* A_pool, int64_t A_stride, const void* B_pool,
+                   int64_t B_stride, int32_t n_adapters, int32_t h_in, int32_t h_out, int32_t r,
+                   float scale, void* workspace, size_t workspace_bytes) {
+  PoolArgs p;
+  p.y = static_cast<uint16_t*>(y);
+  p.x = static_cast<const uint16_t*>(x);
+  p.ids = adapter_ids;
+  p.A = static_cast<const uint16_t*>(A_pool);
+  p.B = static_cast<const uint16_t*>(B_pool);
+  p.ld_y = ld_y;
+  p.ld_x = ld_x;
+  p.A_stride = A_stride;
+  p.B_stride = B_stride;
+  p.n = n;
+  p.n_adapters = n_adapters;
+  p.h_in = h_in;
+  p.h_out = h_out;
+  p.KS = (h_in + pool_kc(r) - 1) / pool_kc(r);
+  p.NS = (h_out + pool_kc(r) - 1) / pool_kc(r);  // 64 lanes x 128/r columns per item
+  p.scale = scale;
+  char* ws = static_cast<char*>(workspace);
+  p.ws_flag = reinterpret_cast<int32_t*>(ws);
+  p.counters = reinterpret_cast<int32_t*>(ws + kWsPoolCounters);
+  p.part = reinterpret_cast<uint64_t*>(ws + pool_offset(workspace_bytes, h_in, r));
+  return p;
+}
+
+}  // namespace
+
+extern "C" int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
+                                  const void* x, int64_t ld_x, const int32_t* adapter_ids,
+                                  int32_t n, const void* A_pool, int64_t A_stride,
+                                  const void* B_pool, int64_t B_stride, int32_t n_adapters,
+                                  int32_t h_in, int32_t h_out, int32_t r, float scale,
+                                  void* workspace, size_t workspace_bytes) {
+  int st = check_pool_call(dtype, y, ld_y, x, ld_x, adapter_ids, n, A_pool, A_stride, B_pool,
+                           B_stride, n_adapters, h_in, h_out, r, workspace, workspace_bytes);
+  if (st || n == 0) return st;
   if ((st = check_device())) return st;
 
   if (n > kPoolMaxN) {
@@ -827,28 +901,9 @@ extern "C" int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, in
         h_in, h_out, scale, workspace));
   }
 
-  PoolArgs p;
-  p.y = static_cast<uint16_t*>(y);
-  p.x = static_cast<const uint16_t*>(x);
-  p.ids = adapter_ids;
-  p.A = static_cast<const uint16_t*>(A_pool);
-  p.B = static_cast<const uint16_t*>(B_pool);
-  p.ld_y = ld_y;
-  p.ld_x = ld_x;
-  p.A_stride = A_stride;
-  p.B_stride = B_stride;
-  p.n = n;
-  p.n_adapters = n_adapters;
-  p.h_in = h_in;
-  p.h_out = h_out;
-  p.KS = (h_in + pool_kc(r) - 1) / pool_kc(r);
-  p.NS = (h_out + pool_kc(r) - 1) / pool_kc(r);  // 64 lanes x 128/r columns per item
-  p.scale = scale;
-  char* ws = static_cast<char*>(workspace);
-  p.ws_flag = reinterpret_cast<int32_t*>(ws);
-  p.counters = reinterpret_cast<int32_t*>(ws + kWsPoolCounters);
-  p.part = reinterpret_cast<uint64_t*>(ws + pool_offset(workspace_bytes, h_in, r));
-
+  const PoolArgs p = pool_args(y, ld_y, x, ld_x, adapter_ids, n, A_pool, A_stride, B_pool,
+                               B_stride, n_adapters, h_in, h_out, r, scale, workspace,
+                               workspace_bytes);
   hipError_t e;
   if (dtype == SGMV_F16) {
     e = (r == 16) ? launch_pool<SGMV_F16, 16>(stream, p)
@@ -856,6 +911,38 @@ extern "C" int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, in
   } else {
     e = (r == 16) ? launch_pool<SGMV_BF16, 16>(stream, p)
         : (r == 32) ? launch_pool<SGMV_BF16, 32>(stream, p) : launch_pool<SGMV_BF16, 64>(stream, p);
+  }
+  return hip_status(e);
+}
+
+extern "C" int sgmv_lora_add_host_ids(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
+                                      const void* x, int64_t ld_x, const int32_t* adapter_ids,
+                                      int32_t n, const void* A_pool, int64_t A_stride,
+                                      const void* B_pool, int64_t B_stride, int32_t n_adapters,
+                                      int32_t h_in, int32_t h_out, int32_t r, float scale,
+                                      void* workspace, size_t workspace_bytes) {
+  if (n > kPoolMaxN) return SGMV_ERR_SHAPE;
+  int st = check_pool_call(dtype, y, ld_y, x, ld_x, adapter_ids, n, A_pool, A_stride, B_pool,
+                           B_stride, n_adapters, h_in, h_out, r, workspace, workspace_bytes);
+  if (st || n == 0) return st;
+  PoolIds ids;
+  for (int i = 0; i < kPoolMaxN; ++i) {
+    if (i < n && (adapter_ids[i] < 0 || adapter_ids[i] >= n_adapters)) return SGMV_ERR_ADAPTER_ID;
+    ids.id[i] = i < n ? adapter_ids[i] : -1;
+  }
+  if ((st = check_device())) return st;
+  // the kernel reads no id from memory: the device pointer stays unused
+  const PoolArgs p = pool_args(y, ld_y, x, ld_x, nullptr, n, A_pool, A_stride, B_pool, B_stride,
+                               n_adapters, h_in, h_out, r, scale, workspace, workspace_bytes);
+  hipError_t e;
+  if (dtype == SGMV_F16) {
+    e = (r == 16) ? launch_ids<SGMV_F16, 16>(stream, p, ids)
+        : (r == 32) ? launch_ids<SGMV_F16, 32>(stream, p, ids)
+                    : launch_ids<SGMV_F16, 64>(stream, p, ids);
+  } else {
+    e = (r == 16) ? launch_ids<SGMV_BF16, 16>(stream, p, ids)
+        : (r == 32) ? launch_ids<SGMV_BF16, 32>(stream, p, ids)
+                    : launch_ids<SGMV_BF16, 64>(stream, p, ids);
   }
   return hip_status(e);
 }

@@ -69,6 +69,13 @@ class DeviceProblem:
                            self.scale if scale is None else scale, workspace)
         return y
 
+    def lora_add_host_ids(self, y=None, workspace=None, scale=None, ids=None):
+        """The host-id decode path (n <= 64, ids in the launch's kernel arguments)."""
+        y = self.fresh_y() if y is None else y
+        sgmv.lora_add_host_ids(y, self.x, self.ids if ids is None else ids, self.A, self.B,
+                               self.scale if scale is None else scale, workspace)
+        return y
+
     def shrink(self, workspace=None):
         return sgmv.shrink(self.x, self.batch, workspace=workspace)
 

@@ -448,6 +448,16 @@ def sgmv_lora_add_pool(stream, dtype, y, ld_y, x, ld_x, adapter_ids, n, A_pool, 
                                          float(scale), workspace, workspace_bytes)
 
 
+def sgmv_lora_add_host_ids(stream, dtype, y, ld_y, x, ld_x, adapter_ids, n, A_pool, A_stride,
+                           B_pool, B_stride, n_adapters, h_in, h_out, r, scale, workspace,
+                           workspace_bytes) -> int:
+    """``adapter_ids`` is a HOST address (int32[n], n <= 64)."""
+    return _lib.lib().sgmv_lora_add_host_ids(stream, dtype, y, ld_y, x, ld_x, adapter_ids, n,
+                                             A_pool, A_stride, B_pool, B_stride, n_adapters,
+                                             h_in, h_out, r, float(scale), workspace,
+                                             workspace_bytes)
+
+
 DECODE_MAX_TOKENS = 64   # one-launch decode kernel
 POOL_MAX_TOKENS = 4096   # device-side segment sort, then the table kernels
 
@@ -492,4 +502,30 @@ def lora_add_pool(y, x, ids, A_pool, B_pool, scale: float, workspace=None, strea
                             int(A_pool.shape[0]), x.shape[1], y.shape[1], r, scale,
                             workspace.data_ptr(), workspace.numel())
     check(st, "sgmv_lora_add_pool")
+    return y
+
+
+def lora_add_host_ids(y, x, ids, A_pool, B_pool, scale: float, workspace=None, stream=None):
+    """y[t] += scale * (x[t] @ A_pool[ids[t]]) @ B_pool[ids[t]] for a decode batch (n <= 64)
+    whose adapter ids are on the host: one launch, the ids travel in its kernel arguments.
+
+    ``ids`` is a host int32 array or CPU tensor [n]; the pools are as for lora_add_pool."""
+    ids_np = np.ascontiguousarray(
+        ids.numpy() if hasattr(ids, "numpy") else np.asarray(ids), dtype=np.int32)
+    n = int(x.shape[0])
+    _check_rows(x, n, "x")
+    _check_rows(y, n, "y")
+    if ids_np.ndim != 1 or ids_np.shape[0] != n:
+        raise ValueError("ids must be a host int32 array [n]")
+    r = int(A_pool.shape[1])
+    _check_adapters([A_pool[0]], [B_pool[0]], r, int(x.shape[1]), int(y.shape[1]),
+                    int(A_pool.shape[0]), int(B_pool.shape[0]))
+    if workspace is None:
+        workspace = make_workspace(n, x.shape[1], r, x.device)
+    st = sgmv_lora_add_host_ids(_stream_handle(stream), dtype_code(y), y.data_ptr(), y.stride(0),
+                                x.data_ptr(), x.stride(0), _ptr(ids_np), n, A_pool.data_ptr(),
+                                A_pool.stride(0), B_pool.data_ptr(), B_pool.stride(0),
+                                int(A_pool.shape[0]), x.shape[1], y.shape[1], r, scale,
+                                workspace.data_ptr(), workspace.numel())
+    check(st, "sgmv_lora_add_host_ids")
     return y

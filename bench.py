@@ -88,6 +88,14 @@ def kernel_source_hash() -> str:
 # --------------------------------------------------------------------------------------
 # CPU oracle baseline
 # --------------------------------------------------------------------------------------
+def cpu_baseline_1thread(p, budget_s: float) -> dict:
+    """The same oracle timing with the BLAS pool limited to one thread."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1, user_api="blas"):
+        out = cpu_baseline(p, budget_s)
+    return out
+
+
 def cpu_baseline(p, budget_s: float = 12.0):
     import oracle
     from threadpoolctl import threadpool_info
@@ -153,6 +161,7 @@ class Rig:
         self.dtype_code = sgmv.dtype_code(self.x)
         self.ld_x, self.ld_y = p.h_in, p.h_out
         self.pool_path = p.n <= sgmv.DECODE_MAX_TOKENS
+        self.host_ids = False
         # table path: metadata staging ring (pinned host -> device)
         self.A_bases = sgmv.adapter_bases(self.A)
         self.B_bases = sgmv.adapter_bases(self.B)
@@ -166,7 +175,29 @@ class Rig:
 
     def step(self, k: int, ev=None):
         """One step on slot k.  ``ev`` = (start, end) events bracket the SGMV call."""
+        if self.host_ids:
+            return self.step_host_ids(k, ev)
         return self.step_pool(k, ev) if self.pool_path else self.step_table(k, ev)
+
+    def step_host_ids(self, k: int, ev=None):
+        """Shrink and expand in one launch, the batch's adapter ids (host memory) carried
+        in the kernel arguments."""
+        import torch
+        from adapter_gemv_amd import sgmv
+        p = self.p
+        slot = k % self.slots
+        stream = torch.cuda.current_stream()
+        if ev is not None:
+            ev[0].record(stream)
+        st = sgmv.sgmv_lora_add_host_ids(
+            stream.cuda_stream, self.dtype_code, self.y[slot].data_ptr(), self.ld_y,
+            self.x[slot].data_ptr(), self.ld_x, self.ids[slot].ctypes.data, p.n,
+            self.A.data_ptr(), self.A.stride(0), self.B.data_ptr(), self.B.stride(0),
+            self.n_pool, p.h_in, p.h_out, p.r, p.scale, self.ws.data_ptr(), self.ws.numel())
+        if ev is not None:
+            ev[1].record(stream)
+        if st != 0:
+            raise RuntimeError(f"sgmv_lora_add_host_ids failed: {sgmv.sgmv_status_string(st)}")
 
     def step_pool(self, k: int, ev=None):
         """Segment metadata, shrink and expand in one launch (device-resident ids)."""
@@ -228,17 +259,18 @@ class Rig:
         self.ring_evt[i] = e
 
 
-def kernel_pass(rig, k0: int, count: int) -> float:
+def kernel_pass(rig, k0: int, count: int, fixed_slot=None) -> float:
     """Average duration of sgmv_lora_add alone on the table path: the segment tables of
     `count` steps are built and uploaded first, the calls are captured in one HIP graph
-    and the replay is bracketed by HIP events."""
+    and the replay is bracketed by HIP events.  ``fixed_slot``: every call on that slot
+    (warm caches) instead of rotating."""
     import torch
     from adapter_gemv_amd import sgmv
     p = rig.p
     calls = []
     keep = []
     for k in range(count):
-        slot = (k0 + k) % rig.slots
+        slot = (k0 + k) % rig.slots if fixed_slot is None else fixed_slot
         b = sgmv.Batch.build(rig.ids[slot], rig.A, rig.B)
         keep.append(b)
         calls.append((slot, b))
@@ -273,6 +305,63 @@ def kernel_pass(rig, k0: int, count: int) -> float:
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e-3 / count
+
+
+def graph_time(body, count: int) -> float:
+    """Average time of one `body(k)` call, k = 0 .. count-1 captured in one HIP graph:
+    one untimed replay, then one replay bracketed by HIP events."""
+    import torch
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        body(0)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k in range(count):
+            body(k)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e-3 / count
+
+
+def warm_call_time(rig, steps: int, use_graph: bool) -> float:
+    """The SGMV call with warm caches: every call on the same slot (slot 1, not the
+    parity slot), so its operands stay in the L2s and the Infinity Cache."""
+    if use_graph:
+        return graph_time(lambda k: rig.step(1), steps)
+    return kernel_pass(rig, 1, min(steps, 500), fixed_slot=1)
+
+
+def floors(nbytes: int, device, count: int) -> dict:
+    """Reference floors on this GPU: a plain device copy moving the call's algorithmic
+    bytes (half read, half written), cache-cold over > 1 GiB of rotating buffers, and
+    one launch of a one-element kernel, both replayed from a HIP graph."""
+    import torch
+    half = max(1, nbytes // 4)                      # fp16 elements per copy side
+    slots = max(2, min(256, -(-ROTATION_BYTES // (4 * half))))
+    src = torch.ones((slots, half), dtype=torch.float16, device=device)
+    dst = torch.empty_like(src)
+    t_copy = graph_time(lambda k: dst[k % slots].copy_(src[k % slots]), count)
+    one = torch.zeros(1, dtype=torch.float32, device=device)
+    t_launch = graph_time(lambda k: one.add_(1.0), count)
+    del src, dst
+    torch.cuda.empty_cache()
+    moved = 4 * half
+    return {"copy_same_bytes": {"bytes": moved, "us": round(t_copy * 1e6, 3),
+                                "gbs": round(moved / t_copy / 1e9, 1),
+                                "how": "torch device copy, rotating slots over > 1 GiB, "
+                                       "graph replay"},
+            "launch_us": round(t_launch * 1e6, 3),
+            "launch_how": "one-element torch add, graph replay"}
 
 
 def parity_check(rig):
@@ -314,7 +403,7 @@ def load_traffic(workload: str, pool_path: bool):
 
 
 def measure(p, device, steps: int, warmup: int, eager: bool = False, force_table: bool = False,
-            force_device: bool = False):
+            force_device: bool = False, host_ids: bool = False):
     """Check slot 0 against the oracle, then time `steps` steps after `warmup` untimed
     ones: wall time per step, GPU time per step, and the SGMV call's average duration."""
     import torch
@@ -326,6 +415,10 @@ def measure(p, device, steps: int, warmup: int, eager: bool = False, force_table
         if p.n > sgmv.POOL_MAX_TOKENS:
             raise SystemExit(f"--path device takes at most {sgmv.POOL_MAX_TOKENS} tokens")
         rig.pool_path = True
+    if host_ids:
+        if p.n > sgmv.DECODE_MAX_TOKENS:
+            raise SystemExit(f"--path host takes at most {sgmv.DECODE_MAX_TOKENS} tokens")
+        rig.host_ids = True
     parity = parity_check(rig)
     print(f"# {p.name}: slots={rig.slots} pool_path={rig.pool_path} parity={parity}",
           file=sys.stderr, flush=True)
@@ -377,8 +470,10 @@ def measure(p, device, steps: int, warmup: int, eager: bool = False, force_table
         call_s = kernel_pass(rig, base + steps, min(steps, 500))
         call_how = "HIP events over a graph of the same calls (tables pre-uploaded) / count"
     flag = int(rig.ws[:4].view(torch.int32).item())
+    warm_s = warm_call_time(rig, steps, use_graph)
+    flag = max(flag, int(rig.ws[:4].view(torch.int32).item()))
     return dict(rig=rig, parity=parity, use_graph=use_graph, wall=wall, gpu_step=gpu_step,
-                call_s=call_s, call_how=call_how, flag=flag)
+                call_s=call_s, call_how=call_how, flag=flag, warm_s=warm_s)
 
 
 def layer_measure(p, device, steps: int) -> dict:
@@ -722,10 +817,11 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="decode7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", choices=["auto", "table", "device"], default="auto",
+    ap.add_argument("--path", choices=["auto", "table", "device", "host"], default="auto",
                     help="auto: one-launch path for batches of <= 64 tokens, host-built tables "
                          "above; device: device ids for any batch up to 4096 tokens "
-                         "(device sort + table kernels, graph-captured); table: host tables")
+                         "(device sort + table kernels, graph-captured); table: host tables; "
+                         "host: one launch with the host ids in its kernel arguments (<= 64)")
     ap.add_argument("--eager", action="store_true", help="no HIP graph on the one-launch path")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--sweep", choices=sorted(SWEEPS),
@@ -771,7 +867,8 @@ def main(argv=None) -> int:
 
     p = workload_problem(args.workload)
     m = measure(p, device, args.steps, args.warmup, eager=args.eager,
-                force_table=args.path == "table", force_device=args.path == "device")
+                force_table=args.path == "table", force_device=args.path == "device",
+                host_ids=args.path == "host")
     rig, parity, use_graph = m["rig"], m["parity"], m["use_graph"]
     wall, gpu_step, call_s, call_how, flag = (m["wall"], m["gpu_step"], m["call_s"],
                                               m["call_how"], m["flag"])
@@ -779,7 +876,10 @@ def main(argv=None) -> int:
     nbytes = algorithmic_bytes(p)
     flops = algorithmic_flops(p)
     traffic = load_traffic(args.workload, rig.pool_path and p.n <= 64) if args.path != "device" or p.n <= 64 else None
-    if rig.pool_path and p.n <= 64:
+    if rig.host_ids:
+        kernel = "lora_add_ids_kernel (one launch per call, ids in the kernel arguments)"
+        traffic = None
+    elif rig.pool_path and p.n <= 64:
         kernel = "lora_add_pool_kernel (one launch per call)"
     elif rig.pool_path:
         kernel = "sgmv_lora_add_pool: device segment sort + table kernels (all launches of one call)"
@@ -803,7 +903,11 @@ def main(argv=None) -> int:
             "distinct_adapters": p.distinct_adapters(), "adapter_pool": p.n_adapters,
             "scale": p.scale, "rotation_slots": rig.slots,
             "rotation_bytes": rig.slots * nbytes, "cache": "cold (rotating slots)",
-            "step": (("sgmv_lora_add_pool: device segment sort + shrink + expand, one launch"
+            "step": ("sgmv_lora_add_host_ids: host ids in the kernel arguments, grouping + "
+                     "shrink + expand in one launch" +
+                     (", K steps replayed from one HIP graph" if use_graph else ", eager"))
+                    if rig.host_ids else
+                    (("sgmv_lora_add_pool: device segment sort + shrink + expand, one launch"
                       if p.n <= 64 else
                       "sgmv_lora_add_pool: device segment sort, then the table kernels") +
                      (", K steps replayed from one HIP graph" if use_graph else ", eager"))
@@ -825,12 +929,17 @@ def main(argv=None) -> int:
             "kernel": kernel,
             "mfma_frac": round(flops / call_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
         },
+        "warm": {"us_per_call": round(m["warm_s"] * 1e6, 3),
+                 "gbs": round(nbytes / m["warm_s"] / 1e9, 1),
+                 "how": "every call on one slot (operands cached), same timing as us_per_call"},
+        "floors": floors(nbytes, device, min(args.steps, 500)),
         "parity": parity,
         "workspace_flag_after": flag,
         "kernel_source_sha256_16": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_budget)
+        out["cpu_baseline_1thread"] = cpu_baseline_1thread(p, args.cpu_budget / 2)
     print(json.dumps(out), flush=True)
     return 0 if parity["ok"] else 1
 

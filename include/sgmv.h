@@ -277,6 +277,27 @@ int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
                        int64_t B_stride, int32_t n_adapters, int32_t h_in, int32_t h_out,
                        int32_t r, float scale, void* workspace, size_t workspace_bytes);
 
+/*
+ * Fused LoRA add-on for a decode batch of at most 64 tokens whose adapter ids are in
+ * HOST memory (the scheduler that forms the batch knows them), adapters in pools,
+ * y[t] += scale * (x[t] @ A[a_t]) @ B[a_t] (project overview, "How It Works"; paper
+ * summary, "Summary" and idea I2: the rows of one adapter are grouped inside the
+ * launch, as in sgmv_lora_add_pool).  The ids are checked on the host and copied into
+ * the kernel's arguments, so they reach the GPU with the launch itself: no separate
+ * upload, and no load of the ids ahead of the adapter fetches.  One kernel launch.
+ *   adapter_ids  HOST int32[n], each in [0, n_adapters), read before the call returns
+ *   n            0 <= n <= 64
+ * Every other argument, the result and the workspace are as for sgmv_lora_add_pool
+ * (ids outside [0, n_adapters) are rejected on the host with SGMV_ERR_ADAPTER_ID, so no
+ * row is skipped).  A graph that captures the call replays it with the ids it had when
+ * captured.  Returns SGMV_ERR_SHAPE for n > 64.
+ */
+int sgmv_lora_add_host_ids(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
+                           const void* x, int64_t ld_x, const int32_t* adapter_ids, int32_t n,
+                           const void* A_pool, int64_t A_stride, const void* B_pool,
+                           int64_t B_stride, int32_t n_adapters, int32_t h_in, int32_t h_out,
+                           int32_t r, float scale, void* workspace, size_t workspace_bytes);
+
 #ifdef __cplusplus
 }
 #endif

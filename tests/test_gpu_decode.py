@@ -445,3 +445,104 @@ def test_pool_large_hip_graph_replay(torch_cuda):
         _ = (dp.x.float() * 2).sum()
         torch.cuda.synchronize()
     assert int(ws[:16640].view(torch.int32).abs().sum().item()) == 0
+
+
+# ------------------------------------------------------------------------------------
+# host ids in the kernel arguments (sgmv_lora_add_host_ids)
+# ------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name", DECODE)
+def test_host_ids_decode_workloads(torch_cuda, name):
+    _say(f"[host-id parity] {name}")
+    p = FACT[name]()
+    dp = _upload(p)
+    y = dp.lora_add_host_ids()
+    y_dev = dp.lora_add_pool()
+    torch_cuda.cuda.synchronize()
+    _assert_close(oracle.decode(_storage(y, p.dtype), p.dtype), oracle.lora_add_problem(p), name)
+    # the same kernel body as the device-id path: the same bits
+    assert torch_cuda.equal(y, y_dev)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("r", [16, 32, 64])
+@pytest.mark.parametrize("n,P,kind", [(1, 3, "u"), (64, 5, "u"), (47, 40, "zipf")])
+def test_host_ids_exact_bit_exact(torch_cuda, dtype, r, n, P, kind):
+    _say(f"[host-id exact] n={n} P={P} r={r} {dtype}")
+    rng = np.random.default_rng(n * 100 + r + 7)
+    ids = {"u": rng.integers(0, P, n), "zipf": synth.truncated_zipf_ids(rng, n, P, 1.2)}[kind]
+    p = synth.exact_problem((91, n, r), n=n, h_in=2056, h_out=1544, r=r, n_adapters=P,
+                            dtype=dtype, ids=ids.astype(np.int32))
+    y = _upload(p).lora_add_host_ids()
+    torch_cuda.cuda.synchronize()
+    want = oracle.round_io(oracle.lora_add_problem(p), dtype).view(np.uint16)
+    assert np.array_equal(_storage(y, dtype).view(np.uint16), want)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_host_ids_gather_probe(torch_cuda, dtype):
+    _say(f"[host-id gather] {dtype}")
+    rng = np.random.default_rng(17)
+    ids = rng.integers(0, 6, 50).astype(np.int32)
+    p = synth.gather_probe((92,), n=50, h_in=512, h_out=384, r=16, n_adapters=6, dtype=dtype,
+                           ids=ids)
+    y = _upload(p).lora_add_host_ids()
+    torch_cuda.cuda.synchronize()
+    want = oracle.round_io(oracle.lora_add_problem(p), dtype).view(np.uint16)
+    assert np.array_equal(_storage(y, dtype).view(np.uint16), want)
+
+
+@pytest.mark.parametrize("n,h_in,h_out,r", [(33, 200, 136, 16), (17, 24, 4104, 64),
+                                            (60, 28672, 8192, 16)])
+def test_host_ids_ragged(torch_cuda, n, h_in, h_out, r):
+    _say(f"[host-id ragged] n={n} {h_in}x{h_out} r={r}")
+    p = synth.random_problem((93, n, h_in, h_out), n=n, h_in=h_in, h_out=h_out, r=r,
+                             n_adapters=7, dtype="bf16", id_dist="zipf", zipf_s=1.1, scale=1.25)
+    y = _upload(p).lora_add_host_ids()
+    torch_cuda.cuda.synchronize()
+    _assert_close(oracle.decode(_storage(y, "bf16"), "bf16"), oracle.lora_add_problem(p),
+                  f"host-id ragged n={n} {h_in}x{h_out} r={r}")
+
+
+def test_host_ids_graph_replay_and_shared_workspace(torch_cuda):
+    """Calls captured with different host ids replay with the ids they were captured with,
+    every replay equal to eager; the workspace is shared with the device-id path and left
+    at zero."""
+    torch = torch_cuda
+    from adapter_gemv_amd import sgmv
+    p = FACT["decode7b"]()
+    dp = _upload(p)
+    ws = sgmv.make_workspace(p.n, p.h_in, 16, dp.x.device)
+    rng = np.random.default_rng(6)
+    id_sets = [rng.permutation(32).astype(np.int32) for _ in range(3)]
+    ref = [dp.fresh_y() for _ in range(3)]
+    for k in range(3):
+        sgmv.lora_add_pool(ref[k], dp.x, torch.as_tensor(id_sets[k], device="cuda"), dp.A, dp.B,
+                           p.scale, ws)
+    torch.cuda.synchronize()
+    ys = [dp.fresh_y() for _ in range(3)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for k in range(3):
+            sgmv.lora_add_host_ids(dp.fresh_y(), dp.x, id_sets[k], dp.A, dp.B, p.scale, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k in range(3):
+            sgmv.lora_add_host_ids(ys[k], dp.x, id_sets[k], dp.A, dp.B, p.scale, ws)
+    id_sets[0][:] = 0  # the captured call keeps the ids it was captured with
+    for rep in range(3):
+        for k in range(3):
+            ys[k].copy_(dp.y0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in range(3):
+            assert torch.equal(ys[k], ref[k]), f"replay {rep} call {k}"
+        _ = (dp.x.float() * 2).sum()
+        torch.cuda.synchronize()
+    assert int(ws[:16640].view(torch.int32).abs().sum().item()) == 0
+    ks = -(-p.h_in // (8192 // 16))
+    tail = 8 * ks * 64 * 16 + 256
+    assert int(ws[-tail:].view(torch.int32).abs().sum().item()) == 0

@@ -244,6 +244,50 @@ def test_lora_add_pool_rejects(name, kw, code):
     assert _pool(**kw) == code
 
 
+HOST_IDS = np.arange(64, dtype=np.int32)
+
+
+def _host_ids(**kw):
+    a = dict(stream=None, dtype=0, y=Y, ld_y=4096, x=X, ld_x=4096,
+             adapter_ids=HOST_IDS.ctypes.data, n=32, A_pool=V, A_stride=16 * 4096,
+             B_pool=V + (1 << 30), B_stride=16 * 4096, n_adapters=4096, h_in=4096, h_out=4096,
+             r=16, scale=2.0, workspace=WS, workspace_bytes=1 << 30)
+    a.update(kw)
+    return sgmv.sgmv_lora_add_host_ids(**a)
+
+
+BAD_IDS = np.array([0, 1, 4096, 2], dtype=np.int32)
+NEG_IDS = np.array([0, -1], dtype=np.int32)
+HOST_ID_REJECTS = [
+    ("n>64", dict(n=65), _lib.ERR_SHAPE),
+    ("n<0", dict(n=-1), _lib.ERR_SHAPE),
+    ("rank", dict(r=8), _lib.ERR_UNSUPPORTED),
+    ("dtype", dict(dtype=7), _lib.ERR_UNSUPPORTED),
+    ("A_stride small", dict(A_stride=16 * 4096 - 8), _lib.ERR_SHAPE),
+    ("ids null", dict(adapter_ids=None), _lib.ERR_NULL),
+    ("pool misaligned", dict(B_pool=V + 8), _lib.ERR_ALIGNMENT),
+    ("ws small", dict(workspace_bytes=1024), _lib.ERR_WORKSPACE),
+    ("alias", dict(y=X + 64), _lib.ERR_ALIAS),
+    ("id too large", dict(adapter_ids=BAD_IDS.ctypes.data, n=4), _lib.ERR_ADAPTER_ID),
+    ("id negative", dict(adapter_ids=NEG_IDS.ctypes.data, n=2), _lib.ERR_ADAPTER_ID),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", HOST_ID_REJECTS, ids=[r[0] for r in HOST_ID_REJECTS])
+def test_lora_add_host_ids_rejects(name, kw, code):
+    assert _host_ids(**kw) == code
+
+
+def test_lora_add_host_ids_n_zero_is_ok():
+    assert _host_ids(n=0) == _lib.OK
+
+
+@pytest.mark.skipif(not _no_gpu_visible(), reason="needs a machine without a GPU: the fake "
+                    "addresses would reach a kernel")
+def test_lora_add_host_ids_valid_call_without_device_is_hip_error():
+    assert _host_ids() == _lib.ERR_HIP
+
+
 def test_build_segments_device_rejects():
     L = _lib.lib()
     assert L.sgmv_build_segments_device(None, TAB, 4097, 4, V, V, V, V) == _lib.ERR_SHAPE
