@@ -718,9 +718,29 @@ __global__ __launch_bounds__(256) void shrink_lds_kernel(
 // faster than the squarer 64 x 128 tiles.
 //
 // Workgroup b runs on XCD b % 8 (round-robin dispatch).  Each XCD owns a contiguous range
-// of column strips, so its L2 holds only that part of every B[a]; within the range the
-// workgroups go row tile by row tile, so the y traffic in flight at any time covers whole
-// rows of a few consecutive tiles.
+// of column strips (and, when the strips are few, a contiguous range of the row tiles), so
+// its L2 holds only that part of every B[a]; within its share the workgroups go row tile
+// by row tile, so the y traffic in flight at any time covers whole rows of a few
+// consecutive tiles.
+// The 8 XCDs split the (strip, tile) grid as xs strip groups times 8 / xs tile groups.
+// xs = 8 (each XCD a contiguous range of strips over all tiles) unless another split
+// gives the busiest XCD fewer tiles to do: with fewer than 8 strips (h_out < 2048 at
+// r = 16) or a strip count that 8 does not divide, whole XCDs would otherwise idle or
+// finish early (for h_out = 1024, four of the eight).
+inline int expand_strip_groups(int strips, int tiles) {
+  int best = kXcds;
+  int64_t best_load = -1;
+  for (int xs = kXcds; xs >= 1; xs /= 2) {
+    const int xt = kXcds / xs;
+    const int64_t load = static_cast<int64_t>((strips + xs - 1) / xs) * ((tiles + xt - 1) / xt);
+    if (best_load < 0 || load < best_load) {
+      best_load = load;
+      best = xs;
+    }
+  }
+  return best;
+}
+
 // split-K slices of long rows that the MFMA expand adds itself (above: reduce_v_kernel)
 constexpr int kExpandSlices = 4;
 
@@ -764,7 +784,7 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
     uint16_t* __restrict__ y, int64_t ld_y, const float* __restrict__ v, int64_t vslice, int32_t vks,
     const uint16_t* const* __restrict__ B_ptrs, const int32_t* __restrict__ seg_starts,
     int32_t S_host, const int32_t* __restrict__ perm, int32_t n, int32_t h_out, float scale,
-    int32_t tiles, int32_t strips, const int32_t* __restrict__ meta) {
+    int32_t tiles, int32_t strips, int32_t xs, const int32_t* __restrict__ meta) {
   const int S = meta ? meta[0] : S_host;
   if (meta && meta[2] < kLongMin) return;  // no long segment at all
   using E = Elem<DT>;
@@ -782,14 +802,19 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
   __shared__ __attribute__((aligned(16))) uint16_t vlds[TR][KT + 8];
   __shared__ int s_exp[TR];  // fp16: the row's sums are multiplied by 2^s_exp[row]
 
-  // XCD x owns strips [sx0, sx1) and walks them tile-major
+  // XCD x owns strip group x % xs and tile group x / xs (xs * xt = 8 groups) and walks
+  // its strips tile-major
   const int b = blockIdx.x;
   const int xcd = b % kXcds, jx = b / kXcds;
-  const int sper = strips / kXcds, srem = strips % kXcds;
-  const int sx0 = xcd * sper + min(xcd, srem);
-  const int nsx = sper + (xcd < srem ? 1 : 0);
-  if (nsx == 0 || jx >= nsx * tiles) return;
-  const int tile = jx / nsx, strip = sx0 + jx % nsx;
+  const int xt = kXcds / xs, sgi = xcd % xs, tgi = xcd / xs;
+  const int sper = strips / xs, srem = strips % xs;
+  const int sx0 = sgi * sper + min(sgi, srem);
+  const int nsx = sper + (sgi < srem ? 1 : 0);
+  const int tper = tiles / xt, trem = tiles % xt;
+  const int tx0 = tgi * tper + min(tgi, trem);
+  const int ntx = tper + (tgi < trem ? 1 : 0);
+  if (nsx == 0 || jx >= nsx * ntx) return;
+  const int tile = tx0 + jx / nsx, strip = sx0 + jx % nsx;
   const int c0 = strip * TC;
   const int g0 = tile * TR;
   const int g1 = min(n, g0 + TR);
@@ -1114,10 +1139,13 @@ template <int DT, int R>
 hipError_t launch_expand_long(hipStream_t st, uint16_t* y, int64_t ld_y, const float* vsrc,
                               int64_t slice, int ks, const Tables& T, int32_t h_out,
                               float scale) {
-  // each XCD takes ceil(strips / 8) strips at most: pad the grid to 8 equal shares
   const int tiles = (T.n + ExpCfg<R>::TR - 1) / ExpCfg<R>::TR;
   const int strips = (h_out + ExpCfg<R>::TC - 1) / ExpCfg<R>::TC;
-  const int64_t share = static_cast<int64_t>(tiles) * ((strips + kXcds - 1) / kXcds);
+  const int xs = expand_strip_groups(strips, tiles);
+  // each XCD takes at most ceil(strips / xs) strips of ceil(tiles / xt) tiles: pad the
+  // grid to 8 equal shares
+  const int64_t share = static_cast<int64_t>((tiles + kXcds / xs - 1) / (kXcds / xs)) *
+                        ((strips + xs - 1) / xs);
   if (share * kXcds > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(share * kXcds));
   if (ks > 1) {
@@ -1125,14 +1153,14 @@ hipError_t launch_expand_long(hipStream_t st, uint16_t* y, int64_t ld_y, const f
       if (ks > kExpandSlices) return hipErrorInvalidValue;
       hipLaunchKernelGGL((expand_mfma_kernel<DT, R, kExpandSlices>), grid, dim3(256), 0, st, y,
                          ld_y, vsrc, slice, ks, T.ptrs, T.seg_starts, T.S, T.perm, T.n, h_out,
-                         scale, tiles, strips, T.meta);
+                         scale, tiles, strips, xs, T.meta);
     } else {
       return hipErrorInvalidValue;  // r = 64: reduce_v_kernel runs first
     }
   } else {
     hipLaunchKernelGGL((expand_mfma_kernel<DT, R, 1>), grid, dim3(256), 0, st, y, ld_y, vsrc,
                        slice, 1, T.ptrs, T.seg_starts, T.S, T.perm, T.n, h_out, scale, tiles,
-                       strips, T.meta);
+                       strips, xs, T.meta);
   }
   return hipGetLastError();
 }
