@@ -403,7 +403,7 @@ def load_traffic(workload: str, pool_path: bool):
 
 
 def measure(p, device, steps: int, warmup: int, eager: bool = False, force_table: bool = False,
-            force_device: bool = False, host_ids: bool = False):
+            force_device: bool = False, host_ids: bool = False, warm: bool = True):
     """Check slot 0 against the oracle, then time `steps` steps after `warmup` untimed
     ones: wall time per step, GPU time per step, and the SGMV call's average duration."""
     import torch
@@ -470,8 +470,10 @@ def measure(p, device, steps: int, warmup: int, eager: bool = False, force_table
         call_s = kernel_pass(rig, base + steps, min(steps, 500))
         call_how = "HIP events over a graph of the same calls (tables pre-uploaded) / count"
     flag = int(rig.ws[:4].view(torch.int32).item())
-    warm_s = warm_call_time(rig, steps, use_graph)
-    flag = max(flag, int(rig.ws[:4].view(torch.int32).item()))
+    warm_s = None
+    if warm:
+        warm_s = warm_call_time(rig, steps, use_graph)
+        flag = max(flag, int(rig.ws[:4].view(torch.int32).item()))
     return dict(rig=rig, parity=parity, use_graph=use_graph, wall=wall, gpu_step=gpu_step,
                 call_s=call_s, call_how=call_how, flag=flag, warm_s=warm_s)
 
@@ -644,7 +646,7 @@ def run_sweep(kind: str, device, args) -> int:
     for name in SWEEPS[kind]:
         p = workload_problem(name)
         steps = args.steps if kind == "decode" else max(20, args.steps // 20)
-        m = measure(p, device, steps, min(args.warmup, steps), eager=args.eager)
+        m = measure(p, device, steps, min(args.warmup, steps), eager=args.eager, warm=False)
         nbytes = algorithmic_bytes(p)
         points.append({
             "workload": p.name, "n_tokens": p.n, "distinct_adapters": p.distinct_adapters(),
@@ -824,6 +826,9 @@ def main(argv=None) -> int:
                          "host: one launch with the host ids in its kernel arguments (<= 64)")
     ap.add_argument("--eager", action="store_true", help="no HIP graph on the one-launch path")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cold-only", action="store_true",
+                    help="skip the warm-cache timing and the floors (profiled runs: only the "
+                         "cold calls reach the profiler)")
     ap.add_argument("--sweep", choices=sorted(SWEEPS),
                     help="time a batch-size (decode) or prompt-length (prefill) sweep instead")
     ap.add_argument("--layer", action="store_true",
@@ -868,7 +873,7 @@ def main(argv=None) -> int:
     p = workload_problem(args.workload)
     m = measure(p, device, args.steps, args.warmup, eager=args.eager,
                 force_table=args.path == "table", force_device=args.path == "device",
-                host_ids=args.path == "host")
+                host_ids=args.path == "host", warm=not args.cold_only)
     rig, parity, use_graph = m["rig"], m["parity"], m["use_graph"]
     wall, gpu_step, call_s, call_how, flag = (m["wall"], m["gpu_step"], m["call_s"],
                                               m["call_how"], m["flag"])
@@ -929,14 +934,16 @@ def main(argv=None) -> int:
             "kernel": kernel,
             "mfma_frac": round(flops / call_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
         },
-        "warm": {"us_per_call": round(m["warm_s"] * 1e6, 3),
-                 "gbs": round(nbytes / m["warm_s"] / 1e9, 1),
-                 "how": "every call on one slot (operands cached), same timing as us_per_call"},
-        "floors": floors(nbytes, device, min(args.steps, 500)),
         "parity": parity,
         "workspace_flag_after": flag,
         "kernel_source_sha256_16": kernel_source_hash(),
     }
+    if m["warm_s"] is not None:
+        out["warm"] = {"us_per_call": round(m["warm_s"] * 1e6, 3),
+                       "gbs": round(nbytes / m["warm_s"] / 1e9, 1),
+                       "how": "every call on one slot (operands cached), same timing as "
+                              "us_per_call"}
+        out["floors"] = floors(nbytes, device, min(args.steps, 500))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_budget)
         out["cpu_baseline_1thread"] = cpu_baseline_1thread(p, args.cpu_budget / 2)
