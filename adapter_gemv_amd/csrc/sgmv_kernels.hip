@@ -344,10 +344,18 @@ struct ShrCfg {
 };
 
 // The LDS-staged shrink (shrink_lds_kernel, 64-row tiles) takes r = 64, and r = 16 when
-// the rows of x are long (h_in > 16384).  Measured on MI355X for the 70B batch: r = 64
-// gate/up shrink 27.6 -> 21.0 us, down 57.6 -> 49.3 us, r = 16 down 41.6 -> 35.6 us; for
-// r = 16 at h_in <= 13824 it is slower than 16-row tiles of shrink_mfma_kernel.
-inline bool shrink_lds_long_rows(int32_t h_in) { return h_in > 16384; }
+// the rows of x are long (h_in > 16384), or longer than 6144 in a call that also has short
+// segments (host tables, and not a rank group of a mixed-rank call, whose groups' shrinks
+// run side by side: there the taller tiles measured slower, ranks 16 + 64 gate/up 110 ->
+// 116 us).  Its split-K slices then need a reduce pass, which a call with short segments
+// runs anyway.  Measured on MI355X for the 70B batch: r = 64 gate/up shrink
+// 27.6 -> 21.0 us, down 57.6 -> 49.3 us, r = 16 down 41.6 -> 35.6 us; r = 16 calls with
+// h_in = 8192: q/o 51.1 -> 47.6 us, k/v 40.1 -> 37.1, gate/up 92.9 -> 89.0.  For the 13B
+// prefill batch (long segments only) the extra reduce pass makes it slower than the
+// 16-row tiles of shrink_mfma_kernel (down projection, h_in = 13824: 41.6 vs 37.5 us).
+inline bool shrink_lds_long_rows(int32_t h_in, bool has_short) {
+  return h_in > 16384 || (has_short && h_in > 6144);
+}
 template <int R> constexpr int kLdsD = (R == 16) ? 3 : 6;  // stage buffers
 constexpr int kLdsMT = 64;                                  // rows per tile
 constexpr int kLdsWgs = 512;                                // workgroup target
@@ -1041,6 +1049,8 @@ struct Tables {
   const int32_t* perm;
   int32_t n, S, min_len, max_len;
   const int32_t* meta = nullptr;
+  // a rank group of sgmv_lora_add_ranked: other groups' kernels may run beside its own
+  bool in_group = false;
   bool use_gemv() const { return meta || min_len < kLongMin; }
   bool use_long() const { return meta || max_len >= kLongMin; }
   // grid of a GEMV kernel with `per` items per segment: one workgroup per item with host
@@ -1114,7 +1124,7 @@ hipError_t launch_shrink_long(hipStream_t st, const uint16_t* x, int64_t ld_x, c
     return launch_shrink_lds<DT, R, kLdsMT, kLdsD<R>>(st, x, ld_x, T, h_in, L, part, v_long,
                                                       rowks, ks_long, kLdsWgs);
   } else {
-    if (R == 16 && shrink_lds_long_rows(h_in))
+    if (R == 16 && shrink_lds_long_rows(h_in, !T.meta && !T.in_group && T.use_gemv()))
       return launch_shrink_lds<DT, 16, kLdsMT, kLdsD<16>>(st, x, ld_x, T, h_in, L, part, v_long,
                                                           rowks, ks_long, kLdsWgs);
     return launch_shrink_mfma<DT, R>(st, x, ld_x, T, h_in, L, part, v_long, rowks, ks_long);
@@ -1613,7 +1623,8 @@ extern "C" int sgmv_lora_add_ranked(hipStream_t stream, int32_t dtype, void* y, 
   if ((st = check_device())) return st;
   auto tables = [&](const sgmv_rank_group& G, const void* const* P) {
     return Tables{reinterpret_cast<const uint16_t* const*>(P) + G.seg0, seg_starts + G.starts0,
-                  perm + G.row0, G.n, G.n_segments, G.min_seg_len, G.max_seg_len};
+                  perm + G.row0, G.n, G.n_segments, G.min_seg_len, G.max_seg_len, nullptr,
+                  true};
   };
   // The groups touch disjoint rows.  Under graph capture, with room for every group's
   // scratch side by side in the workspace, each group's short and long chains run on
