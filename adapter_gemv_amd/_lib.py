@@ -19,12 +19,18 @@ ERR_UNSUPPORTED = 5
 ERR_WORKSPACE = 6
 ERR_ALIAS = 7
 ERR_HIP = 8
+ERR_DEVICE = 9
+
+# flag bits of the workspace's first int32 (SGMV_FLAG_* in include/sgmv.h)
+FLAG_WAIT_TIMEOUT = 1
+FLAG_ADAPTER_ID = 2
+FLAG_SEG_BOUNDS = 4
 
 STATUS_NAMES = {
     OK: "SGMV_OK", ERR_NULL: "SGMV_ERR_NULL", ERR_SHAPE: "SGMV_ERR_SHAPE",
     ERR_ALIGNMENT: "SGMV_ERR_ALIGNMENT", ERR_ADAPTER_ID: "SGMV_ERR_ADAPTER_ID",
     ERR_UNSUPPORTED: "SGMV_ERR_UNSUPPORTED", ERR_WORKSPACE: "SGMV_ERR_WORKSPACE",
-    ERR_ALIAS: "SGMV_ERR_ALIAS", ERR_HIP: "SGMV_ERR_HIP",
+    ERR_ALIAS: "SGMV_ERR_ALIAS", ERR_HIP: "SGMV_ERR_HIP", ERR_DEVICE: "SGMV_ERR_DEVICE",
 }
 
 # every function the header declares, with its ctypes signature
@@ -38,6 +44,7 @@ SIGNATURES = {
     "sgmv_build_segments": (ctypes.c_int, [_p, _i32, _i32, _p, _p, _p, _p, _p, _p]),
     "sgmv_build_ptr_table": (ctypes.c_int, [_p, _i32, _p, _i32, _p]),
     "sgmv_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "sgmv_check_workspace": (ctypes.c_int, [_p, _p, _p, _i32]),
     "sgmv_shrink": (ctypes.c_int, [_p, _i32, _p, _p, _i64, _p, _p, _p, _i32, _i32, _i32, _i32,
                                    _i32, _i32, _p, _sz]),
     "sgmv_expand": (ctypes.c_int, [_p, _i32, _p, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _i32,

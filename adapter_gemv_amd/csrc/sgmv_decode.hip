@@ -300,7 +300,7 @@ __global__ __launch_bounds__(kTabThreads) void tables_kernel(const int32_t* __re
       o.meta[3] = n_valid;
     }
     if (s_bad && o.ws_flag)
-      __hip_atomic_store(o.ws_flag, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      raise_flag(o.ws_flag, kFlagBadId);
   }
 }
 
@@ -484,7 +484,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __r
       o.meta[3] = n_valid;
     }
     if (s_bad && o.ws_flag)
-      __hip_atomic_store(o.ws_flag, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      raise_flag(o.ws_flag, kFlagBadId);
   }
 }
 
@@ -641,7 +641,7 @@ __device__ inline void expand_item(const PoolArgs& p, const Leader& L, int r, in
       for (int u = 0; u < 8; ++u) ready = ready && (w[u] >> 32) != 0;
       if (__ballot(!ready) == 0) break;
       if (spins >= kSpinLimit) {
-        if (lane == 0) __hip_atomic_store(p.ws_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) raise_flag(p.ws_flag, kFlagWaitTimeout);
         break;
       }
       __builtin_amdgcn_s_sleep(1);
@@ -706,7 +706,7 @@ __device__ inline void pool_items(const PoolArgs& p, int id) {
   const int b = blockIdx.x;
   if (b == 0 && wv == 0) {
     const bool bad = __ballot(lane < p.n && (id < 0 || id >= p.n_adapters)) != 0;
-    if (bad && lane == 0) __hip_atomic_store(p.ws_flag, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (bad && lane == 0) raise_flag(p.ws_flag, kFlagBadId);
   }
   Leader L;
   if (b < shrink_wgs) {

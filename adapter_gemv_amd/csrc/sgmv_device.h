@@ -17,6 +17,18 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
 // ------------------------------------------------------------------------------------
+// the workspace's flag word (its first int32): bits set by device-side checks, never
+// cleared by a kernel (sgmv_check_workspace reads and clears them)
+// ------------------------------------------------------------------------------------
+constexpr int32_t kFlagWaitTimeout = SGMV_FLAG_WAIT_TIMEOUT;
+constexpr int32_t kFlagBadId = SGMV_FLAG_ADAPTER_ID;
+constexpr int32_t kFlagSegBounds = SGMV_FLAG_SEG_BOUNDS;
+
+__device__ inline void raise_flag(int32_t* flag, int32_t bit) {
+  __hip_atomic_fetch_or(flag, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------------------------------
 // element helpers: 16-bit values travel packed two per 32-bit word
 // ------------------------------------------------------------------------------------
 template <int DT>

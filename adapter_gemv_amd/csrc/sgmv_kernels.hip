@@ -18,6 +18,7 @@
 
 #include <climits>
 #include <cstdint>
+#include <initializer_list>
 #include <mutex>
 #include <type_traits>
 #include <vector>
@@ -55,12 +56,21 @@ struct GemvCfg {
   static constexpr int MR = 4;                         // token rows loaded per pass
 };
 
+//
+// Every row's slice count in rowks is written for the current call by whichever shrink
+// sees the row first: this kernel writes it for the rows of every segment (rk_long for
+// rows of long segments), the long-segment shrinks for every row of their tiles
+// (rk_short for rows outside long segments).  Both write the same value for a row, so the
+// reduce pass of either chain, which runs after its own shrink, never reads a count left
+// by an earlier call in which the row's segment was of the other kind.  bad_flag is set
+// when the long-segment kernels are not launched (the caller's max_seg_len was below
+// kLongMin) and a long segment is met anyway: its rows are not computed.
 template <int DT, int R>
 __global__ __launch_bounds__(256) void shrink_gemv_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, const uint16_t* const* __restrict__ A_ptrs,
     const int32_t* __restrict__ seg_starts, const int32_t* __restrict__ perm, int32_t h_in,
     float* __restrict__ part, int64_t slice, int32_t* __restrict__ rowks, int32_t ks,
-    const int32_t* __restrict__ meta) {
+    int32_t rk_long, int32_t* __restrict__ bad_flag, const int32_t* __restrict__ meta) {
   using C = GemvCfg<R>;
   __shared__ float red[4][kShortMax][R];
   // items (segment s, chunk kc) = (i % S, i / S): one per workgroup of a (S, ks) grid with
@@ -73,7 +83,14 @@ __global__ __launch_bounds__(256) void shrink_gemv_kernel(
   const int s = item % S, kc = item / S;
   const int seg0 = seg_starts[s];
   const int m = seg_starts[s + 1] - seg0;
-  if (m <= 0 || m >= kLongMin) continue;  // uniform
+  if (m >= kLongMin) {  // uniform: a long segment, computed by the MFMA kernels
+    if (kc == 0) {
+      for (int i = threadIdx.x; i < m; i += 256) rowks[seg0 + i] = rk_long;
+      if (bad_flag && threadIdx.x == 0) raise_flag(bad_flag, kFlagSegBounds);
+    }
+    continue;
+  }
+  if (m <= 0) continue;  // uniform
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int t0 = lane >> 3, c = lane & 7;
   const int kbase = kc * C::KC + w * C::WAVE_K + 8 * c;
@@ -305,6 +322,25 @@ __device__ inline int tile_long_segments_pre(const int32_t* __restrict__ seg_sta
   return tile_segments_impl<ROWS, THREADS, true>(seg_starts, ptrs, S, g0, g1, sh, pre);
 }
 
+// Slice counts of a tile's rows for the current call (written by the tile's first K
+// chunk): rows of long segments get their final v from this kernel (ks == 1, count 0) or
+// ks slices; every other row is a short-segment row, whose count rk_short the GEMV shrink
+// writes too.  bad_flag (non-null when the GEMV kernels are not launched, the caller's
+// min_seg_len being at least kLongMin) is set if the tile meets such a row: it is not
+// computed.
+template <int ROWS>
+__device__ inline void mark_tile_rows(const TileSegs<ROWS>& sh, int r0, int r1, int ks,
+                                      int32_t rk_short, int32_t* __restrict__ rowks,
+                                      int32_t* __restrict__ bad_flag) {
+  bool short_row = false;
+  for (int qr = threadIdx.x; qr < r1 - r0; qr += blockDim.x) {
+    const bool lng = sh.rseg[qr] >= 0;
+    rowks[r0 + qr] = lng ? (ks == 1 ? 0 : ks) : rk_short;
+    short_row = short_row || !lng;
+  }
+  if (bad_flag && short_row) raise_flag(bad_flag, kFlagSegBounds);
+}
+
 // Next long run of a tile at or after row q (rows are in segment order): its slot k in
 // TileSegs, or -1 when there is none; leaves q after the run's last row in the tile.
 template <int ROWS>
@@ -401,8 +437,8 @@ __global__ __launch_bounds__(256, ShrCfg<R>::WAVES_PER_SIMD) void shrink_mfma_ke
     const uint16_t* __restrict__ x, int64_t ld_x, const uint16_t* const* __restrict__ A_ptrs,
     const int32_t* __restrict__ seg_starts, int32_t S_host, const int32_t* __restrict__ perm,
     int32_t n, int32_t h_in, int32_t kcm, int32_t ks, float* __restrict__ part, int64_t slice,
-    float* __restrict__ v_out, int32_t* __restrict__ rowks,
-    const int32_t* __restrict__ meta) {
+    float* __restrict__ v_out, int32_t* __restrict__ rowks, int32_t rk_short,
+    int32_t* __restrict__ bad_flag, const int32_t* __restrict__ meta) {
   const int S = meta ? meta[0] : S_host;
   if (meta && meta[2] < kLongMin) return;  // no long segment at all
   using C = ShrCfg<R>;
@@ -431,7 +467,9 @@ __global__ __launch_bounds__(256, ShrCfg<R>::WAVES_PER_SIMD) void shrink_mfma_ke
   if (tid < MT) s_prow[tid] = (r0 + tid < r1) ? (perm ? perm[r0 + tid] : r0 + tid) : 0;
   if (tid == 0) sh.nseg = 0;
   __syncthreads();
-  if (tile_long_segments_pre<MT, 256>(seg_starts, A_ptrs, S, r0, r1, sh, pre) == 0) return;  // uniform
+  const int nseg = tile_long_segments_pre<MT, 256>(seg_starts, A_ptrs, S, r0, r1, sh, pre);
+  if (kc == 0) mark_tile_rows(sh, r0, r1, ks, rk_short, rowks, bad_flag);
+  if (nseg == 0) return;  // uniform
   const int k_lo = kc * kcm;
   const int k_hi = min(h_in, k_lo + kcm);
   const int nst = (k_hi - k_lo + STAGE - 1) / STAGE;
@@ -497,10 +535,6 @@ __global__ __launch_bounds__(256, ShrCfg<R>::WAVES_PER_SIMD) void shrink_mfma_ke
         part[kc * slice + o] = sum[c];
     }
   }
-  // rows of long segments: final v (ks == 1) or ks slices for reduce_v_kernel
-  if (kc == 0)
-    for (int qr = tid; qr < r1 - r0; qr += 256)
-      if (sh.rseg[qr] >= 0) rowks[r0 + qr] = (ks == 1) ? 0 : ks;
 }
 
 // Shrink on MFMA with the operands staged in LDS by direct global-to-LDS loads.  Same
@@ -572,8 +606,8 @@ __global__ __launch_bounds__(256) void shrink_lds_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, const uint16_t* const* __restrict__ A_ptrs,
     const int32_t* __restrict__ seg_starts, int32_t S_host, const int32_t* __restrict__ perm,
     int32_t n, int32_t h_in, int32_t kcm, int32_t ks, float* __restrict__ part, int64_t slice,
-    float* __restrict__ v_out, int32_t* __restrict__ rowks,
-    const int32_t* __restrict__ meta) {
+    float* __restrict__ v_out, int32_t* __restrict__ rowks, int32_t rk_short,
+    int32_t* __restrict__ bad_flag, const int32_t* __restrict__ meta) {
   using C = ShrLdsCfg<R, MT, D>;
   constexpr int NB = C::NB, RBW = C::RBW, UN = C::UN, STAGE = C::STAGE, XPW = C::XPW;
   constexpr int LPS = C::LPS;
@@ -613,7 +647,9 @@ __global__ __launch_bounds__(256) void shrink_lds_kernel(
   if (tid < MT) s_prow[tid] = (r0 + tid < r1) ? (perm ? perm[r0 + tid] : r0 + tid) : 0;
   if (tid == 0) sh.nseg = 0;
   __syncthreads();
-  if (tile_long_segments_pre<MT, 256>(seg_starts, A_ptrs, S, r0, r1, sh, pre) == 0) return;  // uniform
+  const int nseg = tile_long_segments_pre<MT, 256>(seg_starts, A_ptrs, S, r0, r1, sh, pre);
+  if (kc == 0) mark_tile_rows(sh, r0, r1, ks, rk_short, rowks, bad_flag);
+  if (nseg == 0) return;  // uniform
   const int k_lo = kc * kcm;
   const int k_hi = min(h_in, k_lo + kcm);
   // stages of the chunk, padded to a multiple of D: k past the chunk loads the chunk's last
@@ -705,9 +741,6 @@ __global__ __launch_bounds__(256) void shrink_lds_kernel(
           part[kc * slice + o] = acc[rb][nb][c];
       }
     }
-  if (kc == 0)
-    for (int qr = tid; qr < r1 - r0; qr += 256)
-      if (sh.rseg[qr] >= 0) rowks[r0 + qr] = (ks == 1) ? 0 : ks;
 }
 
 // Expand on MFMA 16x16x32 for a tile of TR sorted rows and TC columns, computed
@@ -971,14 +1004,22 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
 
 // v[i, :] = sum of the split-K slices of sorted row i, for rows whose slice count is
 // nonzero (rows of long segments with one slice already have their final v) and, unless
-// `which` is kReduceAll, whose segment kind (short or long) it names.  A workgroup takes 64
-// consecutive entries of v; wave q adds slices q, q + 4, q + 8, ... of each entry in that
-// order and the four waves' sums are added as (w0 + w1) + (w2 + w3).
+// `which` is kReduceAll, whose segment kind (short or long) it names.  The counts are the
+// current call's: the shrink of the chain that launches this pass wrote them for every row
+// (with device tables, a chain whose kind of segment is absent skips its shrink, and this
+// pass then exits too).  A workgroup takes 64 consecutive entries of v; wave q adds slices
+// q, q + 4, q + 8, ... of each entry in that order and the four waves' sums are added as
+// (w0 + w1) + (w2 + w3).
 template <int R>
 __global__ __launch_bounds__(256) void reduce_v_kernel(float* __restrict__ v,
                                                       const float* __restrict__ part, int64_t slice,
                                                       const int32_t* __restrict__ rowks, int32_t n,
-                                                      int32_t ks_max, int32_t which) {
+                                                      int32_t ks_max, int32_t which,
+                                                      const int32_t* __restrict__ meta) {
+  if (meta) {
+    if (which == kReduceShort && meta[1] >= kLongMin) return;  // no short segment
+    if (which == kReduceLong && meta[2] < kLongMin) return;    // no long segment
+  }
   __shared__ float red[4][64];
   const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 64 + lane;
@@ -1051,6 +1092,9 @@ struct Tables {
   const int32_t* meta = nullptr;
   // a rank group of sgmv_lora_add_ranked: other groups' kernels may run beside its own
   bool in_group = false;
+  // the workspace's flag word, for host tables (kernels flag tables that contradict
+  // min_len / max_len)
+  int32_t* flag = nullptr;
   bool use_gemv() const { return meta || min_len < kLongMin; }
   bool use_long() const { return meta || max_len >= kLongMin; }
   // grid of a GEMV kernel with `per` items per segment: one workgroup per item with host
@@ -1063,72 +1107,86 @@ struct Tables {
   }
 };
 
-template <int DT, int R>
-hipError_t launch_shrink_mfma(hipStream_t st, const uint16_t* x, int64_t ld_x, const Tables& T,
-                              int32_t h_in, const WsLayout& L, float* part, float* v_long,
-                              int32_t* rowks, int* ks_long) {
-  using C = ShrCfg<R>;
-  int kcm, ks;
-  mfma_split<C>(T.n, h_in, L.ks_max, &kcm, &ks);
-  const int tiles = (T.n + C::MT - 1) / C::MT;
-  hipLaunchKernelGGL((shrink_mfma_kernel<DT, R>), dim3(tiles * ks), dim3(256), 0, st, x, ld_x,
-                     T.ptrs, T.seg_starts, T.S, T.perm, T.n, h_in, kcm, ks, part, L.slice,
-                     v_long, rowks, T.meta);
-  *ks_long = ks;
-  return hipGetLastError();
+// Split-K plan of one call, fixed on the host before anything is launched, so that the
+// kernels of either chain can write the slice counts of the other chain's rows (see
+// shrink_gemv_kernel).  bad_flag is the workspace's flag word, passed to a chain's shrink
+// when the other chain is not launched.
+struct Plan {
+  int ksg = 0;          // GEMV shrink: split-K slices of short rows
+  int ksl = 0;          // long shrink: split-K slices of long rows
+  int kcm = 0;          // long shrink: K chunk
+  bool lds = false;     // long shrink: the LDS-staged kernel
+  int32_t* flag = nullptr;
+  int32_t rk_short() const { return kShortRowFlag | ksg; }
+  int32_t rk_long() const { return ksl == 1 ? 0 : ksl; }
+};
+
+template <int R>
+Plan make_plan(const Tables& T, int32_t h_in, const WsLayout& L) {
+  Plan P;
+  P.ksg = (h_in + GemvCfg<R>::KC - 1) / GemvCfg<R>::KC;
+  if constexpr (R == 64) {
+    P.lds = true;
+  } else {
+    P.lds = R == 16 && shrink_lds_long_rows(h_in, !T.meta && !T.in_group && T.use_gemv());
+  }
+  if (P.lds) {
+    // Chunks are whole multiples of D stages.  For the 70B batch this gives 15 chunks, not
+    // a multiple of 8, so each XCD's L2 sees every chunk of A: at r = 64 the L2s miss on A
+    // again (down projection: 175 instead of 127 MB fetched per call), but those misses are
+    // served by the Infinity Cache, and 16 chunks of 64-k multiples, padded to whole ring
+    // turns, measured 5 % slower on MI355X (down 114 vs 119 us per call).
+    if constexpr (R != 32) {
+      using C = ShrLdsCfg<R, kLdsMT, kLdsD<R>>;
+      split_k(T.n, h_in, L.ks_max, kLdsMT, kLdsWgs, C::STAGE * kLdsD<R>, &P.kcm, &P.ksl);
+    }
+  } else {
+    if constexpr (R != 64) mfma_split<ShrCfg<R>>(T.n, h_in, L.ks_max, &P.kcm, &P.ksl);
+  }
+  P.flag = T.meta ? nullptr : T.flag;
+  return P;
 }
 
-// LDS-staged shrink: tiles of MT rows, D stage buffers, about `target` workgroups (the
-// kernel pads a chunk to a whole multiple of D stages)
-template <int DT, int R, int MT, int D>
-hipError_t launch_shrink_lds(hipStream_t st, const uint16_t* x, int64_t ld_x, const Tables& T,
-                             int32_t h_in, const WsLayout& L, float* part, float* v_long,
-                             int32_t* rowks, int* ks_long, int target) {
-  using C = ShrLdsCfg<R, MT, D>;
-  int kcm, ks;
-  // Chunks are whole multiples of D stages.  For the 70B batch this gives 15 chunks, not a
-  // multiple of 8, so each XCD's L2 sees every chunk of A: at r = 64 the L2s miss on A
-  // again (down projection: 175 instead of 127 MB fetched per call), but those misses are
-  // served by the Infinity Cache, and 16 chunks of 64-k multiples, padded to whole ring
-  // turns, measured 5 % slower on MI355X (down 114 vs 119 us per call).
-  split_k(T.n, h_in, L.ks_max, MT, target, C::STAGE * D, &kcm, &ks);
-  const int tiles = (T.n + MT - 1) / MT;
-  hipLaunchKernelGGL((shrink_lds_kernel<DT, R, MT, D>), dim3(tiles * ks), dim3(256), 0, st, x,
-                     ld_x, T.ptrs, T.seg_starts, T.S, T.perm, T.n, h_in, kcm, ks, part, L.slice,
-                     v_long, rowks, T.meta);
-  *ks_long = ks;
-  return hipGetLastError();
-}
-
-// short segments: ks_gemv split-K slices, counted in rowks with kShortRowFlag
+// short segments: P.ksg split-K slices, counted in rowks with kShortRowFlag
 template <int DT, int R>
 hipError_t launch_shrink_short(hipStream_t st, const uint16_t* x, int64_t ld_x, const Tables& T,
-                               int32_t h_in, const WsLayout& L, char* ws, int* ks_gemv) {
+                               int32_t h_in, const WsLayout& L, char* ws, const Plan& P) {
   float* part = reinterpret_cast<float*>(ws + L.part_off);
   int32_t* rowks = reinterpret_cast<int32_t*>(ws + L.rowks_off);
-  const int ks = (h_in + GemvCfg<R>::KC - 1) / GemvCfg<R>::KC;
-  *ks_gemv = ks;
-  hipLaunchKernelGGL((shrink_gemv_kernel<DT, R>), T.gemv_grid(ks, 2048), dim3(256), 0, st, x,
-                     ld_x, T.ptrs, T.seg_starts, T.perm, h_in, part, L.slice, rowks, ks, T.meta);
+  int32_t* bad = T.use_long() ? nullptr : P.flag;
+  hipLaunchKernelGGL((shrink_gemv_kernel<DT, R>), T.gemv_grid(P.ksg, 2048), dim3(256), 0, st, x,
+                     ld_x, T.ptrs, T.seg_starts, T.perm, h_in, part, L.slice, rowks, P.ksg,
+                     P.rk_long(), bad, T.meta);
   return hipGetLastError();
 }
 
-// long segments: the final v in v_long (ks_long == 1) or ks_long slices, counted in rowks
+// long segments: the final v in v_long (P.ksl == 1) or P.ksl slices, counted in rowks
 template <int DT, int R>
 hipError_t launch_shrink_long(hipStream_t st, const uint16_t* x, int64_t ld_x, const Tables& T,
                               int32_t h_in, const WsLayout& L, char* ws, float* v_long,
-                              int* ks_long) {
+                              const Plan& P) {
   float* part = reinterpret_cast<float*>(ws + L.part_off);
   int32_t* rowks = reinterpret_cast<int32_t*>(ws + L.rowks_off);
-  if constexpr (R == 64) {
-    return launch_shrink_lds<DT, R, kLdsMT, kLdsD<R>>(st, x, ld_x, T, h_in, L, part, v_long,
-                                                      rowks, ks_long, kLdsWgs);
-  } else {
-    if (R == 16 && shrink_lds_long_rows(h_in, !T.meta && !T.in_group && T.use_gemv()))
-      return launch_shrink_lds<DT, 16, kLdsMT, kLdsD<16>>(st, x, ld_x, T, h_in, L, part, v_long,
-                                                          rowks, ks_long, kLdsWgs);
-    return launch_shrink_mfma<DT, R>(st, x, ld_x, T, h_in, L, part, v_long, rowks, ks_long);
+  int32_t* bad = T.use_gemv() ? nullptr : P.flag;
+  if (P.lds) {
+    if constexpr (R != 32) {
+      constexpr int MT = kLdsMT, D = kLdsD<R>;
+      const int tiles = (T.n + MT - 1) / MT;
+      hipLaunchKernelGGL((shrink_lds_kernel<DT, R, MT, D>), dim3(tiles * P.ksl), dim3(256), 0, st,
+                         x, ld_x, T.ptrs, T.seg_starts, T.S, T.perm, T.n, h_in, P.kcm, P.ksl, part,
+                         L.slice, v_long, rowks, P.rk_short(), bad, T.meta);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
   }
+  if constexpr (R != 64) {
+    const int tiles = (T.n + ShrCfg<R>::MT - 1) / ShrCfg<R>::MT;
+    hipLaunchKernelGGL((shrink_mfma_kernel<DT, R>), dim3(tiles * P.ksl), dim3(256), 0, st, x, ld_x,
+                       T.ptrs, T.seg_starts, T.S, T.perm, T.n, h_in, P.kcm, P.ksl, part, L.slice,
+                       v_long, rowks, P.rk_short(), bad, T.meta);
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
 }
 
 // short segments sum ks slices of vsrc (slice stride `slice`) themselves
@@ -1183,20 +1241,28 @@ hipError_t launch_reduce(hipStream_t st, float* v, const Tables& T, const WsLayo
   const int64_t total = static_cast<int64_t>(T.n) * R;
   hipLaunchKernelGGL((reduce_v_kernel<R>), dim3(static_cast<unsigned>((total + 63) / 64)), dim3(256),
                      0, st, v, reinterpret_cast<const float*>(ws + L.part_off), L.slice,
-                     reinterpret_cast<const int32_t*>(ws + L.rowks_off), T.n, L.ks_max, which);
+                     reinterpret_cast<const int32_t*>(ws + L.rowks_off), T.n, L.ks_max, which,
+                     T.meta);
   return hipGetLastError();
+}
+
+// whether the long chain's slices need a reduce pass before its expand: a few slices are
+// added by the MFMA expand itself (r <= 32), more are summed once per row
+template <int R>
+bool long_needs_reduce(int ksl) {
+  return ksl > 1 && (ksl > kExpandSlices || R > 32);
 }
 
 template <int DT, int R>
 hipError_t run_shrink(hipStream_t st, float* v, const uint16_t* x, int64_t ld_x, const Tables& T,
                       int32_t h_in, const WsLayout& L, char* ws) {
-  int ksg = 0, ksl = 0;
+  const Plan P = make_plan<R>(T, h_in, L);
   hipError_t e;
-  if (T.use_gemv() && (e = launch_shrink_short<DT, R>(st, x, ld_x, T, h_in, L, ws, &ksg)) != hipSuccess)
+  if (T.use_gemv() && (e = launch_shrink_short<DT, R>(st, x, ld_x, T, h_in, L, ws, P)) != hipSuccess)
     return e;
-  if (T.use_long() && (e = launch_shrink_long<DT, R>(st, x, ld_x, T, h_in, L, ws, v, &ksl)) != hipSuccess)
+  if (T.use_long() && (e = launch_shrink_long<DT, R>(st, x, ld_x, T, h_in, L, ws, v, P)) != hipSuccess)
     return e;
-  if (ksg == 0 && ksl <= 1) return hipSuccess;
+  if (!T.use_gemv() && P.ksl <= 1) return hipSuccess;
   return launch_reduce<R>(st, v, T, L, ws, kReduceAll);
 }
 
@@ -1264,9 +1330,18 @@ class SideStream {
         if (e == hipSuccess) e = hipEventCreateWithFlags(&made.join[i], hipEventDisableTiming);
       }
       if (e == hipSuccess) e = hipEventCreateWithFlags(&made.fork, hipEventDisableTiming);
-      if (cur != dev) hipSetDevice(cur);
+      if (e != hipSuccess) {
+        // release whatever was made; the slot stays empty and a later call tries again
+        for (int i = 0; i < kSideStreams; ++i) {
+          if (made.join[i]) (void)hipEventDestroy(made.join[i]);
+          if (made.stream[i]) (void)hipStreamDestroy(made.stream[i]);
+        }
+        if (made.fork) (void)hipEventDestroy(made.fork);
+      }
+      const hipError_t er = (cur != dev) ? hipSetDevice(cur) : hipSuccess;
       if (e != hipSuccess) return e;
       slot = made;
+      if (er != hipSuccess) return er;
     }
     if (cap != hipStreamCaptureStatusActive) return hipSuccess;
     const int k = want < kSideStreams ? want : kSideStreams;
@@ -1333,34 +1408,33 @@ template <int DT, int R>
 hipError_t run_short_chain(hipStream_t st, uint16_t* y, int64_t ld_y, const uint16_t* x,
                            int64_t ld_x, const Tables& TA, const Tables& TB, int32_t h_in,
                            int32_t h_out, float scale, const WsLayout& L, char* ws) {
-  int ksg = 0;
-  hipError_t e = launch_shrink_short<DT, R>(st, x, ld_x, TA, h_in, L, ws, &ksg);
+  const Plan P = make_plan<R>(TA, h_in, L);
+  hipError_t e = launch_shrink_short<DT, R>(st, x, ld_x, TA, h_in, L, ws, P);
   if (e != hipSuccess) return e;
   float* v_long = reinterpret_cast<float*>(ws + L.v_off);
   const float* part = reinterpret_cast<const float*>(ws + L.part_off);
   // up to 16 slices are added by the GEMV expand itself; more are summed once per row
   // instead of once per column chunk
-  if (ksg > 16) {
+  if (P.ksg > 16) {
     if ((e = launch_reduce<R>(st, v_long, TA, L, ws, kReduceShort)) != hipSuccess) return e;
     return launch_expand_short<DT, R>(st, y, ld_y, v_long, 0, 1, TB, h_out, scale);
   }
-  return launch_expand_short<DT, R>(st, y, ld_y, part, L.slice, ksg, TB, h_out, scale);
+  return launch_expand_short<DT, R>(st, y, ld_y, part, L.slice, P.ksg, TB, h_out, scale);
 }
 
-// the long chain after its shrink (which left ksl slices)
+// the long chain after its shrink
 template <int DT, int R>
 hipError_t run_long_tail(hipStream_t st, uint16_t* y, int64_t ld_y, const Tables& TA,
                          const Tables& TB, int32_t h_out, float scale, const WsLayout& L,
-                         char* ws, int ksl) {
-  hipError_t e;
+                         char* ws, const Plan& P) {
   float* v_long = reinterpret_cast<float*>(ws + L.v_off);
   const float* part = reinterpret_cast<const float*>(ws + L.part_off);
-  // a few slices are added by the MFMA expand itself (r <= 32); more are summed once per row
-  if (ksl > 1 && (ksl > kExpandSlices || R > 32)) {
-    if ((e = launch_reduce<R>(st, v_long, TA, L, ws, kReduceLong)) != hipSuccess) return e;
-    ksl = 1;
+  if (long_needs_reduce<R>(P.ksl)) {
+    const hipError_t e = launch_reduce<R>(st, v_long, TA, L, ws, kReduceLong);
+    if (e != hipSuccess) return e;
+    return launch_expand_long<DT, R>(st, y, ld_y, v_long, 0, 1, TB, h_out, scale);
   }
-  if (ksl > 1) return launch_expand_long<DT, R>(st, y, ld_y, part, L.slice, ksl, TB, h_out, scale);
+  if (P.ksl > 1) return launch_expand_long<DT, R>(st, y, ld_y, part, L.slice, P.ksl, TB, h_out, scale);
   return launch_expand_long<DT, R>(st, y, ld_y, v_long, 0, 1, TB, h_out, scale);
 }
 
@@ -1368,11 +1442,11 @@ template <int DT, int R>
 hipError_t run_long_chain(hipStream_t st, uint16_t* y, int64_t ld_y, const uint16_t* x,
                           int64_t ld_x, const Tables& TA, const Tables& TB, int32_t h_in,
                           int32_t h_out, float scale, const WsLayout& L, char* ws) {
-  int ksl = 0;
+  const Plan P = make_plan<R>(TA, h_in, L);
   float* v_long = reinterpret_cast<float*>(ws + L.v_off);
-  const hipError_t e = launch_shrink_long<DT, R>(st, x, ld_x, TA, h_in, L, ws, v_long, &ksl);
+  const hipError_t e = launch_shrink_long<DT, R>(st, x, ld_x, TA, h_in, L, ws, v_long, P);
   if (e != hipSuccess) return e;
-  return run_long_tail<DT, R>(st, y, ld_y, TA, TB, h_out, scale, L, ws, ksl);
+  return run_long_tail<DT, R>(st, y, ld_y, TA, TB, h_out, scale, L, ws, P);
 }
 
 // Where the short chain starts under capture.  Started with the long chain, the GEMV
@@ -1385,6 +1459,13 @@ inline bool short_after_long_shrink(int r, int32_t h_in, int32_t h_out) {
   return r == 64 && h_in > h_out && h_out >= 4096;
 }
 
+// first error of a sequence of steps
+inline hipError_t first_error(std::initializer_list<hipError_t> es) {
+  for (hipError_t e : es)
+    if (e != hipSuccess) return e;
+  return hipSuccess;
+}
+
 template <int DT, int R>
 hipError_t run_lora_add(hipStream_t st, uint16_t* y, int64_t ld_y, const uint16_t* x, int64_t ld_x,
                         const Tables& TA, const Tables& TB, int32_t h_in, int32_t h_out, float scale,
@@ -1395,53 +1476,48 @@ hipError_t run_lora_add(hipStream_t st, uint16_t* y, int64_t ld_y, const uint16_
       return run_short_chain<DT, R>(st, y, ld_y, x, ld_x, TA, TB, h_in, h_out, scale, L, ws);
     return run_long_chain<DT, R>(st, y, ld_y, x, ld_x, TA, TB, h_in, h_out, scale, L, ws);
   }
+  const Plan P = make_plan<R>(TA, h_in, L);
+  float* v_long = reinterpret_cast<float*>(ws + L.v_off);
   if (short_after_long_shrink(R, h_in, h_out) && SideStream::ready(st)) {
     // the long shrink first; the short chain, forked after it, overlaps the long chain's
     // reduce and expand instead of competing with its shrink
-    int ksl = 0;
-    float* v_long = reinterpret_cast<float*>(ws + L.v_off);
-    hipError_t e = launch_shrink_long<DT, R>(st, x, ld_x, TA, h_in, L, ws, v_long, &ksl);
+    hipError_t e = launch_shrink_long<DT, R>(st, x, ld_x, TA, h_in, L, ws, v_long, P);
     if (e != hipSuccess) return e;
     SideStream side;
     e = side.fork(st, 1);
     const hipStream_t ss = (e == hipSuccess && side.count() > 0) ? side.stream(0) : st;
     const hipError_t e1 =
         run_short_chain<DT, R>(ss, y, ld_y, x, ld_x, TA, TB, h_in, h_out, scale, L, ws);
-    const hipError_t e2 = run_long_tail<DT, R>(st, y, ld_y, TA, TB, h_out, scale, L, ws, ksl);
+    const hipError_t e2 = run_long_tail<DT, R>(st, y, ld_y, TA, TB, h_out, scale, L, ws, P);
     const hipError_t e3 = side.join(st);
-    return e != hipSuccess ? e : (e1 != hipSuccess ? e1 : (e2 != hipSuccess ? e2 : e3));
+    return first_error({e, e1, e2, e3});
   }
   SideStream side;
   hipError_t e = side.fork(st, 1);
-  if (e != hipSuccess) {
-    side.join(st);
-    return e;
-  }
+  if (e != hipSuccess) return first_error({e, side.join(st)});
   if (side.count() > 0) {
     e = run_short_chain<DT, R>(side.stream(0), y, ld_y, x, ld_x, TA, TB, h_in, h_out, scale, L, ws);
     const hipError_t e2 =
         run_long_chain<DT, R>(st, y, ld_y, x, ld_x, TA, TB, h_in, h_out, scale, L, ws);
     const hipError_t e3 = side.join(st);
-    return e != hipSuccess ? e : (e2 != hipSuccess ? e2 : e3);
+    return first_error({e, e2, e3});
   }
-  side.join(st);
+  if ((e = side.join(st)) != hipSuccess) return e;
   // both chains on the caller's stream: one reduce_v_kernel pass for all rows if either
   // kind needs one
-  int ksg = 0, ksl = 0;
-  float* v_long = reinterpret_cast<float*>(ws + L.v_off);
   const float* part = reinterpret_cast<const float*>(ws + L.part_off);
-  if ((e = launch_shrink_short<DT, R>(st, x, ld_x, TA, h_in, L, ws, &ksg)) != hipSuccess) return e;
-  if ((e = launch_shrink_long<DT, R>(st, x, ld_x, TA, h_in, L, ws, v_long, &ksl)) != hipSuccess)
+  if ((e = launch_shrink_short<DT, R>(st, x, ld_x, TA, h_in, L, ws, P)) != hipSuccess) return e;
+  if ((e = launch_shrink_long<DT, R>(st, x, ld_x, TA, h_in, L, ws, v_long, P)) != hipSuccess)
     return e;
-  if ((ksl > 1 && (ksl > kExpandSlices || R > 32)) || ksg > 16) {
+  if (long_needs_reduce<R>(P.ksl) || P.ksg > 16) {
     if ((e = launch_reduce<R>(st, v_long, TA, L, ws, kReduceAll)) != hipSuccess) return e;
     if ((e = launch_expand_short<DT, R>(st, y, ld_y, v_long, 0, 1, TB, h_out, scale)) != hipSuccess)
       return e;
     return launch_expand_long<DT, R>(st, y, ld_y, v_long, 0, 1, TB, h_out, scale);
   }
-  if ((e = launch_expand_short<DT, R>(st, y, ld_y, part, L.slice, ksg, TB, h_out, scale)) != hipSuccess)
+  if ((e = launch_expand_short<DT, R>(st, y, ld_y, part, L.slice, P.ksg, TB, h_out, scale)) != hipSuccess)
     return e;
-  if (ksl > 1) return launch_expand_long<DT, R>(st, y, ld_y, part, L.slice, ksl, TB, h_out, scale);
+  if (P.ksl > 1) return launch_expand_long<DT, R>(st, y, ld_y, part, L.slice, P.ksl, TB, h_out, scale);
   return launch_expand_long<DT, R>(st, y, ld_y, v_long, 0, 1, TB, h_out, scale);
 }
 
@@ -1506,6 +1582,29 @@ hipError_t table_lora_add_device(hipStream_t st, int32_t dtype, int32_t r, void*
 
 }  // namespace sgmv_host
 
+extern "C" int sgmv_check_workspace(hipStream_t stream, void* workspace, int32_t* flags,
+                                    int32_t clear) {
+  if (!workspace) return SGMV_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return SGMV_ERR_WORKSPACE;
+  int st = check_device();
+  if (st) return st;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
+    return SGMV_ERR_HIP;  // a read-back cannot be captured
+  int32_t f = 0;
+  if (hipMemcpyAsync(&f, workspace, sizeof(f), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return SGMV_ERR_HIP;
+  if (clear && f != 0) {
+    const int32_t zero = 0;
+    if (hipMemcpyAsync(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+      return SGMV_ERR_HIP;
+  }
+  if (flags) *flags = f;
+  return f != 0 ? SGMV_ERR_DEVICE : SGMV_OK;
+}
+
 extern "C" size_t sgmv_workspace_bytes(int32_t n, int32_t h_in, int32_t r) {
   if (n < 0 || h_in < 8 || h_in > kMaxDim || !rank_ok(r)) return 0;
   return ws_layout(n, h_in, r).total;
@@ -1531,8 +1630,9 @@ extern "C" int sgmv_shrink(hipStream_t stream, int32_t dtype, float* v, const vo
       (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return SGMV_ERR_WORKSPACE;
   if ((st = check_device())) return st;
-  const Tables T{reinterpret_cast<const uint16_t* const*>(A_ptrs), seg_starts, perm, n,
-                 n_segments, min_seg_len, max_seg_len};
+  Tables T{reinterpret_cast<const uint16_t* const*>(A_ptrs), seg_starts, perm, n,
+           n_segments, min_seg_len, max_seg_len};
+  T.flag = static_cast<int32_t*>(workspace);
   return hip_status(dispatch<ShrinkOp>(dtype, r, stream, v, static_cast<const uint16_t*>(x), ld_x,
                                        T, h_in, L, static_cast<char*>(workspace)));
 }
@@ -1580,8 +1680,9 @@ extern "C" int sgmv_lora_add(hipStream_t stream, int32_t dtype, void* y, int64_t
       (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return SGMV_ERR_WORKSPACE;
   if ((st = check_device())) return st;
-  const Tables TA{reinterpret_cast<const uint16_t* const*>(A_ptrs), seg_starts, perm, n,
-                  n_segments, min_seg_len, max_seg_len};
+  Tables TA{reinterpret_cast<const uint16_t* const*>(A_ptrs), seg_starts, perm, n,
+            n_segments, min_seg_len, max_seg_len};
+  TA.flag = static_cast<int32_t*>(workspace);
   const Tables TB{reinterpret_cast<const uint16_t* const*>(B_ptrs), seg_starts, perm, n,
                   n_segments, min_seg_len, max_seg_len};
   return hip_status(dispatch<LoraOp>(dtype, r, stream, static_cast<uint16_t*>(y), ld_y,
@@ -1603,16 +1704,19 @@ extern "C" int sgmv_lora_add_ranked(hipStream_t stream, int32_t dtype, void* y, 
   int st;
   if ((st = check_dim(h_in, ld_x))) return st;
   if ((st = check_dim(h_out, ld_y))) return st;
-  size_t ws_need = 0;
+  int32_t r_max = 0;
   for (int32_t g = 0; g < n_groups; ++g) {
     const sgmv_rank_group& G = groups[g];
     if (!rank_ok(G.r)) return SGMV_ERR_UNSUPPORTED;
     if ((st = check_segments(G.n, G.n_segments, G.min_seg_len, G.max_seg_len))) return st;
     if (G.row0 < 0 || G.seg0 < 0 || G.starts0 < 0 || static_cast<int64_t>(G.row0) + G.n > n)
       return SGMV_ERR_SHAPE;
-    if (G.n > 0) ws_need = std::max(ws_need, ws_layout(G.n, h_in, G.r).total);
+    if (G.n > 0) r_max = std::max(r_max, G.r);
   }
-  if (n == 0 || ws_need == 0) return SGMV_OK;
+  if (n == 0 || r_max == 0) return SGMV_OK;
+  // the buffer the header asks for: room for a call of all n rows at the largest rank
+  const WsLayout L_all = ws_layout(n, h_in, r_max);
+  const size_t ws_need = L_all.total;
   if (!y || !x || !A_ptrs || !B_ptrs || !seg_starts || !perm) return SGMV_ERR_NULL;
   if (!aligned16(x) || !aligned16(y)) return SGMV_ERR_ALIGNMENT;
   if (ranges_overlap(x, matrix_bytes(n, ld_x, h_in), y, matrix_bytes(n, ld_y, h_out)))
@@ -1622,9 +1726,10 @@ extern "C" int sgmv_lora_add_ranked(hipStream_t stream, int32_t dtype, void* y, 
     return SGMV_ERR_WORKSPACE;
   if ((st = check_device())) return st;
   auto tables = [&](const sgmv_rank_group& G, const void* const* P) {
-    return Tables{reinterpret_cast<const uint16_t* const*>(P) + G.seg0, seg_starts + G.starts0,
-                  perm + G.row0, G.n, G.n_segments, G.min_seg_len, G.max_seg_len, nullptr,
-                  true};
+    Tables T{reinterpret_cast<const uint16_t* const*>(P) + G.seg0, seg_starts + G.starts0,
+             perm + G.row0, G.n, G.n_segments, G.min_seg_len, G.max_seg_len, nullptr, true};
+    T.flag = static_cast<int32_t*>(workspace);
+    return T;
   };
   // The groups touch disjoint rows.  Under graph capture, with room for every group's
   // scratch side by side in the workspace, each group's short and long chains run on
@@ -1639,12 +1744,15 @@ extern "C" int sgmv_lora_add_ranked(hipStream_t stream, int32_t dtype, void* y, 
     gr[g] = G.r;
     if (G.n > 0) chains += (G.min_seg_len < kLongMin) + (G.max_seg_len >= kLongMin);
   }
+  // Side by side, the groups' scratch must end where the scratch of one call of all n rows
+  // at the largest rank would: then, like that call, it stays clear of the counters and
+  // tagged partials of every call the buffer is sized for.
   const bool fits =
-      ranked_side_by_side(gn.data(), gr.data(), n_groups, h_in, goff.data()) <= workspace_bytes;
+      ranked_side_by_side(gn.data(), gr.data(), n_groups, h_in, goff.data()) <= L_all.table_end;
   SideStream side;
   if (fits && chains > 1) {
     if (side.fork(stream, chains - 1) != hipSuccess) {
-      side.join(stream);
+      (void)side.join(stream);
       return SGMV_ERR_HIP;
     }
   }
@@ -1675,7 +1783,7 @@ extern "C" int sgmv_lora_add_ranked(hipStream_t stream, int32_t dtype, void* y, 
     const hipError_t ej = side.join(stream);
     return (e == hipSuccess && ej == hipSuccess) ? SGMV_OK : SGMV_ERR_HIP;
   }
-  side.join(stream);
+  if (side.join(stream) != hipSuccess) return SGMV_ERR_HIP;
   for (int32_t g = 0; g < n_groups; ++g) {
     const sgmv_rank_group& G = groups[g];
     if (G.n == 0) continue;

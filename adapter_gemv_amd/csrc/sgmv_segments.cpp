@@ -23,6 +23,7 @@ extern "C" const char* sgmv_status_string(int status) {
     case SGMV_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case SGMV_ERR_ALIAS: return "output overlaps an input";
     case SGMV_ERR_HIP: return "HIP runtime error";
+    case SGMV_ERR_DEVICE: return "a device-side check flagged the workspace";
     default: return "unknown status";
   }
 }

@@ -82,6 +82,20 @@ def sgmv_workspace_bytes(n: int, h_in: int, r: int) -> int:
     return int(_lib.lib().sgmv_workspace_bytes(int(n), int(h_in), int(r)))
 
 
+def sgmv_check_workspace(stream, workspace, flags, clear) -> int:
+    return _lib.lib().sgmv_check_workspace(stream, workspace, flags, int(clear))
+
+
+def workspace_flags(workspace, clear: bool = False, stream=None) -> int:
+    """The workspace's device-side flag bits (FLAG_* in ``_lib``), read after every call
+    enqueued on ``stream`` has finished; ``clear`` resets them to zero."""
+    f = np.zeros(1, np.int32)
+    st = sgmv_check_workspace(_stream_handle(stream), workspace.data_ptr(), _ptr(f), clear)
+    if st not in (_lib.OK, _lib.ERR_DEVICE):
+        check(st, "sgmv_check_workspace")
+    return int(f[0])
+
+
 def sgmv_shrink(stream, dtype, v, x, ld_x, A_ptrs, seg_starts, perm, n, n_segments,
                 min_seg_len, max_seg_len, h_in, r, workspace, workspace_bytes) -> int:
     return _lib.lib().sgmv_shrink(stream, dtype, v, x, ld_x, A_ptrs, seg_starts, perm, n,

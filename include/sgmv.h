@@ -42,13 +42,18 @@
  * the caller, except where a comment says "host".  The library allocates no device
  * memory, keeps no per-call state and never synchronises: device calls are enqueued on
  * `stream` and return.  Calls that share a workspace must be ordered (same stream).
- * Streams: a fused call (sgmv_lora_add, sgmv_lora_add_ranked, sgmv_lora_add_pool above
- * 64 rows) whose batch has segments both shorter and longer than 16 rows, made while
- * `stream` is being captured into a HIP graph, runs its short-segment kernels on a
- * second stream that the library creates once per device (default priority, on the
- * first such call that is not captured) and joins it back into `stream` before
- * returning: the captured graph orders everything after the call exactly as `stream`
- * alone would, and its two branches overlap on the GPU.  Eager calls use `stream` only.
+ * Streams (the one state the library holds): a fused call (sgmv_lora_add,
+ * sgmv_lora_add_ranked, sgmv_lora_add_pool above 64 rows) whose batch has segments both
+ * shorter and longer than 16 rows, or a mixed-rank call with several rank groups, made
+ * while `stream` is being captured into a HIP graph, runs some of its kernel chains on
+ * side streams and joins them back into `stream` before returning: the captured graph
+ * orders everything after the call exactly as `stream` alone would, and its branches
+ * overlap on the GPU.  Eager calls use `stream` only.  The side streams (four per device,
+ * default priority, non-blocking) and their events are created by the first fused call on
+ * a device that is not being captured and live until the process ends; a call captured
+ * before that runs every chain on `stream`, so such a graph replays its chains one after
+ * another.  A process-wide mutex keeps each fused call's fork-launch-join sequence whole
+ * when host threads call concurrently.
  *
  * Errors: every argument check is done on the host before any HIP call, so a
  * rejected call has no effect.  The contents of device tables (seg_starts, perm,
@@ -83,11 +88,27 @@ extern "C" {
 #define SGMV_ERR_WORKSPACE 6   /* workspace missing, too small or not 256-byte aligned */
 #define SGMV_ERR_ALIAS 7       /* an output overlaps an input */
 #define SGMV_ERR_HIP 8         /* a HIP runtime call or kernel launch failed (e.g. no device) */
+#define SGMV_ERR_DEVICE 9      /* sgmv_check_workspace: a device-side check set a flag bit */
 
-/* Version of this interface (SGMV_ABI_VERSION of the library that was built). */
+/*
+ * Flag bits of the workspace's first int32, set by device-side checks of calls that ran
+ * on it (a set bit means some rows of some call were not computed as asked).  No kernel
+ * clears them; sgmv_check_workspace reads and optionally clears them.
+ */
+#define SGMV_FLAG_WAIT_TIMEOUT 1 /* one-launch decode path: a bounded wait for partial sums
+                                    ran out (the rows it served got wrong values) */
+#define SGMV_FLAG_ADAPTER_ID 2   /* device ids: a row's id lay outside [0, n_adapters) and
+                                    the row was left unchanged */
+#define SGMV_FLAG_SEG_BOUNDS 4   /* host tables: a segment's length contradicted the
+                                    caller's min_seg_len / max_seg_len (a long segment with
+                                    max_seg_len < 16, or a short one with min_seg_len >= 16);
+                                    its rows were not computed */
+
+/* Version of this interface (SGMV_ABI_VERSION of the library that was built).  Library
+ * plumbing: no passage of the pages defines it. */
 int sgmv_abi_version(void);
 
-/* Static English text for a status code; never NULL. */
+/* Static English text for a status code; never NULL.  Library plumbing. */
 const char* sgmv_status_string(int status);
 
 /*
@@ -153,7 +174,10 @@ int sgmv_build_segments_ranked(const int32_t* adapter_ids, int32_t n, int32_t n_
                                int32_t* seg_adapter, sgmv_rank_group* groups, int32_t* n_groups);
 
 /*
- * Per-segment pointer table (host): seg_ptrs[s] = adapter_base[seg_adapter[s]].
+ * Per-segment pointer table (host): seg_ptrs[s] = adapter_base[seg_adapter[s]].  This is
+ * the "gather" of SGMV: each segment reads its own adapter's weights (paper summary,
+ * "Summary": the low-rank additions of different adapters computed together in one
+ * batch; project overview, "How It Works": A and B applied through SGMV).
  *   adapter_base  host uint64[n_adapters]: device address of each adapter's A (or B)
  *   seg_ptrs      host uint64[n_segments] out
  * Returns SGMV_ERR_ADAPTER_ID for an entry of seg_adapter out of range and
@@ -163,8 +187,19 @@ int sgmv_build_ptr_table(const uint64_t* adapter_base, int32_t n_adapters,
                          const int32_t* seg_adapter, int32_t n_segments, uint64_t* seg_ptrs);
 
 /*
+ * Device-side check results of the calls that ran on `workspace` (library plumbing):
+ * waits for everything enqueued on `stream`, reads the workspace's flag word into *flags
+ * (host; may be NULL) and, if `clear` is nonzero, resets it to zero.  Returns SGMV_OK when
+ * no flag is set, SGMV_ERR_DEVICE when one is (see SGMV_FLAG_*), SGMV_ERR_HIP if the
+ * stream is being captured or a copy fails.  Synchronising: not for use under capture.
+ */
+int sgmv_check_workspace(hipStream_t stream, void* workspace, int32_t* flags, int32_t clear);
+
+/*
  * Bytes of device workspace that sgmv_shrink, sgmv_lora_add, sgmv_lora_add_ranked and
- * sgmv_lora_add_pool need for calls of up to n rows, h_in and rank r: float32 split-K
+ * sgmv_lora_add_pool need for calls of up to n rows, h_in and rank r.  Library plumbing
+ * for the shrink's split-K (v = x @ A[a] summed over K chunks, the shrink of the paper
+ * summary's "Summary"): float32 split-K
  * partial sums, device-built segment tables, a few counters, and the decode path's
  * tagged partial sums, which sit at the end of the buffer.  The workspace must be 256-byte aligned and zero-filled once before its first
  * use; every call leaves it ready for the next one.  One workspace may serve any mix of
@@ -174,9 +209,14 @@ int sgmv_build_ptr_table(const uint64_t* adapter_base, int32_t n_adapters,
 size_t sgmv_workspace_bytes(int32_t n, int32_t h_in, int32_t r);
 
 /*
- * Shrink only: v[i, :] = x[perm[i], :] @ A[segment of i]   (float32, sorted order).
+ * Shrink only: v[i, :] = x[perm[i], :] @ A[segment of i]   (float32, sorted order): the
+ * first product of the low-rank add-on x @ A @ B (project overview, "How It Works": the
+ * two smaller matrices A and B; paper summary, "Summary": computed per adapter for the
+ * grouped requests).
  *   v  device float32 [n, r] out, row i = sorted position i, overwritten
- * Other arguments as described above.  v must not overlap x.
+ * Other arguments as described above.  v must not overlap x.  A segment whose length
+ * contradicts min_seg_len / max_seg_len is not computed and sets SGMV_FLAG_SEG_BOUNDS in
+ * the workspace (see sgmv_check_workspace).
  */
 int sgmv_shrink(hipStream_t stream, int32_t dtype, float* v,
                 const void* x, int64_t ld_x, const void* const* A_ptrs,
@@ -185,9 +225,12 @@ int sgmv_shrink(hipStream_t stream, int32_t dtype, float* v,
                 int32_t h_in, int32_t r, void* workspace, size_t workspace_bytes);
 
 /*
- * Expand only: y[perm[i], :] += scale * v[i, :] @ B[segment of i], rounded once.
+ * Expand only: y[perm[i], :] += scale * v[i, :] @ B[segment of i], rounded once: the
+ * second product of the low-rank add-on, added to the backbone output (project overview,
+ * "How It Works"; paper summary, "Summary").
  *   v  device float32 [n, r], row i = sorted position i (as written by sgmv_shrink)
- * y must not overlap v.
+ * y must not overlap v.  This call has no workspace, so min_seg_len / max_seg_len must be
+ * true bounds of the tables (sgmv_shrink on the same tables flags them if they are not).
  */
 int sgmv_expand(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y, const float* v,
                 const void* const* B_ptrs, const int32_t* seg_starts, const int32_t* perm,
@@ -196,7 +239,11 @@ int sgmv_expand(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y, const 
 
 /*
  * Fused LoRA add-on: shrink then expand, y[t] += scale * (x[t] @ A[a_t]) @ B[a_t]
- * for every row, with v kept in float32 in the workspace.  x and y must not overlap.
+ * for every row, with v kept in float32 in the workspace (paper summary, "Summary": the
+ * per-adapter low-rank additions of one batch computed together, same-adapter requests
+ * grouped; project overview, "How It Works").  x and y must not overlap.  A segment whose
+ * length contradicts min_seg_len / max_seg_len is not computed and sets
+ * SGMV_FLAG_SEG_BOUNDS in the workspace (see sgmv_check_workspace).
  */
 int sgmv_lora_add(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
                   const void* x, int64_t ld_x,
@@ -207,7 +254,9 @@ int sgmv_lora_add(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
                   void* workspace, size_t workspace_bytes);
 
 /*
- * Fused LoRA add-on for a mixed-rank batch: for every group g of `groups` (host array,
+ * Fused LoRA add-on for a mixed-rank batch (paper summary, "Summary": one batch mixes
+ * requests of many adapters; the pages fix no common rank, so adapters of ranks 16, 32
+ * and 64 may share a call): for every group g of `groups` (host array,
  * as written by sgmv_build_segments_ranked, with the scales filled in), the rows of g get
  * y[t] += g.scale * (x[t] @ A[a_t]) @ B[a_t] with A[a_t] of g.r columns.  Called eagerly,
  * the groups run one after another on `stream`, each as sgmv_lora_add on its part of the
@@ -252,7 +301,9 @@ int sgmv_build_segments_device(hipStream_t stream, const int32_t* adapter_ids, i
 
 /*
  * Fused LoRA add-on for adapter ids in device memory and adapters in pools,
- * y[t] += scale * (x[t] @ A[a_t]) @ B[a_t], with no host work that depends on the ids
+ * y[t] += scale * (x[t] @ A[a_t]) @ B[a_t] (project overview, "How It Works"; paper
+ * summary, "Summary" and idea I2: the batch grouped by adapter, each group's low-rank
+ * addition computed together), with no host work that depends on the ids
  * (the call can be captured in a HIP graph and replayed with new ids):
  *   n <= 64:        one kernel launch: segment metadata, shrink and expand (decode);
  *   64 < n <= 4096: one workgroup groups the rows by adapter (a hash table in LDS; the
@@ -267,9 +318,14 @@ int sgmv_build_segments_device(hipStream_t stream, const int32_t* adapter_ids, i
  *   B_pool       device: adapter a's B ([h_out, r] row-major) at B_pool + a * B_stride
  *   workspace    as for sgmv_lora_add (sgmv_workspace_bytes(n, h_in, r) bytes,
  *                zero-filled once); calls sharing a workspace must be stream-ordered
- * Rows whose id lies outside [0, n_adapters) are left unchanged and set the int32 at
- * the start of the workspace to 2 (a device-side wait that timed out sets it to 1;
- * it is never cleared by the library).  Returns SGMV_ERR_SHAPE for n > 4096.
+ * Rows whose id lies outside [0, n_adapters) are left unchanged and set
+ * SGMV_FLAG_ADAPTER_ID in the workspace's flag word; a bounded device-side wait of the
+ * one-launch kernel that ran out sets SGMV_FLAG_WAIT_TIMEOUT (the call still returns
+ * SGMV_OK: it is asynchronous; sgmv_check_workspace reports both).
+ * Stacked multi-layer pools: for adapters stored as [layers, P, r, h_in] (A) and
+ * [layers, P, h_out, r] (B), layer l's pools are A_pool + l * P * A_stride and
+ * B_pool + l * P * B_stride elements (each still 16-byte aligned); pass those with the
+ * same strides, one call per layer.  Returns SGMV_ERR_SHAPE for n > 4096.
  */
 int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
                        const void* x, int64_t ld_x, const int32_t* adapter_ids, int32_t n,

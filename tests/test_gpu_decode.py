@@ -372,17 +372,18 @@ def test_pool_large_exact_bit_exact(torch_cuda, dtype, r, kind, n):
     assert np.array_equal(_storage(y, dtype).view(np.uint16), want)
 
 
-@pytest.mark.parametrize("name", ["prefill13b_gateup", "mixed70b_r64_gate"])
+@pytest.mark.parametrize("name", [f"prefill13b_{p}" for p in synth.PREFILL13B_SHAPES])
 def test_pool_large_full_workloads(torch_cuda, name):
-    """The full prefill / mixed batches with device ids (2048 and 2112 rows)."""
+    """The full prefill batches with device ids (2048 rows), every row against the oracle
+    (the 70B mixed batch with device ids is compared in full with its host-table run)."""
+    from parity_util import compare_all_rows
     _say(f"[pool large full] {name}")
     p = FACT[name]()
     y = _upload(p).lora_add_pool()
     torch_cuda.cuda.synchronize()
-    got = oracle.decode(_storage(y, p.dtype), p.dtype)
-    rows = np.r_[0:64, np.random.default_rng(11).choice(np.arange(64, p.n), 64, replace=False)]
-    ref = oracle.lora_add(p.y[rows], p.x[rows], p.ids[rows], p.A, p.B, p.scale, p.dtype)
-    _assert_close(got[rows], ref, f"pool large full {name}")
+    compare_all_rows({"device ids": _storage(y, p.dtype)}, p.n,
+                     lambda rows: oracle.lora_add(p.y[rows], p.x[rows], p.ids[rows], p.A, p.B,
+                                                  p.scale, p.dtype), p.dtype, name)
 
 
 def test_pool_large_invalid_ids(torch_cuda):

@@ -77,18 +77,24 @@ MIXED = [f"mixed70b_r{r}_{proj}" for r in (16, 64) for proj in synth.MIXED70B_SH
 
 
 @pytest.mark.parametrize("name", MIXED)
-def test_mixed70b_sampled_rows(torch_cuda, name):
-    """Full-size mixed batch in the benchmark's launch configuration; the oracle is
-    evaluated on every decode row and 96 sampled prefill rows (rows are independent)."""
+def test_mixed70b_all_rows(torch_cuda, name):
+    """The full 70B mixed batch (2112 rows, every column) in the benchmark's launch
+    configuration, through host segment tables (sgmv_lora_add) and through device ids
+    (sgmv_lora_add_pool: device grouping + the same table kernels), both against the
+    oracle evaluated in blocks of rows (rows are independent)."""
+    from adapter_gemv_amd.device_problem import to_numpy_storage
+    from parity_util import compare_all_rows
     _say(f"[parity] {name}")
     p = FACT[name]()
-    _, y = _run_lora(p)
-    rng = np.random.default_rng(77)
-    rows = np.concatenate([np.arange(64), 64 + rng.choice(p.n - 64, 96, replace=False)])
-    rows.sort()
-    ref = oracle.lora_add(p.y[rows], p.x[rows], p.ids[rows], p.A, p.B, p.scale, p.dtype)
-    got = _y_f64(y[torch_cuda.as_tensor(rows, device=y.device)], p.dtype)
-    _assert_close(got, ref, name)
+    dp, y_tab = _run_lora(p)
+    y_dev = dp.lora_add_pool()
+    torch_cuda.cuda.synchronize()
+    outs = {"host tables": to_numpy_storage(y_tab, p.dtype),
+            "device ids": to_numpy_storage(y_dev, p.dtype)}
+    del y_tab, y_dev, dp
+    compare_all_rows(outs, p.n, lambda rows: oracle.lora_add(p.y[rows], p.x[rows], p.ids[rows],
+                                                             p.A, p.B, p.scale, p.dtype),
+                     p.dtype, name)
 
 
 # --------------------------------------------------------------------------------------
@@ -104,10 +110,15 @@ EXACT_CASES = [
     ("r64_decode", 12, 8192, 1024, 64, 12, "perm"),
     ("deep_k", 40, 28672, 264, 16, 3, "mixed"),
     ("deep_k_long", 150, 20480, 264, 16, 3, "mixed"),  # r = 16 with 64-row shrink tiles
+    # r = 16, short and long segments, 6144 < h_in <= 16384: the LDS-staged shrink with a
+    # reduce pass, ragged last tile
+    ("lds_r16_mixed", 150, 8200, 1032, 16, 12, "mixed"),
 ]
 
 
 def _ids(kind, n, P, rng):
+    if kind == "mixed70b":
+        return synth.mixed70b_ids(rng)
     if kind == "perm":
         return rng.permutation(n).astype(np.int32) % P
     if kind == "uniform":
@@ -174,6 +185,10 @@ RAGGED = [
                                                     # v written directly, padded stages
     (70, 16648, 520, 16, 2, "blocks", 8, False),    # r = 16 LDS-staged shrink, last chunk
                                                     # padded to a whole ring turn
+    (150, 8200, 1032, 16, 12, "mixed", 8, False),   # r = 16 LDS-staged shrink at
+                                                    # 6144 < h_in <= 16384 (short segments
+                                                    # present), ragged last tile
+    (2112, 8192, 1024, 16, 50, "mixed70b", 0, False),  # the 70B k/v shape at full size
 ]
 
 
@@ -362,9 +377,10 @@ def _mixed_ids(n_long, n_short_each, n_short_adapters, seed):
 
 
 # (r, h_in, h_out, long rows per segment, short rows per segment, short segments):
-#   r = 16, h_in = 8200: 17 GEMV slices (a reduce pass for the short rows) while the long
-#   rows' 4 slices are added by the MFMA expand itself;
-#   r = 32: few GEMV slices summed by the GEMV expand; r = 64: reduce passes on both sides
+#   r = 16, h_in = 8200: 17 GEMV slices and the LDS-staged shrink's many slices, each
+#   kind summed by its own reduce pass;
+#   r = 32: few GEMV slices summed by the GEMV expand, the long rows' few slices by the
+#   MFMA expand; r = 64: reduce passes on both sides
 GRAPH_MIXED = [(16, 8200, 1032, 520, 3, 9), (32, 1032, 2056, 40, 5, 4), (64, 2056, 1032, 70, 15, 3)]
 
 
@@ -403,3 +419,109 @@ def test_mixed_batch_graph_equals_eager(torch_cuda, r, h_in, h_out, n_long, n_sh
         assert torch.equal(y, y_eager), f"replay {rep} differs from the eager call"
         _ = (dp.x.float() * 2).sum()
         torch.cuda.synchronize()
+
+
+# (r, h_in, h_out): both reduce passes of a mixed call (r = 16 with the LDS-staged shrink,
+# r = 64), and r = 32 (GEMV slices summed by the GEMV expand, long slices by the MFMA
+# expand)
+FLIP = [(16, 8200, 1032), (32, 1032, 2056), (64, 2056, 1032)]
+
+
+@pytest.mark.parametrize("r,h_in,h_out", FLIP)
+def test_graph_calls_whose_segments_change_kind(torch_cuda, r, h_in, h_out):
+    """Two calls captured in one graph on one workspace, with different ids: the rows at
+    the start of the sorted order belong to a 40-row (long) segment in the first call and
+    to a 5-row (short) one in the second, and the reverse for a later segment.  Under
+    capture each call's short and long chains run side by side; every slice count the
+    reduce passes read must be the current call's.  Every replay must equal the eager
+    calls bit for bit (eager: fresh workspaces)."""
+    torch = torch_cuda
+    from adapter_gemv_amd import sgmv
+    _say(f"[graph flip] r={r} h_in={h_in} h_out={h_out}")
+    rng = np.random.default_rng(500 + r)
+    short = np.repeat(np.arange(2, 10, dtype=np.int32), 3)
+    ids1 = rng.permutation(np.concatenate([np.zeros(40, np.int32), np.ones(5, np.int32), short]))
+    ids2 = rng.permutation(np.concatenate([np.zeros(5, np.int32), np.ones(40, np.int32), short]))
+    n = ids1.size
+    assert ids2.size == n
+    p = synth.random_problem((94, r), n=n, h_in=h_in, h_out=h_out, r=r, n_adapters=10,
+                             dtype="bf16", ids=ids1)
+    dp = _upload(p)
+    b1 = sgmv.Batch.build(ids1, dp.A, dp.B)
+    b2 = sgmv.Batch.build(ids2, dp.A, dp.B)
+    eager = []
+    for b in (b1, b2):
+        y = dp.fresh_y()
+        sgmv.lora_add(y, dp.x, b, p.scale, sgmv.make_workspace(n, h_in, r, dp.x.device))
+        eager.append(y)
+    torch.cuda.synchronize()
+    for b, y, ids in zip((b1, b2), eager, (ids1, ids2)):
+        ref = oracle.lora_add(p.y, p.x, ids, p.A, p.B, p.scale, p.dtype)
+        _assert_close(_y_f64(y, p.dtype), ref, f"flip r={r} eager")
+    ws = sgmv.make_workspace(n, h_in, r, dp.x.device)
+    y1, y2 = dp.fresh_y(), dp.fresh_y()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # creates the library's side streams before the capture
+        sgmv.lora_add(y1, dp.x, b1, p.scale, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sgmv.lora_add(y1, dp.x, b1, p.scale, ws)
+        sgmv.lora_add(y2, dp.x, b2, p.scale, ws)
+    for rep in range(4):
+        y1.copy_(dp.y0)
+        y2.copy_(dp.y0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _say(f"[graph flip] r={r} replay {rep}")
+        assert torch.equal(y1, eager[0]), f"replay {rep}: first call differs from eager"
+        assert torch.equal(y2, eager[1]), f"replay {rep}: second call differs from eager"
+        _ = (dp.x.float() * 2).sum()
+        torch.cuda.synchronize()
+    assert sgmv.workspace_flags(ws) == 0
+
+
+@pytest.mark.parametrize("wrong", ["max_below_16", "min_at_least_16"])
+def test_segment_bounds_that_contradict_the_tables_are_flagged(torch_cuda, wrong):
+    """min_seg_len / max_seg_len only choose which kernels run.  A caller bound that hides
+    a segment kind leaves that kind's rows uncomputed, and the kernels that do run flag
+    the workspace (SGMV_FLAG_SEG_BOUNDS); rows of the other kind are still right."""
+    torch = torch_cuda
+    from adapter_gemv_amd import _lib, sgmv
+    # one 20-row segment and short ones (n = 40, S = 5), or one 50-row segment and a
+    # 14-row one (n = 64, S = 2); both pass the host's pigeonhole check
+    if wrong == "max_below_16":
+        ids = np.concatenate([np.zeros(20, np.int32), np.repeat(np.arange(1, 5, dtype=np.int32), 5)])
+    else:
+        ids = np.concatenate([np.zeros(50, np.int32), np.ones(14, np.int32)])
+    p = synth.random_problem((95, len(ids)), n=ids.size, h_in=1032, h_out=520, r=16,
+                             n_adapters=5, dtype="bf16", ids=ids)
+    dp = _upload(p)
+    t = dp.batch.table
+    lo, hi = (t.min_seg_len, 15) if wrong == "max_below_16" else (16, t.max_seg_len)
+    ws = sgmv.make_workspace(p.n, p.h_in, 16, dp.x.device)
+    y = dp.fresh_y()
+    st = sgmv.sgmv_lora_add(sgmv._stream_handle(), _lib.BF16, y.data_ptr(), y.stride(0),
+                            dp.x.data_ptr(), dp.x.stride(0), dp.batch.A_ptrs_addr,
+                            dp.batch.B_ptrs_addr, dp.batch.seg_starts_addr, dp.batch.perm_addr,
+                            p.n, t.n_segments, lo, hi, p.h_in, p.h_out, 16, p.scale,
+                            ws.data_ptr(), ws.numel())
+    assert st == _lib.OK
+    torch.cuda.synchronize()
+    assert sgmv.workspace_flags(ws) == _lib.FLAG_SEG_BOUNDS
+    counts = np.bincount(ids)
+    computed = (counts[ids] < 16) if wrong == "max_below_16" else (counts[ids] >= 16)
+    got = _y_f64(y, p.dtype)
+    ref = oracle.lora_add(p.y[computed], p.x[computed], p.ids[computed], p.A, p.B, p.scale,
+                          p.dtype)
+    _assert_close(got[computed], ref, f"bounds {wrong}: rows computed")
+    assert np.array_equal(got[~computed], oracle.decode(p.y[~computed], p.dtype))
+    # sgmv_check_workspace reports the flag and clears it on request
+    f = np.zeros(1, np.int32)
+    assert sgmv.sgmv_check_workspace(sgmv._stream_handle(), ws.data_ptr(), f.ctypes.data, 1) \
+        == _lib.ERR_DEVICE
+    assert int(f[0]) == _lib.FLAG_SEG_BOUNDS
+    assert sgmv.workspace_flags(ws) == 0

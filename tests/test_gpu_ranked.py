@@ -1,6 +1,6 @@
 """GPU tests of the mixed-rank call (sgmv_build_segments_ranked + sgmv_lora_add_ranked):
 parity with the fp64 oracle, bit equality with one sgmv_lora_add per rank on that rank's
-rows, the 70B mixed batch with ranks 16 and 64 at full size (sampled rows) and HIP graph
+rows, the 70B mixed batch with ranks 16 and 64 at full size (every row) and HIP graph
 replay."""
 import sys
 
@@ -122,20 +122,37 @@ def test_ranked_equals_one_call_per_rank(torch_cuda, name):
     assert torch.equal(y, want)
 
 
-@pytest.mark.parametrize("proj", ["gate", "down", "k"])
+@pytest.mark.parametrize("proj", list(synth.MIXED70B_SHAPES))
 def test_ranked_mixed70b_full_size(torch_cuda, proj):
-    """The 70B mixed batch with ranks 16 and 64 in one call, at full size: every decode
-    row and 96 prefill rows against the oracle."""
+    """The 70B mixed batch with ranks 16 and 64 in one call, at full size: all 2112 rows
+    and every column against the oracle (evaluated in blocks of rows), eagerly and
+    replayed from a HIP graph (the rank groups' chains side by side)."""
+    torch = torch_cuda
+    from adapter_gemv_amd import sgmv
+    from parity_util import compare_all_rows
     q = synth.mixed70b_ranked(proj)
     _say(f"[ranked full] {q.name} n={q.n} h_in={q.h_in} h_out={q.h_out}")
     d = Dev(q)
     y = d.run()
-    torch_cuda.cuda.synchronize()
-    rng = np.random.default_rng(35)
-    rows = np.concatenate([np.arange(64), 64 + rng.choice(q.n - 64, 96, replace=False)])
-    got = oracle.decode(_storage(y, q.dtype), q.dtype)[rows]
-    ref = oracle.lora_add_ranked(q.y[rows], q.x[rows], q.ids[rows], q.pools, q.scales, q.dtype)
-    _assert_close(got, ref, q.name)
+    ws = sgmv.make_workspace(q.n, q.h_in, 64, torch.device("cuda"))
+    yg = d.y0.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        d.run(yg, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        d.run(yg, ws)
+    yg.copy_(d.y0)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    outs = {"eager": _storage(y, q.dtype), "graph": _storage(yg, q.dtype)}
+    del y, yg, g
+    compare_all_rows(outs, q.n, lambda rows: oracle.lora_add_ranked(
+        q.y[rows], q.x[rows], q.ids[rows], q.pools, q.scales, q.dtype), q.dtype, q.name)
 
 
 def test_ranked_graph_replay(torch_cuda):

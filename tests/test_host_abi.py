@@ -132,6 +132,29 @@ def test_workspace_layout_sharing_rule(tmp_path):
     assert out.returncode == 0 and out.stdout.startswith("ok"), out.stdout
 
 
+def test_host_code_under_sanitizers(tmp_path):
+    """The host code that needs no GPU (segment builders, pointer table, argument checks,
+    workspace layout) built with AddressSanitizer and UndefinedBehaviorSanitizer and run
+    over random and edge-case inputs, every rejection included."""
+    import shutil
+    import subprocess
+    cxx = shutil.which("g++")
+    if cxx is None:
+        pytest.skip("g++ not found")
+    exe = str(tmp_path / "host_sanitize_check")
+    subprocess.run([cxx, "-O1", "-g", "-std=c++17", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-Wall", "-Werror",
+                    "-I/opt/rocm/include", "-D__HIP_PLATFORM_AMD__",
+                    os.path.join(ROOT, "tests", "host_sanitize_check.cpp"),
+                    os.path.join(ROOT, "adapter_gemv_amd", "csrc", "sgmv_segments.cpp"),
+                    "-o", exe], check=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    env.pop("LD_PRELOAD", None)
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=120, env=env)
+    assert out.returncode == 0 and out.stdout.startswith("ok"), out.stdout + out.stderr
+
+
 # --------------------------------------------------------------------------------------
 # validation: every one of these returns before any HIP call
 # --------------------------------------------------------------------------------------
@@ -288,6 +311,24 @@ def test_lora_add_host_ids_valid_call_without_device_is_hip_error():
     assert _host_ids() == _lib.ERR_HIP
 
 
+def test_check_workspace_rejects():
+    L = _lib.lib()
+    assert L.sgmv_check_workspace(None, None, None, 0) == _lib.ERR_NULL
+    assert L.sgmv_check_workspace(None, WS + 16, None, 0) == _lib.ERR_WORKSPACE
+
+
+@pytest.mark.skipif(not _no_gpu_visible(), reason="needs a machine without a GPU: the fake "
+                    "address would be read")
+def test_check_workspace_without_device_is_hip_error():
+    assert _lib.lib().sgmv_check_workspace(None, WS, None, 0) == _lib.ERR_HIP
+
+
+def test_status_strings_cover_every_code():
+    for code in range(0, 10):
+        assert sgmv.sgmv_status_string(code) != "unknown status", code
+    assert sgmv.sgmv_status_string(10) == "unknown status"
+
+
 def test_build_segments_device_rejects():
     L = _lib.lib()
     assert L.sgmv_build_segments_device(None, TAB, 4097, 4, V, V, V, V) == _lib.ERR_SHAPE
@@ -360,6 +401,10 @@ RANKED_REJECTS = [
     ("dtype", [G16], dict(dtype=5), _lib.ERR_UNSUPPORTED),
     ("ws for r=16 only", [G16, G64], dict(workspace_bytes=sgmv.sgmv_workspace_bytes(64, 4096, 16)),
      _lib.ERR_WORKSPACE),
+    # room for the largest group alone is not the buffer the header asks for (all rows at
+    # the largest rank): side-by-side scratch could reach the decode path's partial sums
+    ("ws per group only", [G16, G64],
+     dict(workspace_bytes=sgmv.sgmv_workspace_bytes(32, 4096, 64)), _lib.ERR_WORKSPACE),
     ("alias", [G16, G64], dict(y=X + 64), _lib.ERR_ALIAS),
     ("h_in%8", [G16], dict(h_in=4092, ld_x=4092), _lib.ERR_ALIGNMENT),
 ]
