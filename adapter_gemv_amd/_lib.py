@@ -57,6 +57,9 @@ SIGNATURES = {
     "sgmv_lora_add_host_ids": (ctypes.c_int, [_p, _i32, _p, _i64, _p, _i64, _p, _i32, _p, _i64,
                                               _p, _i64, _i32, _i32, _i32, _i32, ctypes.c_float,
                                               _p, _sz]),
+    "sgmv_lora_add_host_ids_noalloc": (ctypes.c_int, [_p, _i32, _p, _i64, _p, _i64, _p, _i32,
+                                                      _p, _i64, _p, _i64, _i32, _i32, _i32,
+                                                      _i32, ctypes.c_float]),
 }
 
 

@@ -24,6 +24,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/sgmv.h"
 #include "sgmv_checks.h"
@@ -802,11 +803,11 @@ extern "C" int sgmv_build_segments_device(hipStream_t stream, const int32_t* ada
 
 namespace {
 
-// Host checks shared by the pool entry points (no HIP call).
-int check_pool_call(int32_t dtype, void* y, int64_t ld_y, const void* x, int64_t ld_x,
+// Host checks of the pool entry points' arguments other than the workspace (no HIP call).
+int check_pool_args(int32_t dtype, void* y, int64_t ld_y, const void* x, int64_t ld_x,
                     const int32_t* adapter_ids, int32_t n, const void* A_pool, int64_t A_stride,
                     const void* B_pool, int64_t B_stride, int32_t n_adapters, int32_t h_in,
-                    int32_t h_out, int32_t r, void* workspace, size_t workspace_bytes) {
+                    int32_t h_out, int32_t r) {
   if (dtype != SGMV_F16 && dtype != SGMV_BF16) return SGMV_ERR_UNSUPPORTED;
   if (!rank_ok(r)) return SGMV_ERR_UNSUPPORTED;
   if (n < 0 || n > kDevSortMax || n_adapters <= 0 || n_adapters > (1 << 24)) return SGMV_ERR_SHAPE;
@@ -822,6 +823,17 @@ int check_pool_call(int32_t dtype, void* y, int64_t ld_y, const void* x, int64_t
     return SGMV_ERR_ALIGNMENT;
   if (ranges_overlap(x, matrix_bytes(n, ld_x, h_in), y, matrix_bytes(n, ld_y, h_out)))
     return SGMV_ERR_ALIAS;
+  return SGMV_OK;
+}
+
+// Host checks shared by the pool entry points (no HIP call).
+int check_pool_call(int32_t dtype, void* y, int64_t ld_y, const void* x, int64_t ld_x,
+                    const int32_t* adapter_ids, int32_t n, const void* A_pool, int64_t A_stride,
+                    const void* B_pool, int64_t B_stride, int32_t n_adapters, int32_t h_in,
+                    int32_t h_out, int32_t r, void* workspace, size_t workspace_bytes) {
+  int st = check_pool_args(dtype, y, ld_y, x, ld_x, adapter_ids, n, A_pool, A_stride, B_pool,
+                           B_stride, n_adapters, h_in, h_out, r);
+  if (st || n == 0) return st;
   if (!workspace || workspace_bytes < sgmv_workspace_bytes(n, h_in, r) ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return SGMV_ERR_WORKSPACE;
@@ -915,25 +927,18 @@ extern "C" int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, in
   return hip_status(e);
 }
 
-extern "C" int sgmv_lora_add_host_ids(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
-                                      const void* x, int64_t ld_x, const int32_t* adapter_ids,
-                                      int32_t n, const void* A_pool, int64_t A_stride,
-                                      const void* B_pool, int64_t B_stride, int32_t n_adapters,
-                                      int32_t h_in, int32_t h_out, int32_t r, float scale,
-                                      void* workspace, size_t workspace_bytes) {
-  if (n > kPoolMaxN) return SGMV_ERR_SHAPE;
-  int st = check_pool_call(dtype, y, ld_y, x, ld_x, adapter_ids, n, A_pool, A_stride, B_pool,
-                           B_stride, n_adapters, h_in, h_out, r, workspace, workspace_bytes);
-  if (st || n == 0) return st;
-  PoolIds ids;
-  for (int i = 0; i < kPoolMaxN; ++i) {
-    if (i < n && (adapter_ids[i] < 0 || adapter_ids[i] >= n_adapters)) return SGMV_ERR_ADAPTER_ID;
-    ids.id[i] = i < n ? adapter_ids[i] : -1;
-  }
-  if ((st = check_device())) return st;
-  // the kernel reads no id from memory: the device pointer stays unused
+namespace {
+
+// The one-launch kernel with host ids on a workspace that the caller's checks accepted.
+int run_host_ids(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y, const void* x,
+                 int64_t ld_x, const int32_t* adapter_ids, int32_t n, const void* A_pool,
+                 int64_t A_stride, const void* B_pool, int64_t B_stride, int32_t n_adapters,
+                 int32_t h_in, int32_t h_out, int32_t r, float scale, void* workspace,
+                 size_t workspace_bytes) {
   const PoolArgs p = pool_args(y, ld_y, x, ld_x, nullptr, n, A_pool, A_stride, B_pool, B_stride,
                                n_adapters, h_in, h_out, r, scale, workspace, workspace_bytes);
+  PoolIds ids;
+  for (int i = 0; i < kPoolMaxN; ++i) ids.id[i] = i < n ? adapter_ids[i] : -1;
   hipError_t e;
   if (dtype == SGMV_F16) {
     e = (r == 16) ? launch_ids<SGMV_F16, 16>(stream, p, ids)
@@ -945,4 +950,93 @@ extern "C" int sgmv_lora_add_host_ids(hipStream_t stream, int32_t dtype, void* y
                     : launch_ids<SGMV_BF16, 64>(stream, p, ids);
   }
   return hip_status(e);
+}
+
+// host-side check of host ids: each in [0, n_adapters)
+int check_host_ids(const int32_t* adapter_ids, int32_t n, int32_t n_adapters) {
+  for (int i = 0; i < n; ++i)
+    if (adapter_ids[i] < 0 || adapter_ids[i] >= n_adapters) return SGMV_ERR_ADAPTER_ID;
+  return SGMV_OK;
+}
+
+}  // namespace
+
+extern "C" int sgmv_lora_add_host_ids(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
+                                      const void* x, int64_t ld_x, const int32_t* adapter_ids,
+                                      int32_t n, const void* A_pool, int64_t A_stride,
+                                      const void* B_pool, int64_t B_stride, int32_t n_adapters,
+                                      int32_t h_in, int32_t h_out, int32_t r, float scale,
+                                      void* workspace, size_t workspace_bytes) {
+  if (n > kPoolMaxN) return SGMV_ERR_SHAPE;
+  int st = check_pool_call(dtype, y, ld_y, x, ld_x, adapter_ids, n, A_pool, A_stride, B_pool,
+                           B_stride, n_adapters, h_in, h_out, r, workspace, workspace_bytes);
+  if (st || n == 0) return st;
+  if ((st = check_host_ids(adapter_ids, n, n_adapters))) return st;
+  if ((st = check_device())) return st;
+  // the kernel reads no id from memory: the ids travel in its arguments
+  return run_host_ids(stream, dtype, y, ld_y, x, ld_x, adapter_ids, n, A_pool, A_stride, B_pool,
+                      B_stride, n_adapters, h_in, h_out, r, scale, workspace, workspace_bytes);
+}
+
+// ------------------------------------------------------------------------------------
+// allocation-free variant of sgmv_lora_add_host_ids
+// ------------------------------------------------------------------------------------
+// The one-launch kernel's scratch (flag word, per-row counters, tagged partial sums) in a
+// static device array instead of a caller workspace: zero when the code object is loaded,
+// and every call that completes leaves its counters and partial sums at zero again.  In
+// host code `scratch` names a host-side stand-in; its device address comes from
+// hipGetSymbolAddress, once per device, and only that address reaches a kernel.
+constexpr size_t kScratchPartMax = size_t(8) << 20;  // tagged partial sums, at most
+constexpr size_t kScratchBytes =
+    kWsPoolCounters + sizeof(int32_t) * kCounterInts * kMaxPoolRows + 256 + kScratchPartMax;
+static_assert(kScratchBytes % 256 == 0, "scratch layout");
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+// the device address of `scratch` on the current device (looked up once per device)
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return SGMV_ERR_HIP;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SGMV_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SGMV_OK;
+}
+
+}  // namespace
+
+extern "C" int sgmv_lora_add_host_ids_noalloc(hipStream_t stream, int32_t dtype, void* y,
+                                              int64_t ld_y, const void* x, int64_t ld_x,
+                                              const int32_t* adapter_ids, int32_t n,
+                                              const void* A_pool, int64_t A_stride,
+                                              const void* B_pool, int64_t B_stride,
+                                              int32_t n_adapters, int32_t h_in, int32_t h_out,
+                                              int32_t r, float scale) {
+  if (n > kPoolMaxN) return SGMV_ERR_SHAPE;
+  int st = check_pool_args(dtype, y, ld_y, x, ld_x, adapter_ids, n, A_pool, A_stride, B_pool,
+                           B_stride, n_adapters, h_in, h_out, r);
+  if (st || n == 0) return st;
+  if (pool_bytes(h_in, r) > kScratchPartMax) return SGMV_ERR_WORKSPACE;
+  if ((st = check_host_ids(adapter_ids, n, n_adapters))) return st;
+  if ((st = check_device())) return st;
+  if (stream) {
+    int sdev = -1, cur = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess || hipGetDevice(&cur) != hipSuccess ||
+        sdev != cur)
+      return SGMV_ERR_HIP;  // the scratch used is the current device's
+  }
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  return run_host_ids(stream, dtype, y, ld_y, x, ld_x, adapter_ids, n, A_pool, A_stride, B_pool,
+                      B_stride, n_adapters, h_in, h_out, r, scale, ws, kScratchBytes);
 }

@@ -543,3 +543,35 @@ def lora_add_host_ids(y, x, ids, A_pool, B_pool, scale: float, workspace=None, s
                                 workspace.data_ptr(), workspace.numel())
     check(st, "sgmv_lora_add_host_ids")
     return y
+
+
+def sgmv_lora_add_host_ids_noalloc(stream, dtype, y, ld_y, x, ld_x, adapter_ids, n, A_pool,
+                                   A_stride, B_pool, B_stride, n_adapters, h_in, h_out, r,
+                                   scale) -> int:
+    """``adapter_ids`` is a HOST address (int32[n], n <= 64); no workspace."""
+    return _lib.lib().sgmv_lora_add_host_ids_noalloc(stream, dtype, y, ld_y, x, ld_x,
+                                                     adapter_ids, n, A_pool, A_stride, B_pool,
+                                                     B_stride, n_adapters, h_in, h_out, r,
+                                                     float(scale))
+
+
+def lora_add_host_ids_noalloc(y, x, ids, A_pool, B_pool, scale: float, stream=None):
+    """As ``lora_add_host_ids`` with no workspace: the library's static device scratch
+    (calls on one GPU must not overlap in time)."""
+    ids_np = np.ascontiguousarray(
+        ids.numpy() if hasattr(ids, "numpy") else np.asarray(ids), dtype=np.int32)
+    n = int(x.shape[0])
+    _check_rows(x, n, "x")
+    _check_rows(y, n, "y")
+    if ids_np.ndim != 1 or ids_np.shape[0] != n:
+        raise ValueError("ids must be a host int32 array [n]")
+    r = int(A_pool.shape[1])
+    _check_adapters([A_pool[0]], [B_pool[0]], r, int(x.shape[1]), int(y.shape[1]),
+                    int(A_pool.shape[0]), int(B_pool.shape[0]))
+    st = sgmv_lora_add_host_ids_noalloc(_stream_handle(stream), dtype_code(y), y.data_ptr(),
+                                        y.stride(0), x.data_ptr(), x.stride(0), _ptr(ids_np), n,
+                                        A_pool.data_ptr(), A_pool.stride(0), B_pool.data_ptr(),
+                                        B_pool.stride(0), int(A_pool.shape[0]), x.shape[1],
+                                        y.shape[1], r, scale)
+    check(st, "sgmv_lora_add_host_ids_noalloc")
+    return y

@@ -354,6 +354,32 @@ int sgmv_lora_add_host_ids(hipStream_t stream, int32_t dtype, void* y, int64_t l
                            int64_t B_stride, int32_t n_adapters, int32_t h_in, int32_t h_out,
                            int32_t r, float scale, void* workspace, size_t workspace_bytes);
 
+/*
+ * Allocation-free variant of sgmv_lora_add_host_ids, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernel, arguments and result, with no workspace.  Its scratch (the
+ * flag word, one counter per row and the tagged float32 partial sums) is a static device
+ * array of the library, about 8.4 MB per GPU, held until the process ends; the device
+ * address is looked up once per device (the current device, which `stream` must belong
+ * to).  The array is zero when the library is loaded and every call that completes leaves
+ * its counters and partial sums at zero again, so no clearing is needed between calls.
+ * Calls on one GPU share the array: calls that overlap in time (different streams with no
+ * ordering between them) race and give wrong results, so order them.  No hipMalloc,
+ * hipFree or allocating library routine is called.  The flag word is not readable by the
+ * caller (host ids are checked on the host; only a device-side wait that ran out, which
+ * leaves wrong values, would set it).
+ *   Shapes: as sgmv_lora_add_host_ids (0 <= n <= 64), and the tagged partial sums of
+ *   (h_in, r), 8 * 64 * r * ceil(h_in * r / 8192) bytes, must fit 8 MiB: h_in up to
+ *   524288 at r = 16, 131072 at r = 32, 32768 at r = 64.  Larger shapes return
+ *   SGMV_ERR_WORKSPACE before any HIP call; other errors as sgmv_lora_add_host_ids, and
+ *   SGMV_ERR_HIP if `stream` belongs to another device than the current one.
+ */
+int sgmv_lora_add_host_ids_noalloc(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y,
+                                   const void* x, int64_t ld_x, const int32_t* adapter_ids,
+                                   int32_t n, const void* A_pool, int64_t A_stride,
+                                   const void* B_pool, int64_t B_stride, int32_t n_adapters,
+                                   int32_t h_in, int32_t h_out, int32_t r, float scale);
+
 #ifdef __cplusplus
 }
 #endif

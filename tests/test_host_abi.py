@@ -301,6 +301,45 @@ def test_lora_add_host_ids_rejects(name, kw, code):
     assert _host_ids(**kw) == code
 
 
+def _noalloc(**kw):
+    a = dict(stream=None, dtype=0, y=Y, ld_y=4096, x=X, ld_x=4096,
+             adapter_ids=HOST_IDS.ctypes.data, n=32, A_pool=V, A_stride=16 * 4096,
+             B_pool=V + (1 << 30), B_stride=16 * 4096, n_adapters=4096, h_in=4096, h_out=4096,
+             r=16, scale=2.0)
+    a.update(kw)
+    return sgmv.sgmv_lora_add_host_ids_noalloc(**a)
+
+
+NOALLOC_REJECTS = [
+    ("n>64", dict(n=65), _lib.ERR_SHAPE),
+    ("rank", dict(r=8), _lib.ERR_UNSUPPORTED),
+    ("ids null", dict(adapter_ids=None), _lib.ERR_NULL),
+    ("alias", dict(y=X + 64), _lib.ERR_ALIAS),
+    ("id too large", dict(adapter_ids=BAD_IDS.ctypes.data, n=4), _lib.ERR_ADAPTER_ID),
+    # partial sums of h_in = 32776 at r = 64 (8.4 MB) pass the static scratch's 8 MiB
+    ("beyond scratch r64", dict(r=64, h_in=32776, ld_x=32776, A_stride=64 * 32776,
+                                B_stride=64 * 4096), _lib.ERR_WORKSPACE),
+    ("beyond scratch r16", dict(h_in=524296, ld_x=524296, A_stride=16 * 524296),
+     _lib.ERR_WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", NOALLOC_REJECTS, ids=[r[0] for r in NOALLOC_REJECTS])
+def test_lora_add_host_ids_noalloc_rejects(name, kw, code):
+    assert _noalloc(**kw) == code
+
+
+@pytest.mark.skipif(not _no_gpu_visible(), reason="needs a machine without a GPU: the fake "
+                    "addresses would reach a kernel")
+def test_lora_add_host_ids_noalloc_largest_shapes_pass_the_checks():
+    """The largest shapes the static scratch holds pass every host check (and fail only for
+    want of a device here)."""
+    assert _noalloc(r=64, h_in=32768, ld_x=32768, A_stride=64 * 32768,
+                    B_stride=64 * 4096) == _lib.ERR_HIP
+    assert _noalloc(h_in=524288, ld_x=524288, A_stride=16 * 524288) == _lib.ERR_HIP
+    assert _noalloc(n=0) == _lib.OK
+
+
 def test_lora_add_host_ids_n_zero_is_ok():
     assert _host_ids(n=0) == _lib.OK
 
