@@ -46,6 +46,7 @@ METRIC = "SGMV shrink+expand us/call and HBM GB/s, h=4096 r=16 bs=32 distinct ad
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16/fp16 MFMA, AMD published figure
 ROTATION_BYTES = 1 << 30       # operand slots cycled per pass (> 2x the 256 MB MALL)
+FLUSH_BYTES = 1 << 30          # read before every timed replay (4x the 256 MB MALL)
 KERNEL_SRCS = [os.path.join(ROOT, "adapter_gemv_amd", "csrc", f)
                for f in ("sgmv_checks.h", "sgmv_device.h", "sgmv_kernels.hip", "sgmv_decode.hip")]
 
@@ -96,28 +97,49 @@ def cpu_baseline_1thread(p, budget_s: float) -> dict:
     return out
 
 
-def cpu_baseline(p, budget_s: float = 12.0):
+def cpu_baseline(p, budget_s: float = 12.0, runs: int = 5):
+    """The fp64 oracle on the same workload, its inputs decoded to float64 before the timed
+    region (x, y and every adapter the batch uses), so that what is timed is the oracle's
+    per-adapter products (x[rows] @ A) @ B and the y update: `runs` runs of repeated full
+    calls for budget_s / runs seconds each, the median of the runs' per-call times."""
     import oracle
     from threadpoolctl import threadpool_info
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.lora_add_problem(p)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    per_call = el / reps
-    threads = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
-    cores = int(threads[0]) if threads else 1
+    X, Y = oracle.decode(p.x, p.dtype), oracle.decode(p.y, p.dtype)
+    A64, B64 = oracle.DecodedPool(p.A, p.dtype), oracle.DecodedPool(p.B, p.dtype)
+    for a in np.unique(p.ids):
+        A64[int(a)], B64[int(a)]
+    oracle.lora_add_f64(Y, X, p.ids, A64, B64, p.scale)      # untimed first call
+    per_run, calls = [], 0
+    for _ in range(runs):
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.lora_add_f64(Y, X, p.ids, A64, B64, p.scale)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s / runs:
+                break
+        per_run.append(el / reps)
+        calls += reps
+    per_call = float(np.median(per_run))
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    cores = int(blas[0].get("num_threads", 1)) if blas else 1
+    lib = (f"{blas[0].get('internal_api')} {blas[0].get('version')}" if blas else "none")
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
     return {
         "value": round(algorithmic_bytes(p) / per_call / 1e9, 4),
         "unit": "GB/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"{reps} full calls of the same workload ({p.name}) in {el:.1f} s; "
-                  f"{per_call * 1e3:.2f} ms/call; numpy fp64, BLAS threads {cores}, "
-                  f"os.cpu_count() {os.cpu_count()}",
+        "sample": f"{p.name}, full calls, inputs decoded to fp64 before timing; median of "
+                  f"{runs} runs ({calls} calls in {budget_s:.0f} s): {per_call * 1e3:.3f} ms/call, "
+                  f"{algorithmic_flops(p) / per_call / 1e9:.2f} GFLOP/s; numpy fp64 on {lib}, "
+                  f"BLAS threads {cores}, os.cpu_count() {os.cpu_count()}, affinity {affinity}",
+        "us_per_call": round(per_call * 1e6, 2),
+        "runs_us": [round(t * 1e6, 2) for t in per_run],
     }
 
 
@@ -299,6 +321,12 @@ def kernel_pass(rig, k0: int, count: int, fixed_slot=None) -> float:
         run()
     g.replay()
     torch.cuda.synchronize()
+    # the untimed replay's operands out of the caches; the timed replay is queued behind
+    # the flush (warm calls: behind a spin kernel), so that its submission is not timed
+    if fixed_slot is None:
+        flush_caches(rig.device, wait=False)
+    else:
+        gpu_hold()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     g.replay()
@@ -307,29 +335,55 @@ def kernel_pass(rig, k0: int, count: int, fixed_slot=None) -> float:
     return e0.elapsed_time(e1) * 1e-3 / count
 
 
-def graph_time(body, count: int) -> float:
-    """Average time of one `body(k)` call, k = 0 .. count-1 captured in one HIP graph:
-    one untimed replay, then one replay bracketed by HIP events."""
+_FLUSH = {}
+
+
+def flush_caches(device, wait: bool = True) -> int:
+    """Read FLUSH_BYTES of a buffer used for nothing else (a reduction: the lines it leaves
+    in the caches are clean), so that whatever an untimed replay brought into the L2s and
+    the Infinity Cache is evicted before the timed one.  With wait=False the read is only
+    enqueued: a timed region whose start event follows it on the stream then begins with
+    the launches already queued behind the flush, so their submission is not timed.
+    Returns the bytes read."""
+    import torch
+    buf = _FLUSH.get(device)
+    if buf is None:
+        buf = _FLUSH[device] = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=device)
+    torch.cuda.synchronize()
+    buf.sum()
+    if wait:
+        torch.cuda.synchronize()
+    return FLUSH_BYTES
+
+
+def gpu_hold(us: float = 200.0, sync: bool = True) -> None:
+    """Enqueue a spin kernel of about `us` microseconds (no memory traffic), so that the
+    launches that follow are queued before the GPU reaches them and their submission is
+    not timed (for warm-cache timings, where a flush would evict what they reuse)."""
+    import torch
+    if sync:
+        torch.cuda.synchronize()
+    torch.cuda._sleep(int(us * 2400))   # cycles at about 2.4 GHz
+
+
+def queued_time(body, count: int, flush=None) -> float:
+    """Average time of one `body(k)` call, k = 0 .. count-1 launched one after another on
+    the current stream, queued behind a spin kernel long enough for the host to enqueue
+    them all (and, with `flush`, behind a cache flush), bracketed by HIP events: the
+    GPU runs them back to back with no launch gap.  body(0) runs once untimed first."""
     import torch
     stream = torch.cuda.current_stream()
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        body(0)
-    stream.wait_stream(side)
+    body(0)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for k in range(count):
-            body(k)
-    g.replay()
-    torch.cuda.synchronize()
+    if flush is not None:
+        flush_caches(flush, wait=False)
+    gpu_hold(100.0 + 40.0 * count, sync=flush is None)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    g.replay()
-    e1.record()
+    e0.record(stream)
+    for k in range(count):
+        body(k)
+    e1.record(stream)
     torch.cuda.synchronize()
-    del g
     return e0.elapsed_time(e1) * 1e-3 / count
 
 
@@ -337,7 +391,7 @@ def warm_call_time(rig, steps: int, use_graph: bool) -> float:
     """The SGMV call with warm caches: every call on the same slot (slot 1, not the
     parity slot), so its operands stay in the L2s and the Infinity Cache."""
     if use_graph:
-        return graph_time(lambda k: rig.step(1), steps)
+        return queued_time(lambda k: rig.step(1), steps)
     return kernel_pass(rig, 1, min(steps, 500), fixed_slot=1)
 
 
@@ -350,18 +404,20 @@ def floors(nbytes: int, device, count: int) -> dict:
     slots = max(2, min(256, -(-ROTATION_BYTES // (4 * half))))
     src = torch.ones((slots, half), dtype=torch.float16, device=device)
     dst = torch.empty_like(src)
-    t_copy = graph_time(lambda k: dst[k % slots].copy_(src[k % slots]), count)
+    # slot 0 is copied untimed first; the timed copies start at slot 1
+    t_copy = queued_time(lambda k: dst[(k + 1) % slots].copy_(src[(k + 1) % slots]), count,
+                         flush=device)
     one = torch.zeros(1, dtype=torch.float32, device=device)
-    t_launch = graph_time(lambda k: one.add_(1.0), count)
+    t_launch = queued_time(lambda k: one.add_(1.0), count)
     del src, dst
     torch.cuda.empty_cache()
     moved = 4 * half
     return {"copy_same_bytes": {"bytes": moved, "us": round(t_copy * 1e6, 3),
                                 "gbs": round(moved / t_copy / 1e9, 1),
                                 "how": "torch device copy, rotating slots over > 1 GiB, "
-                                       "graph replay"},
+                                       "after a 1 GiB cache flush, timed like us_per_call"},
             "launch_us": round(t_launch * 1e6, 3),
-            "launch_how": "one-element torch add, graph replay"}
+            "launch_how": "one-element torch add, timed like us_per_call"}
 
 
 def parity_check(rig):
@@ -386,20 +442,26 @@ def parity_check(rig):
 def load_traffic(workload: str, pool_path: bool):
     """HBM bytes per call from the committed rocprofv3 counter summary (FETCH_SIZE and
     WRITE_SIZE scaled by a plain copy of known size), if it was taken on the current
-    kernel source; otherwise None."""
+    kernel source; otherwise None.  Returns (bytes or None, where the figure comes from)."""
     kernel = "lora_add_pool_kernel" if pool_path else "sgmv_lora_add"
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.txt")
+    rel = os.path.join("profiles", f"{kernel}_{workload}_counters.txt")
+    path = os.path.join(ROOT, rel)
     if not os.path.exists(path):
-        return None
+        return None, f"no counter summary {rel} for this workload"
     rec = {}
     with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith(("#", "rocprofv3", "`")):
                 k, v = line.split(":", 1)
                 rec[k.strip()] = v.split()[0] if v.split() else ""
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
-        return None
-    return int(float(rec["hbm_bytes_per_call"]))
+    src = rec.get("kernel_source_sha256_16")
+    if src != kernel_source_hash():
+        return None, (f"{rel} was taken on kernel source {src}, not this build's "
+                      f"{kernel_source_hash()}")
+    return int(float(rec["hbm_bytes_per_call"])), (
+        f"from {rel}: FETCH_SIZE + WRITE_SIZE per call from two rocprofv3 --pmc runs, scaled "
+        f"by a plain copy of known size; taken on kernel source {src}, the same as this "
+        f"build; not measured in this run")
 
 
 def measure(p, device, steps: int, warmup: int, eager: bool = False, force_table: bool = False,
@@ -441,8 +503,25 @@ def measure(p, device, steps: int, warmup: int, eager: bool = False, force_table
         with torch.cuda.graph(graph):
             for k in range(steps):
                 rig.step(base + k)
-        graph.replay()                     # untimed: uploads the graph, K warm steps
+        graph.replay()                     # untimed: uploads the graph
         torch.cuda.synchronize()
+        # The kernel's duration: the K calls launched one after another on the stream,
+        # queued behind a cache flush and a spin kernel long enough for the host to
+        # enqueue them all, so that the GPU runs them back to back and the HIP events
+        # around them see no launch gap (a graph launch adds about 12 us of its own per
+        # replay on this GPU, whatever it holds).
+        flush_caches(device, wait=False)
+        gpu_hold(100.0 + 40.0 * steps, sync=False)
+        k_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        k_ev[0].record(stream)
+        for k in range(steps):
+            rig.step(base + k)
+        k_ev[1].record(stream)
+        torch.cuda.synchronize()
+        kernel_s = k_ev[0].elapsed_time(k_ev[1]) * 1e-3 / steps
+        # the K steps' wall time: host clock (and HIP events) around a replay of the graph
+        # after a cache flush
+        flush_caches(device)
         t0 = time.perf_counter()
         t_ev[0].record(stream)
         graph.replay()
@@ -452,6 +531,7 @@ def measure(p, device, steps: int, warmup: int, eager: bool = False, force_table
         del graph
     else:
         torch.cuda.synchronize()
+        flush_caches(device)
         t0 = time.perf_counter()
         t_ev[0].record(stream)
         for k in range(steps):
@@ -462,10 +542,9 @@ def measure(p, device, steps: int, warmup: int, eager: bool = False, force_table
     wall = (t1 - t0) / steps
     gpu_step = t_ev[0].elapsed_time(t_ev[1]) * 1e-3 / steps
     if use_graph:
-        # each step is one kernel, replayed back to back: the events over the timed
-        # region give the kernel's average duration
-        call_s = gpu_step
-        call_how = "HIP events over the timed graph replay / K"
+        call_s = kernel_s
+        call_how = ("HIP events around the K calls launched one after another, queued behind "
+                    "a cache flush and a spin kernel (no launch gap), / K")
     else:
         call_s = kernel_pass(rig, base + steps, min(steps, 500))
         call_how = "HIP events over a graph of the same calls (tables pre-uploaded) / count"
@@ -550,6 +629,7 @@ def layer_measure(p, device, steps: int) -> dict:
                 body(1 + k)
         graph.replay()
         torch.cuda.synchronize()
+        flush_caches(device, wait=False)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(st)
         graph.replay()
@@ -584,7 +664,7 @@ def run_layer(device, args) -> int:
         torch.cuda.empty_cache()
     print(json.dumps({"metric": "LoRA linear layer: backbone GEMM alone vs GEMM + SGMV, us per call",
                       "unit": "us", "higher_is_better": False, "n_gpus": 1, "data": "synthetic",
-                      "cache": "cold (rotating slots)", "points": rows}), flush=True)
+                      "cache": "cold (rotating slots, 1 GiB read before each timed run)", "points": rows}), flush=True)
     return 0 if all(r["parity"]["ok"] for r in rows) else 1
 
 
@@ -665,7 +745,7 @@ def run_sweep(kind: str, device, args) -> int:
     print(json.dumps({
         "metric": f"SGMV us/call against {'batch size' if kind == 'decode' else 'prompt length'}",
         "sweep": kind, "unit": "us", "higher_is_better": False, "n_gpus": 1,
-        "data": "synthetic", "cache": "cold (rotating slots)", "points": points,
+        "data": "synthetic", "cache": "cold (rotating slots, 1 GiB read before each timed run)", "points": points,
     }), flush=True)
     return 0 if ok else 1
 
@@ -760,14 +840,18 @@ def run_ranked(device, args) -> int:
             call(1 + k)
     graph.replay()
     torch.cuda.synchronize()
+    flush_caches(device, wait=False)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
     e0.record(stream)
     graph.replay()
     e1.record(stream)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / args.steps
     call_s = e0.elapsed_time(e1) * 1e-3 / args.steps
+    flush_caches(device)
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
     ranks = q.ranks()
     out = {
         "metric": METRIC,
@@ -787,7 +871,8 @@ def run_ranked(device, args) -> int:
             "rows_per_rank": {int(r): int((ranks[q.ids] == r).sum()) for r in q.scales},
             "scales": {int(r): v for r, v in q.scales.items()},
             "distinct_adapters": int(np.unique(q.ids).size), "rotation_slots": slots,
-            "cache": "cold (rotating slots)",
+            "cache": "cold: every timed call on its own slot, "
+                     f"{FLUSH_BYTES >> 20} MiB read between the untimed and the timed run",
             "step": "sgmv_lora_add_ranked (one call, both rank groups), tables pre-uploaded, "
                     "K calls replayed from one HIP graph",
         },
@@ -880,10 +965,13 @@ def main(argv=None) -> int:
 
     nbytes = algorithmic_bytes(p)
     flops = algorithmic_flops(p)
-    traffic = load_traffic(args.workload, rig.pool_path and p.n <= 64) if args.path != "device" or p.n <= 64 else None
+    if args.path != "device" or p.n <= 64:
+        traffic, traffic_src = load_traffic(args.workload, rig.pool_path and p.n <= 64)
+    else:
+        traffic, traffic_src = None, "no counter summary for the device-id table path"
     if rig.host_ids:
         kernel = "lora_add_ids_kernel (one launch per call, ids in the kernel arguments)"
-        traffic = None
+        traffic, traffic_src = None, "no counter summary for the host-id kernel"
     elif rig.pool_path and p.n <= 64:
         kernel = "lora_add_pool_kernel (one launch per call)"
     elif rig.pool_path:
@@ -907,7 +995,11 @@ def main(argv=None) -> int:
             "workload": p.name, "n_tokens": p.n, "h_in": p.h_in, "h_out": p.h_out, "r": p.r,
             "distinct_adapters": p.distinct_adapters(), "adapter_pool": p.n_adapters,
             "scale": p.scale, "rotation_slots": rig.slots,
-            "rotation_bytes": rig.slots * nbytes, "cache": "cold (rotating slots)",
+            "rotation_bytes": rig.slots * nbytes,
+            "cache": "cold: every timed step on its own slot of x, y, ids and adapters, and "
+                     f"{FLUSH_BYTES >> 20} MiB read between the untimed and the timed run",
+            "min_bytes_between_slot_reuse": min(FLUSH_BYTES, rig.slots * nbytes)
+                                            if args.steps > rig.slots else FLUSH_BYTES,
             "step": ("sgmv_lora_add_host_ids: host ids in the kernel arguments, grouping + "
                      "shrink + expand in one launch" +
                      (", K steps replayed from one HIP graph" if use_graph else ", eager"))
@@ -931,6 +1023,7 @@ def main(argv=None) -> int:
             "unit": "GB/s",
             "frac": round(nbytes / call_s / 1e9 / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "traffic_source": traffic_src,
             "kernel": kernel,
             "mfma_frac": round(flops / call_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
         },

@@ -133,33 +133,65 @@ def ptr_table(adapter_base: np.ndarray, seg_adapter: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------------------
 # the low-rank update
 # --------------------------------------------------------------------------------------
-def shrink(x: np.ndarray, ids: np.ndarray, A_pool: np.ndarray, dtype: str) -> np.ndarray:
-    """v[t, :] = x[t, :] @ A[ids[t]]  in float64, caller row order, shape [n, r]."""
-    X = decode(x, dtype)
-    n, r = X.shape[0], A_pool.shape[1]
+class DecodedPool:
+    """Adapter pool in storage format, decoded to float64 one adapter at a time, on first
+    use (each decoded adapter is kept).  ``shape`` is the storage pool's shape."""
+
+    def __init__(self, pool: np.ndarray, dtype: str):
+        self.pool, self.dtype, self.shape = pool, dtype, pool.shape
+        self._done = {}
+
+    def __getitem__(self, a: int) -> np.ndarray:
+        if a not in self._done:
+            self._done[a] = decode(self.pool[a], self.dtype)
+        return self._done[a]
+
+
+def shrink_f64(X: np.ndarray, ids: np.ndarray, A64) -> np.ndarray:
+    """v[t, :] = X[t, :] @ A[ids[t]] on float64 values: X [n, h_in]; A64[a] is adapter
+    a's stored A, [r, h_in] (column j of A is row j), and A64.shape[1] is r."""
+    n, r = X.shape[0], A64.shape[1]
     v = np.zeros((n, r), dtype=np.float64)
     for a in np.unique(ids):
         rows = np.nonzero(ids == a)[0]
-        A_a = decode(A_pool[int(a)], dtype)          # [r, h_in]: column j of A is row j
+        A_a = A64[int(a)]
         v[rows] = X[rows] @ A_a.T
     return v
+
+
+def expand_f64(Y: np.ndarray, v: np.ndarray, ids: np.ndarray, B64, scale: float) -> np.ndarray:
+    """Y[t, :] + scale * (v[t, :] @ B[ids[t]]) on float64 values: B64[a] is adapter a's
+    stored B, [h_out, r] (column c of B is row c)."""
+    out = Y.copy()
+    for a in np.unique(ids):
+        rows = np.nonzero(ids == a)[0]
+        B_a = B64[int(a)]
+        out[rows] += float(scale) * (np.asarray(v, np.float64)[rows] @ B_a.T)
+    return out
+
+
+def shrink(x: np.ndarray, ids: np.ndarray, A_pool: np.ndarray, dtype: str) -> np.ndarray:
+    """v[t, :] = x[t, :] @ A[ids[t]]  in float64, caller row order, shape [n, r]."""
+    return shrink_f64(decode(x, dtype), ids, DecodedPool(A_pool, dtype))
 
 
 def expand(y: np.ndarray, v: np.ndarray, ids: np.ndarray, B_pool: np.ndarray,
            scale: float, dtype: str) -> np.ndarray:
     """y_in[t, :] + scale * (v[t, :] @ B[ids[t]])  in float64 (not rounded)."""
-    out = decode(y, dtype).copy()
-    for a in np.unique(ids):
-        rows = np.nonzero(ids == a)[0]
-        B_a = decode(B_pool[int(a)], dtype)          # [h_out, r]: column c of B is row c
-        out[rows] += float(scale) * (np.asarray(v, np.float64)[rows] @ B_a.T)
-    return out
+    return expand_f64(decode(y, dtype), v, ids, DecodedPool(B_pool, dtype), scale)
+
+
+def lora_add_f64(Y: np.ndarray, X: np.ndarray, ids: np.ndarray, A64, B64,
+                 scale: float) -> np.ndarray:
+    """SGMV on float64 values (see shrink_f64 / expand_f64)."""
+    return expand_f64(Y, shrink_f64(X, ids, A64), ids, B64, scale)
 
 
 def lora_add(y: np.ndarray, x: np.ndarray, ids: np.ndarray, A_pool: np.ndarray,
              B_pool: np.ndarray, scale: float, dtype: str) -> np.ndarray:
     """SGMV result: y_in + scale * (x @ A[a_t]) @ B[a_t] per row, float64, unrounded."""
-    return expand(y, shrink(x, ids, A_pool, dtype), ids, B_pool, scale, dtype)
+    return lora_add_f64(decode(y, dtype), decode(x, dtype), ids, DecodedPool(A_pool, dtype),
+                        DecodedPool(B_pool, dtype), scale)
 
 
 def lora_add_problem(p) -> np.ndarray:

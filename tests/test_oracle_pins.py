@@ -378,13 +378,13 @@ def test_segments_ranked_definition(case):
 # --------------------------------------------------------------------------------------
 MUTATIONS = [
     ("drop scale", "float(scale) * (", "1.0 * ("),
-    ("wrong adapter for A", "A_pool[int(a)]", "A_pool[(int(a) + 1) % A_pool.shape[0]]"),
+    ("wrong adapter for A", "A64[int(a)]", "A64[(int(a) + 1) % A64.shape[0]]"),
     ("B not transposed", "@ B_a.T)", "@ B_a)"),
     ("sign", "out[rows] += float(scale)", "out[rows] -= float(scale)"),
     ("unstable sort", "for i, t in enumerate(ids):", "for i, t in reversed(list(enumerate(ids))):"),
     ("bf16 shift", "<< np.uint32(16)", "<< np.uint32(15)"),
     ("round toward zero", "np.rint(np.ldexp(m, 8))", "np.trunc(np.ldexp(m, 8))"),
-    ("y not added", "out = decode(y, dtype).copy()\n    for a in", "out = np.zeros_like(decode(y, dtype))\n    for a in"),
+    ("y not added", "out = Y.copy()", "out = np.zeros_like(Y)"),
     ("ranked: one scale for every rank", "B_k, scales[r], dtype)", "B_k, scales[min(scales)], dtype)"),
     ("ranked: pools not offset", "        off += P\n    return out", "        off += 0\n    return out"),
     ("ranked: rank not the leading key", "keys = [(int(rank[a]), int(a), t)", "keys = [(0 * int(rank[a]), int(a), t)"),
