@@ -70,6 +70,13 @@ class RankGroup(ctypes.Structure):
                 ("scale", ctypes.c_float)]
 
 
+SIGNATURES["sgmv_slot_cache_create"] = (ctypes.c_int, [_i32, _p])
+SIGNATURES["sgmv_slot_cache_destroy"] = (None, [_p])
+SIGNATURES["sgmv_slot_cache_map"] = (ctypes.c_int, [_p, _p, _i32, _p, _p, _p, _p])
+SIGNATURES["sgmv_slot_cache_lookup"] = (ctypes.c_int, [_p, _i64, _p])
+SIGNATURES["sgmv_slot_cache_evict"] = (ctypes.c_int, [_p, _i64])
+SIGNATURES["sgmv_upload_adapter"] = (ctypes.c_int, [_p, _p, _i64, _p, _i64, _i32, _i32, _p, _p,
+                                                    _i32, _i32, _i32])
 SIGNATURES["sgmv_build_segments_ranked"] = (ctypes.c_int, [_p, _i32, _i32, _p, _p, _p, _p, _p, _p])
 SIGNATURES["sgmv_lora_add_ranked"] = (ctypes.c_int, [_p, _i32, _p, _i64, _p, _i64, _p, _p, _p, _p,
                                                      _i32, _p, _i32, _i32, _i32, _p, _sz])

@@ -23,7 +23,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libsgmv.so")
 ARCH = "gfx950"
 
-SOURCES = ["sgmv_segments.cpp", "sgmv_kernels.hip", "sgmv_decode.hip"]
+SOURCES = ["sgmv_segments.cpp", "sgmv_cache.cpp", "sgmv_kernels.hip", "sgmv_decode.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}",
           "-Wall", "-Wno-unused-function",

@@ -1605,6 +1605,29 @@ extern "C" int sgmv_check_workspace(hipStream_t stream, void* workspace, int32_t
   return f != 0 ? SGMV_ERR_DEVICE : SGMV_OK;
 }
 
+extern "C" int sgmv_upload_adapter(hipStream_t stream, void* A_pool, int64_t A_stride,
+                                   void* B_pool, int64_t B_stride, int32_t slot,
+                                   int32_t n_slots, const void* A_host, const void* B_host,
+                                   int32_t r, int32_t h_in, int32_t h_out) {
+  if (!rank_ok(r)) return SGMV_ERR_UNSUPPORTED;
+  int st;
+  if ((st = check_dim(h_in, h_in)) || (st = check_dim(h_out, h_out))) return st;
+  if (n_slots <= 0 || slot < 0 || slot >= n_slots) return SGMV_ERR_SHAPE;
+  if (A_stride < static_cast<int64_t>(r) * h_in || B_stride < static_cast<int64_t>(h_out) * r)
+    return SGMV_ERR_SHAPE;
+  if (A_stride % 8 != 0 || B_stride % 8 != 0) return SGMV_ERR_ALIGNMENT;
+  if (!A_pool || !B_pool || !A_host || !B_host) return SGMV_ERR_NULL;
+  if (!aligned16(A_pool) || !aligned16(B_pool)) return SGMV_ERR_ALIGNMENT;
+  if ((st = check_device())) return st;
+  const size_t a_bytes = 2 * static_cast<size_t>(r) * h_in, b_bytes = 2 * static_cast<size_t>(r) * h_out;
+  char* a_dst = static_cast<char*>(A_pool) + 2 * static_cast<size_t>(slot) * A_stride;
+  char* b_dst = static_cast<char*>(B_pool) + 2 * static_cast<size_t>(slot) * B_stride;
+  if (hipMemcpyAsync(a_dst, A_host, a_bytes, hipMemcpyHostToDevice, stream) != hipSuccess ||
+      hipMemcpyAsync(b_dst, B_host, b_bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
+    return SGMV_ERR_HIP;
+  return SGMV_OK;
+}
+
 extern "C" size_t sgmv_workspace_bytes(int32_t n, int32_t h_in, int32_t r) {
   if (n < 0 || h_in < 8 || h_in > kMaxDim || !rank_ok(r)) return 0;
   return ws_layout(n, h_in, r).total;

@@ -494,12 +494,27 @@ def build_segments_device(ids, n_adapters: int, stream=None):
     return perm, starts, seg_ad, S
 
 
-def lora_add_pool(y, x, ids, A_pool, B_pool, scale: float, workspace=None, stream=None):
+def _layer_pools(A_pool, B_pool, layer):
+    """Stacked multi-layer pools [layers, P, ...]: layer ``layer``'s pools (a pointer
+    offset of layer * P adapters); 3-D pools are returned as they are."""
+    if A_pool.dim() == 4 or B_pool.dim() == 4:
+        if layer is None or A_pool.dim() != 4 or B_pool.dim() != 4:
+            raise ValueError("stacked [layers, P, ...] pools need a layer index (both pools)")
+        return A_pool[layer], B_pool[layer]
+    if layer not in (None, 0):
+        raise ValueError("a layer index needs stacked [layers, P, ...] pools")
+    return A_pool, B_pool
+
+
+def lora_add_pool(y, x, ids, A_pool, B_pool, scale: float, workspace=None, stream=None,
+                  layer: Optional[int] = None):
     """y[t] += scale * (x[t] @ A_pool[ids[t]]) @ B_pool[ids[t]] with device ids (n <= 4096):
     one launch for n <= 64, device segment sort plus the table kernels above.
 
     ``ids`` is a device int32 tensor [n]; ``A_pool`` [P, r, h_in] and ``B_pool``
-    [P, h_out, r] are device tensors with contiguous adapters."""
+    [P, h_out, r] are device tensors with contiguous adapters, or stacked multi-layer
+    pools [layers, P, ...] with ``layer`` naming the layer."""
+    A_pool, B_pool = _layer_pools(A_pool, B_pool, layer)
     n = int(x.shape[0])
     _check_rows(x, n, "x")
     _check_rows(y, n, "y")
@@ -519,11 +534,13 @@ def lora_add_pool(y, x, ids, A_pool, B_pool, scale: float, workspace=None, strea
     return y
 
 
-def lora_add_host_ids(y, x, ids, A_pool, B_pool, scale: float, workspace=None, stream=None):
+def lora_add_host_ids(y, x, ids, A_pool, B_pool, scale: float, workspace=None, stream=None,
+                      layer: Optional[int] = None):
     """y[t] += scale * (x[t] @ A_pool[ids[t]]) @ B_pool[ids[t]] for a decode batch (n <= 64)
     whose adapter ids are on the host: one launch, the ids travel in its kernel arguments.
 
     ``ids`` is a host int32 array or CPU tensor [n]; the pools are as for lora_add_pool."""
+    A_pool, B_pool = _layer_pools(A_pool, B_pool, layer)
     ids_np = np.ascontiguousarray(
         ids.numpy() if hasattr(ids, "numpy") else np.asarray(ids), dtype=np.int32)
     n = int(x.shape[0])

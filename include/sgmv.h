@@ -355,6 +355,48 @@ int sgmv_lora_add_host_ids(hipStream_t stream, int32_t dtype, void* y, int64_t l
                            int32_t r, float scale, void* workspace, size_t workspace_bytes);
 
 /*
+ * On-demand adapter loading into a device adapter pool (paper summary, "Summary": the
+ * runner fetches only the small LoRA matrices of an adapter when a request needs them;
+ * "Key points": loading an adapter on demand takes milliseconds).
+ *
+ * sgmv_slot_cache (host bookkeeping, no GPU work): which adapter key occupies which slot
+ * of a pool of n_slots adapters (pools laid out as for sgmv_lora_add_pool).  Not thread
+ * safe: one cache per pool, used by one host thread.
+ *   create   SGMV_ERR_SHAPE unless 0 < n_slots <= 2^24; *cache = NULL on failure
+ *   map      keys: host int64[n] adapter keys of a batch (any values, repeats allowed);
+ *            slots: host int32[n] out, the pool slot of every key.  A key that is not
+ *            resident takes the lowest free slot, else the least recently used slot whose
+ *            key the batch does not use (that key is evicted); each such (key, slot) is
+ *            written to miss_keys / miss_slots (host, n entries) and *n_miss counts them:
+ *            the caller uploads those adapters (sgmv_upload_adapter) before the SGMV call
+ *            that reads them, on the same stream.  Returns SGMV_ERR_SHAPE, changing
+ *            nothing, if the batch has more distinct keys than slots.
+ *   lookup   *slot = the key's slot, or -1 if it is not resident
+ *   evict    frees the key's slot (SGMV_ERR_ADAPTER_ID if the key is not resident)
+ */
+typedef struct sgmv_slot_cache sgmv_slot_cache;
+int sgmv_slot_cache_create(int32_t n_slots, sgmv_slot_cache** cache);
+void sgmv_slot_cache_destroy(sgmv_slot_cache* cache);
+int sgmv_slot_cache_map(sgmv_slot_cache* cache, const int64_t* keys, int32_t n, int32_t* slots,
+                        int64_t* miss_keys, int32_t* miss_slots, int32_t* n_miss);
+int sgmv_slot_cache_lookup(const sgmv_slot_cache* cache, int64_t key, int32_t* slot);
+int sgmv_slot_cache_evict(sgmv_slot_cache* cache, int64_t key);
+
+/*
+ * Upload one adapter from host memory into slot `slot` of device pools (same passages as
+ * above): A_host ([r, h_in] row-major, 16-bit elements) to A_pool + slot * A_stride
+ * elements and B_host ([h_out, r]) to B_pool + slot * B_stride, as two hipMemcpyAsync on
+ * `stream`.  With pinned host memory (hipHostMalloc, or torch's pin_memory) the copies
+ * are asynchronous; from pageable memory they return only when the data has been staged.
+ * Kernels enqueued later on `stream` see the new adapter.  Host arrays must stay valid
+ * until the copies complete.  Checks as for sgmv_lora_add_pool's pools, and 0 <= slot <
+ * n_slots.
+ */
+int sgmv_upload_adapter(hipStream_t stream, void* A_pool, int64_t A_stride, void* B_pool,
+                        int64_t B_stride, int32_t slot, int32_t n_slots, const void* A_host,
+                        const void* B_host, int32_t r, int32_t h_in, int32_t h_out);
+
+/*
  * Allocation-free variant of sgmv_lora_add_host_ids, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation): the same kernel, arguments and result, with no workspace.  Its scratch (the

@@ -1,5 +1,6 @@
 // Host code of libsgmv under AddressSanitizer and UndefinedBehaviorSanitizer: the segment
-// builders and the pointer table (sgmv_segments.cpp) and the argument checks and
+// builders and the pointer table (sgmv_segments.cpp), the adapter slot cache
+// (sgmv_cache.cpp) and the argument checks and
 // workspace layout (sgmv_checks.h), driven over random and edge-case inputs, including
 // every rejection.  Built with g++ (no GPU code) and run by tests/test_host_abi.py; prints
 // "ok <count>" and exits 0 when every case behaves, any sanitizer report aborts the run.
@@ -143,6 +144,65 @@ static void ranked_cases() {
     }
 }
 
+// the slot cache over random batches: every key of a batch gets one slot, distinct keys
+// distinct slots, misses are exactly the keys that were not resident, and the cache never
+// holds more keys than slots
+static void cache_cases() {
+  std::mt19937 rng(5);
+  for (int n_slots : {1, 3, 17, 64}) {
+    sgmv_slot_cache* c = nullptr;
+    EXPECT(sgmv_slot_cache_create(n_slots, &c) == SGMV_OK && c);
+    std::vector<int64_t> resident_before;
+    for (int round = 0; round < 400; ++round) {
+      const int n = static_cast<int>(rng() % (2 * n_slots + 3));
+      std::vector<int64_t> keys(n);
+      for (auto& k : keys) k = static_cast<int64_t>(rng() % (3 * n_slots + 1)) - 5;
+      std::vector<int32_t> slots(n > 0 ? n : 1), ms(n > 0 ? n : 1), was(n > 0 ? n : 1);
+      std::vector<int64_t> mk(n > 0 ? n : 1);
+      for (int t = 0; t < n; ++t) EXPECT(sgmv_slot_cache_lookup(c, keys[t], &was[t]) == SGMV_OK);
+      int32_t miss = -1;
+      const int st = sgmv_slot_cache_map(c, keys.data(), n, slots.data(), mk.data(), ms.data(), &miss);
+      std::vector<int64_t> distinct;
+      for (int t = 0; t < n; ++t) {
+        bool seen = false;
+        for (int64_t d : distinct) seen = seen || d == keys[t];
+        if (!seen) distinct.push_back(keys[t]);
+      }
+      if (static_cast<int>(distinct.size()) > n_slots) {
+        EXPECT(st == SGMV_ERR_SHAPE);
+        continue;
+      }
+      EXPECT(st == SGMV_OK);
+      int expect_miss = 0;
+      for (int64_t d : distinct) {
+        int first = -1;
+        for (int t = 0; t < n && first < 0; ++t)
+          if (keys[t] == d) first = t;
+        expect_miss += was[first] < 0;
+      }
+      EXPECT(miss == expect_miss);
+      for (int t = 0; t < n; ++t) {
+        EXPECT(slots[t] >= 0 && slots[t] < n_slots);
+        int32_t now = -2;
+        EXPECT(sgmv_slot_cache_lookup(c, keys[t], &now) == SGMV_OK && now == slots[t]);
+        if (was[t] >= 0) EXPECT(was[t] == slots[t]);
+        for (int u = 0; u < t; ++u) EXPECT((keys[u] == keys[t]) == (slots[u] == slots[t]));
+      }
+      if (n > 0 && round % 7 == 0) {
+        EXPECT(sgmv_slot_cache_evict(c, keys[0]) == SGMV_OK);
+        int32_t gone = 0;
+        EXPECT(sgmv_slot_cache_lookup(c, keys[0], &gone) == SGMV_OK && gone == -1);
+        EXPECT(sgmv_slot_cache_evict(c, keys[0]) == SGMV_ERR_ADAPTER_ID);
+      }
+    }
+    sgmv_slot_cache_destroy(c);
+  }
+  sgmv_slot_cache* c = nullptr;
+  EXPECT(sgmv_slot_cache_create(0, &c) == SGMV_ERR_SHAPE && c == nullptr);
+  EXPECT(sgmv_slot_cache_create(4, nullptr) == SGMV_ERR_NULL);
+  sgmv_slot_cache_destroy(nullptr);
+}
+
 static void check_cases() {
   // segment bounds, including extreme values (no overflow in the pigeonhole products)
   EXPECT(check_segments(0, 0, 0, 0) == SGMV_OK);
@@ -188,6 +248,7 @@ static void check_cases() {
 int main() {
   builder_cases();
   ranked_cases();
+  cache_cases();
   check_cases();
   std::printf("ok %ld\n", g_checks);
   return 0;

@@ -147,6 +147,7 @@ def test_host_code_under_sanitizers(tmp_path):
                     "-I/opt/rocm/include", "-D__HIP_PLATFORM_AMD__",
                     os.path.join(ROOT, "tests", "host_sanitize_check.cpp"),
                     os.path.join(ROOT, "adapter_gemv_amd", "csrc", "sgmv_segments.cpp"),
+                    os.path.join(ROOT, "adapter_gemv_amd", "csrc", "sgmv_cache.cpp"),
                     "-o", exe], check=True)
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
