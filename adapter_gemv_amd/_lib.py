@@ -5,7 +5,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-from .build import LIB_PATH
+from .build import LIB_PATH, PHASES_LIB_PATH
 
 F16 = 0
 BF16 = 1
@@ -82,6 +82,16 @@ SIGNATURES["sgmv_lora_add_ranked"] = (ctypes.c_int, [_p, _i32, _p, _i64, _p, _i6
                                                      _i32, _p, _i32, _i32, _i32, _p, _sz])
 
 _LIB = None
+_PATH = LIB_PATH
+
+
+def use_phase_stamps() -> None:
+    """Load the profiling variant (libsgmv_phases.so, built with build --phases) instead of
+    libsgmv.so; must be called before the library is first used."""
+    global _PATH
+    if _LIB is not None and _PATH != PHASES_LIB_PATH:
+        raise RuntimeError("libsgmv is already loaded")
+    _PATH = PHASES_LIB_PATH
 
 
 class SgmvError(RuntimeError):
@@ -94,14 +104,17 @@ def lib() -> ctypes.CDLL:
     """The loaded libsgmv.so (raises if it was not built)."""
     global _LIB
     if _LIB is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+        if not os.path.exists(_PATH):
+            raise RuntimeError(f"{_PATH} is missing; build it with "
                                "`python -m adapter_gemv_amd.build` (hipcc, gfx950)")
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
+        if _PATH == PHASES_LIB_PATH:
+            L.sgmv_phase_stamps_attach.restype = ctypes.c_int64
+            L.sgmv_phase_stamps_attach.argtypes = [ctypes.c_void_p, ctypes.c_int64]
         _LIB = L
     return _LIB
 

@@ -2,6 +2,7 @@
 
     python -m adapter_gemv_amd.build          # compile and link
     python -m adapter_gemv_amd.build --asm    # also write the gfx950 assembly
+    python -m adapter_gemv_amd.build --phases # profiling variant with phase timestamps
 
 Every HIP source is compiled with packed FP32 instructions disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``).
@@ -21,6 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libsgmv.so")
+PHASES_LIB_PATH = os.path.join(PKG, "libsgmv_phases.so")
 ARCH = "gfx950"
 
 SOURCES = ["sgmv_segments.cpp", "sgmv_cache.cpp", "sgmv_kernels.hip", "sgmv_decode.hip"]
@@ -46,16 +48,21 @@ def _run(cmd):
     return "\n".join(lines)
 
 
-def build(asm: bool = False, verbose: bool = False) -> str:
-    """Compile every source and link libsgmv.so; returns the library path."""
+def build(asm: bool = False, verbose: bool = False, phases: bool = False) -> str:
+    """Compile every source and link libsgmv.so; returns the library path.  phases=True
+    builds the profiling variant libsgmv_phases.so instead, whose one-launch kernels write
+    per-phase timestamps (-DSGMV_PHASE_STAMPS; bench.py --phases reads them)."""
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    bdir = os.path.join(BUILD_DIR, "phases") if phases else BUILD_DIR
+    out = PHASES_LIB_PATH if phases else LIB_PATH
+    flags = COMMON + (["-DSGMV_PHASE_STAMPS"] if phases else [])
+    os.makedirs(bdir, exist_ok=True)
     objs = []
     jobs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        jobs.append([hipcc, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([hipcc, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
     if asm:
         for src in SOURCES:
             if src.endswith(".hip"):
@@ -67,18 +74,20 @@ def build(asm: bool = False, verbose: bool = False) -> str:
         for o in outs:
             if o:
                 print(o)
-    tmp = LIB_PATH + ".tmp"
+    tmp = out + ".tmp"
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--asm", action="store_true")
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--phases", action="store_true",
+                    help="build the phase-timestamp profiling variant libsgmv_phases.so")
     args = ap.parse_args(argv)
-    print(build(asm=args.asm, verbose=args.verbose))
+    print(build(asm=args.asm, verbose=args.verbose, phases=args.phases))
     return 0
 
 

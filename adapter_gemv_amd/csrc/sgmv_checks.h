@@ -59,7 +59,8 @@ inline int check_device() {
 // workspace layout shared by every entry point (the same bytes serve both paths).
 // Regions that must be zero between calls (counters, tagged partials) sit at the two
 // ends; scratch grows from the front:
-//   [0, 4)                  int32 flag (decode path: 1 = a wait timed out, 2 = bad id)
+//   [0, 4)                  int32 flag bits (SGMV_FLAG_*: wait timed out, bad id, segment
+//                           bounds that contradict the tables)
 //   [256, 16640)            decode path: one counter per row, one per 256-byte line
 //   [rowks_off, ...)        table path: split-K slice count of each sorted row
 //   [v_off, ...)            table path: final float32 v of rows of long segments
@@ -86,6 +87,10 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // split-K chunk (elements of h_in) of the table path's GEMV shrink and of the decode path
 inline int table_gemv_kc(int r) { return r == 16 ? 512 : 256; }
 inline int pool_kc(int r) { return 8192 / r; }
+// decode path: output columns per lane of an expand item (256 contiguous bytes of B; half
+// as many, with twice the expand items, measured no faster on MI355X: the shorter
+// epilogue was lost to the longer wait for the partial sums with more waves polling)
+constexpr int pool_cpl(int r) { return 128 / r; }
 // 64-bit words per row of a decode-path partial slice (r words: at least 128 bytes)
 constexpr int pool_part_row(int r) { return r; }
 // 64-bit words per decode-path partial slice (64 rows)

@@ -508,6 +508,31 @@ inline hipError_t launch_device_sort(hipStream_t st, const int32_t* ids, int32_t
 // half and a nonzero tag in the high half, written and read with agent-scope atomics:
 // a reader that sees the tag sees the value, with no L2 write-back or invalidate
 // between XCDs and no separate ready counter.
+// ------------------------------------------------------------------------------------
+// phase timestamps (profiling builds only, compiled with -DSGMV_PHASE_STAMPS)
+// ------------------------------------------------------------------------------------
+// Lane 0 of every wave of the one-launch kernels writes the 100 MHz real-time counter at
+// fixed points of its item to stamps[blockIdx.x * kStampSlots + i] with an ordinary
+// vector store, after waiting for all of the wave's memory operations where `wait` says
+// so.  Points: 0 wave start, 1 ids in registers, then for a shrink item 2 A and x loaded,
+// 3 tagged partial sums issued, 4 their stores acknowledged; for an expand item 2 B and y
+// loaded, 3 every partial sum present, 4 y stored (issued), 5 y store acknowledged, 6 item
+// done.  Normal builds compile no stamp.
+[[maybe_unused]] constexpr int kStampSlots = 8;
+[[maybe_unused]] constexpr int kStampMaxWgs = 8192;  // launches with a larger grid write no stamps
+#ifdef SGMV_PHASE_STAMPS
+#define SGMV_STAMP(p, i, wait)                                                              \
+  do {                                                                                      \
+    if (wait) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                              \
+    if ((p).stamps && (threadIdx.x & 63) == 0)                                              \
+      (p).stamps[blockIdx.x * kStampSlots + (i)] = __builtin_amdgcn_s_memrealtime();        \
+  } while (0)
+#else
+#define SGMV_STAMP(p, i, wait) \
+  do {                         \
+  } while (0)
+#endif
+
 struct PoolArgs {
   uint16_t* y;
   const uint16_t* x;
@@ -521,6 +546,7 @@ struct PoolArgs {
   int32_t* ws_flag;
   int32_t* counters;
   uint64_t* part;
+  uint64_t* stamps;  // profiling builds: this launch's phase timestamps, or NULL
 };
 
 struct Leader {
@@ -573,6 +599,7 @@ __device__ inline void shrink_item(const PoolArgs& p, const Leader& L, int blk, 
     const int kk = kbase + 32 * u;
     xv[u] = (xr && kk < p.h_in) ? ld16(xr + kk) : zero4();
   }
+  SGMV_STAMP(p, 2, true);
   f32x4_t acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -590,16 +617,19 @@ __device__ inline void shrink_item(const PoolArgs& p, const Leader& L, int blk, 
                       acc[nb][e]);
     }
   }
+  SGMV_STAMP(p, 3, false);
+  SGMV_STAMP(p, 4, true);
 }
 
 // expand item: one caller row r and columns [nc*64*CPL, (nc+1)*64*CPL); lane owns
-// CPL = 128/R consecutive columns, i.e. 256 contiguous bytes of the stored [h_out, r]
-// B[a].  Keying expand items by row spreads an adapter with many rows over as many
-// wavefronts.  B and y are loaded (and B widened to float32) while the shrink runs.
+// CPL = pool_cpl(R) consecutive columns, i.e. CPL * R * 2 contiguous bytes of the stored
+// [h_out, r] B[a].  Keying expand items by row spreads an adapter with many rows over as
+// many wavefronts.  B and y are loaded (and B widened to float32) while the shrink runs.
 template <int DT, int R>
 __device__ inline void expand_item(const PoolArgs& p, const Leader& L, int r, int nc) {
   using E = Elem<DT>;
-  constexpr int CPL = 128 / R;
+  constexpr int CPL = pool_cpl(R);
+  constexpr int NV = CPL * R / 8;  // 16-byte loads of B per lane
   constexpr int YW = CPL / 2;
   constexpr int G = 64 / R;  // lanes per column j when reading the partial slices
   const int lane = threadIdx.x & 63;
@@ -608,11 +638,11 @@ __device__ inline void expand_item(const PoolArgs& p, const Leader& L, int r, in
   const int cl = cin ? c0 : 0;  // lanes past h_out load column 0 and store nothing
 
   // unconditional loads keep the compiler's wait counts exact
-  uint4 b[16];
+  uint4 b[NV];
   const gptr<const uint16_t> Bblk =
       global_ptr(p.B) + static_cast<int64_t>(L.a) * p.B_stride + static_cast<int64_t>(cl) * R;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) b[v] = ld16(Bblk + 8 * v);
+  for (int v = 0; v < NV; ++v) b[v] = ld16(Bblk + 8 * v);
   uint32_t yv[YW];
   const gptr<uint16_t> yrow = global_ptr(p.y) + static_cast<int64_t>(r) * p.ld_y + cl;
   load_words<YW>(yrow, yv);
@@ -620,6 +650,7 @@ __device__ inline void expand_item(const PoolArgs& p, const Leader& L, int r, in
   float bf[CPL * R];
 #pragma unroll
   for (int e = 0; e < CPL * R; ++e) bf[e] = elem<DT>(b[e >> 3], e & 7);
+  SGMV_STAMP(p, 2, true);
 
   // v[r, j]: lane (j = lane % R, g = lane / R) takes slices g, g+G, ... of column j in
   // batches of 8, polls each batch until every tag is present and adds it in order; the
@@ -650,6 +681,7 @@ __device__ inline void expand_item(const PoolArgs& p, const Leader& L, int r, in
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc += __uint_as_float(static_cast<uint32_t>(w[u]));
   }
+  SGMV_STAMP(p, 3, false);
   // count this reader; whether it is the row's last is looked at after the y store
   int old = 0;
   if (lane == 0)
@@ -679,6 +711,8 @@ __device__ inline void expand_item(const PoolArgs& p, const Leader& L, int r, in
     }
     store_words<YW>(yrow, packed);
   }
+  SGMV_STAMP(p, 4, false);
+  SGMV_STAMP(p, 5, true);
 
   // the last of row r's NS readers clears the row's partials and its counter, leaving
   // both at zero for the next call
@@ -691,6 +725,7 @@ __device__ inline void expand_item(const PoolArgs& p, const Leader& L, int r, in
       __hip_atomic_store(&p.counters[r * kCounterStride], 0, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
   }
+  SGMV_STAMP(p, 6, true);
 }
 
 // Grid: n * KS shrink items (caller row r = i % n, chunk i / n; active when r is the
@@ -701,6 +736,7 @@ __device__ inline void expand_item(const PoolArgs& p, const Leader& L, int r, in
 // The kernel body, given lane's adapter id (the id of caller row `lane`, -1 past n).
 template <int DT, int R>
 __device__ inline void pool_items(const PoolArgs& p, int id) {
+  SGMV_STAMP(p, 1, true);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n_shrink = p.n * p.KS;
   const int shrink_wgs = (n_shrink + kItemsPerWg - 1) / kItemsPerWg;
@@ -738,6 +774,7 @@ __device__ inline void pool_items(const PoolArgs& p, int id) {
 // Adapter ids in device memory: every wave starts with one coalesced load of them.
 template <int DT, int R>
 __global__ __launch_bounds__(64 * kItemsPerWg) void lora_add_pool_kernel(PoolArgs p) {
+  SGMV_STAMP(p, 0, false);
   const int lane = threadIdx.x & 63;
   pool_items<DT, R>(p, lane < p.n ? p.ids[lane] : -1);
 }
@@ -751,6 +788,7 @@ struct PoolIds {
 
 template <int DT, int R>
 __global__ __launch_bounds__(64 * kItemsPerWg) void lora_add_ids_kernel(PoolArgs p, PoolIds ids) {
+  SGMV_STAMP(p, 0, false);
   const int lane = threadIdx.x & 63;
   const int raw = ids.id[lane];  // every lane loads: the load need not wait for p.n
   pool_items<DT, R>(p, lane < p.n ? raw : -1);
@@ -840,6 +878,19 @@ int check_pool_call(int32_t dtype, void* y, int64_t ld_y, const void* x, int64_t
   return SGMV_OK;
 }
 
+#ifdef SGMV_PHASE_STAMPS
+// profiling builds: the stamp buffer attached by sgmv_phase_stamps_attach, used round robin
+// one launch's slice at a time
+uint64_t* g_stamp_buf = nullptr;
+int64_t g_stamp_cap = 0, g_stamp_next = 0;
+uint64_t* next_stamps(int grid) {
+  if (!g_stamp_buf || grid > kStampMaxWgs) return nullptr;
+  return g_stamp_buf + (g_stamp_next++ % g_stamp_cap) * static_cast<int64_t>(kStampMaxWgs) * kStampSlots;
+}
+#else
+uint64_t* next_stamps(int) { return nullptr; }
+#endif
+
 // Arguments of the one-launch kernels (n <= 64).
 PoolArgs pool_args(void* y, int64_t ld_y, const void* x, int64_t ld_x, const int32_t* adapter_ids,
                    int32_t n, const void* A_pool, int64_t A_stride, const void* B_pool,
@@ -860,12 +911,14 @@ PoolArgs pool_args(void* y, int64_t ld_y, const void* x, int64_t ld_x, const int
   p.h_in = h_in;
   p.h_out = h_out;
   p.KS = (h_in + pool_kc(r) - 1) / pool_kc(r);
-  p.NS = (h_out + pool_kc(r) - 1) / pool_kc(r);  // 64 lanes x 128/r columns per item
+  const int cols = 64 * pool_cpl(r);
+  p.NS = (h_out + cols - 1) / cols;  // 64 lanes x pool_cpl(r) columns per item
   p.scale = scale;
   char* ws = static_cast<char*>(workspace);
   p.ws_flag = reinterpret_cast<int32_t*>(ws);
   p.counters = reinterpret_cast<int32_t*>(ws + kWsPoolCounters);
   p.part = reinterpret_cast<uint64_t*>(ws + pool_offset(workspace_bytes, h_in, r));
+  p.stamps = next_stamps(n * (p.KS + p.NS));
   return p;
 }
 
@@ -1040,3 +1093,17 @@ extern "C" int sgmv_lora_add_host_ids_noalloc(hipStream_t stream, int32_t dtype,
   return run_host_ids(stream, dtype, y, ld_y, x, ld_x, adapter_ids, n, A_pool, A_stride, B_pool,
                       B_stride, n_adapters, h_in, h_out, r, scale, ws, kScratchBytes);
 }
+
+#ifdef SGMV_PHASE_STAMPS
+// Profiling builds only (not declared in the public header): attach a device buffer of
+// `launches` * 8192 * 8 uint64 words; each later one-launch call writes its waves' phase
+// timestamps into the next launch's slice (round robin).  NULL detaches.  Returns the
+// number of launches stamped since the last attach.
+extern "C" int64_t sgmv_phase_stamps_attach(uint64_t* device_buf, int64_t launches) {
+  const int64_t done = g_stamp_next;
+  g_stamp_buf = launches > 0 ? device_buf : nullptr;
+  g_stamp_cap = launches > 0 ? launches : 0;
+  g_stamp_next = 0;
+  return done;
+}
+#endif

@@ -439,11 +439,11 @@ def parity_check(rig):
             "ok": bool(np.all(err <= tol)) and flag == 0, "workspace_flag": flag}
 
 
-def load_traffic(workload: str, pool_path: bool):
+def load_traffic(workload: str, kernel: str):
     """HBM bytes per call from the committed rocprofv3 counter summary (FETCH_SIZE and
-    WRITE_SIZE scaled by a plain copy of known size), if it was taken on the current
-    kernel source; otherwise None.  Returns (bytes or None, where the figure comes from)."""
-    kernel = "lora_add_pool_kernel" if pool_path else "sgmv_lora_add"
+    WRITE_SIZE scaled by a plain copy of known size) of `kernel` on `workload`, if it was
+    taken on the current kernel source; otherwise None.  Returns (bytes or None, where the
+    figure comes from)."""
     rel = os.path.join("profiles", f"{kernel}_{workload}_counters.txt")
     path = os.path.join(ROOT, rel)
     if not os.path.exists(path):
@@ -767,6 +767,86 @@ def upload_and_first_call(device) -> list:
     return out
 
 
+def use_host_ids(path: str, p) -> bool:
+    """The default path of a decode batch (<= 64 tokens) is the one-launch kernel with the
+    ids in its arguments (the scheduler that forms the batch has them on the host)."""
+    from adapter_gemv_amd import sgmv
+    return path == "host" or (path == "auto" and p.n <= sgmv.DECODE_MAX_TOKENS)
+
+
+def run_phases(device, args) -> int:
+    """Per-phase timeline of the one-launch decode kernel, from the profiling variant of the
+    library (libsgmv_phases.so: lane 0 of every wave stamps the 100 MHz real-time counter at
+    fixed points of its item).  K cache-cold calls queued behind a flush and a spin kernel,
+    as for us_per_call; each call's stamps are taken relative to its first wave's start.
+    One JSON line: per phase, the median and p90 over every wave of every call."""
+    import torch
+    from adapter_gemv_amd import _lib, sgmv
+    _lib.use_phase_stamps()
+    p = workload_problem(args.workload)
+    if p.n > sgmv.DECODE_MAX_TOKENS:
+        raise SystemExit("--phases times the one-launch decode kernel (<= 64 tokens)")
+    rig = Rig(p, device)
+    rig.host_ids = use_host_ids(args.path, p)
+    parity = parity_check(rig)
+    K = args.steps
+    kc, cols = 8192 // p.r, 64 * (128 // p.r)   # shrink K chunk, expand columns per item
+    KS, NS = -(-p.h_in // kc), -(-p.h_out // cols)
+    grid = p.n * (KS + NS)
+    if grid > 8192:
+        raise SystemExit("grid too large for the stamp buffer")
+    buf = torch.zeros(K * 8192 * 8, dtype=torch.int64, device=device)
+    for k in range(args.warmup):
+        rig.step(1 + k)
+    base = 1 + args.warmup
+    stream = torch.cuda.current_stream()
+    flush_caches(device, wait=False)
+    gpu_hold(100.0 + 40.0 * K, sync=False)
+    L = _lib.lib()
+    L.sgmv_phase_stamps_attach(buf.data_ptr(), K)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for k in range(K):
+        rig.step(base + k)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    stamped = int(L.sgmv_phase_stamps_attach(None, 0))
+    call_us = e0.elapsed_time(e1) * 1e3 / K
+    st = buf.view(K, 8192, 8)[:stamped, :grid].cpu().numpy().astype(np.float64)
+    t0 = np.where(st[:, :, 0] > 0, st[:, :, 0], np.inf).min(axis=1)[:, None]
+    rel = (st - t0[:, :, None]) * 0.01                      # 100 MHz ticks -> us
+    shrink, expand = rel[:, : p.n * KS], rel[:, p.n * KS:]
+    active = st[:, : p.n * KS, 2] > 0                        # shrink items that had work
+
+    def stat(a):
+        a = a[np.isfinite(a)]
+        return {"median_us": round(float(np.median(a)), 3), "p90_us": round(float(np.percentile(a, 90)), 3)} \
+            if a.size else None
+
+    names_s = ["wave start", "ids in registers", "A and x loaded", "partial sums issued",
+               "partial sums acknowledged"]
+    names_e = ["wave start", "ids in registers", "B and y loaded", "every partial sum present",
+               "y stored (issued)", "y store acknowledged", "item done"]
+    span = np.nanmax(np.where(st > 0, rel, np.nan).reshape(stamped, -1), axis=1)
+    out = {
+        "metric": "one-launch decode kernel: phase timeline (us after the call's first wave started)",
+        "workload": p.name, "path": "host ids" if rig.host_ids else "device ids",
+        "calls": stamped, "grid": grid, "shrink_items": p.n * KS, "expand_items": p.n * NS,
+        "active_shrink_items_per_call": round(float(active.sum(axis=1).mean()), 1),
+        "us_per_call_stamped_build": round(call_us, 3),
+        "first_to_last_wave_start_us": stat(np.nanmax(np.where(st[:, :, 0] > 0, rel[:, :, 0], np.nan), axis=1)),
+        "last_stamp_us": stat(span),
+        "shrink": {n: stat(np.where(active, shrink[:, :, i], np.nan)) for i, n in enumerate(names_s)},
+        "expand": {n: stat(expand[:, :, i]) for i, n in enumerate(names_e)},
+        "parity": parity,
+        "how": "libsgmv_phases.so (-DSGMV_PHASE_STAMPS): s_memrealtime after waiting for the "
+               "wave's memory operations at each point; the waits themselves change timing a "
+               "little (compare us_per_call_stamped_build with bench.py's us_per_call)",
+    }
+    print(json.dumps(out), flush=True)
+    return 0 if parity["ok"] else 1
+
+
 SWEEPS = {
     # the pages' idea I5: latency against batch size, per stage
     "decode": [f"decode7b_bs{n}" for n in (1, 2, 4, 8, 16, 24, 32, 48, 64)],
@@ -783,11 +863,13 @@ def run_sweep(kind: str, device, args) -> int:
     for name in SWEEPS[kind]:
         p = workload_problem(name)
         steps = args.steps if kind == "decode" else max(20, args.steps // 20)
-        m = measure(p, device, steps, min(args.warmup, steps), eager=args.eager, warm=False)
+        m = measure(p, device, steps, min(args.warmup, steps), eager=args.eager, warm=False,
+                    host_ids=use_host_ids(args.path, p))
         nbytes = algorithmic_bytes(p)
         points.append({
             "workload": p.name, "n_tokens": p.n, "distinct_adapters": p.distinct_adapters(),
-            "path": "one launch (sgmv_lora_add_pool)" if m["rig"].pool_path else
+            "path": ("one launch, host ids (sgmv_lora_add_host_ids)" if m["rig"].host_ids else
+                     "one launch (sgmv_lora_add_pool)") if m["rig"].pool_path else
                     "table (sgmv_lora_add)",
             "us_per_call": round(m["call_s"] * 1e6, 3),
             "us_per_step": round(m["wall"] * 1e6, 3),
@@ -962,10 +1044,11 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="decode7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", choices=["auto", "table", "device", "host"], default="auto",
-                    help="auto: one-launch path for batches of <= 64 tokens, host-built tables "
-                         "above; device: device ids for any batch up to 4096 tokens "
-                         "(device sort + table kernels, graph-captured); table: host tables; "
-                         "host: one launch with the host ids in its kernel arguments (<= 64)")
+                    help="auto: one launch with the host ids in its kernel arguments for "
+                         "batches of <= 64 tokens, host-built tables above; device: device ids "
+                         "for any batch up to 4096 tokens (one launch up to 64, device "
+                         "grouping + table kernels above, graph-captured); table: host "
+                         "tables; host: the one-launch host-id kernel (<= 64)")
     ap.add_argument("--eager", action="store_true", help="no HIP graph on the one-launch path")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--cold-only", action="store_true",
@@ -977,6 +1060,8 @@ def main(argv=None) -> int:
                     help="time the LoRA linear layer (backbone GEMM + SGMV) on several workloads")
     ap.add_argument("--load", action="store_true",
                     help="time LoRA adapter uploads from host memory into HBM")
+    ap.add_argument("--phases", action="store_true",
+                    help="per-phase timeline of the one-launch decode kernel (profiling build)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args(argv)
@@ -1003,6 +1088,8 @@ def main(argv=None) -> int:
         print(json.dumps({"copy_probe_bytes": 2 * n}))
         return 0
 
+    if args.phases:
+        return run_phases(device, args)
     if args.sweep:
         return run_sweep(args.sweep, device, args)
     if args.layer:
@@ -1015,20 +1102,23 @@ def main(argv=None) -> int:
     p = workload_problem(args.workload)
     m = measure(p, device, args.steps, args.warmup, eager=args.eager,
                 force_table=args.path == "table", force_device=args.path == "device",
-                host_ids=args.path == "host", warm=not args.cold_only)
+                host_ids=use_host_ids(args.path, p), warm=not args.cold_only)
     rig, parity, use_graph = m["rig"], m["parity"], m["use_graph"]
     wall, gpu_step, call_s, call_how, flag = (m["wall"], m["gpu_step"], m["call_s"],
                                               m["call_how"], m["flag"])
 
     nbytes = algorithmic_bytes(p)
     flops = algorithmic_flops(p)
-    if args.path != "device" or p.n <= 64:
-        traffic, traffic_src = load_traffic(args.workload, rig.pool_path and p.n <= 64)
+    if rig.host_ids:
+        traffic, traffic_src = load_traffic(args.workload, "lora_add_ids_kernel")
+    elif rig.pool_path and p.n <= 64:
+        traffic, traffic_src = load_traffic(args.workload, "lora_add_pool_kernel")
+    elif not rig.pool_path:
+        traffic, traffic_src = load_traffic(args.workload, "sgmv_lora_add")
     else:
         traffic, traffic_src = None, "no counter summary for the device-id table path"
     if rig.host_ids:
         kernel = "lora_add_ids_kernel (one launch per call, ids in the kernel arguments)"
-        traffic, traffic_src = None, "no counter summary for the host-id kernel"
     elif rig.pool_path and p.n <= 64:
         kernel = "lora_add_pool_kernel (one launch per call)"
     elif rig.pool_path:
