@@ -782,22 +782,37 @@ inline int expand_strip_groups(int strips, int tiles) {
   return best;
 }
 
-// split-K slices of long rows that the MFMA expand adds itself (above: reduce_v_kernel)
-constexpr int kExpandSlices = 4;
+// split-K slices of long rows that the MFMA expand adds itself (more: reduce_v_kernel
+// first): four; with one-pass tiles at r = 16 (few tiles, registers to spare) sixteen, so
+// that the LDS-staged shrink's slices (11 for the 70B batch) need no reduce pass there.
+// Measured on MI355X, 70B mixed batch at r = 16, graph replay: k/v 36.6 -> 34.4 us; with
+// two-pass tiles sixteen slices cost more occupancy than the reduce pass (q/o 48.6 -> 54.7
+// us, gate/up 90.4 -> 96.8, down 70.8 -> 75.0).
+template <int R, int P>
+constexpr int kExpandSlices = (R == 16 && P == 1) ? 16 : 4;
 
-template <int R>
+template <int R, int P = 2>
 struct ExpCfg {
   // rows per pass and columns per tile (TC/4 columns per wave); measured on MI355X
   static constexpr int TRP = 32;
   static constexpr int TC = (R == 32) ? 128 : 256;
   // passes over the tile's rows, one after another with the same B registers: B is read
-  // once for PASSES * TRP rows
-  static constexpr int PASSES = 2;
+  // once for PASSES * TRP rows (one pass when two would leave CUs without a tile)
+  static constexpr int PASSES = P;
   static constexpr int TR = TRP * PASSES;            // rows per tile
   static constexpr int RB = TRP / 16, CB = TC / 64;  // 16 x 16 blocks per wave and pass
-  // waves per SIMD the register budget is set for (five spill at r = 64)
-  static constexpr int WAVES_PER_SIMD = (R == 64) ? 4 : 5;
+  // waves per SIMD the register budget is set for (five spill at r = 64; one-pass tiles are
+  // used only when there are fewer tiles than CUs, so at most two waves per SIMD are ever
+  // resident and they get the registers of two)
+  static constexpr int WAVES_PER_SIMD = (P == 1) ? 2 : (R == 64) ? 4 : 5;
 };
+
+// the register budget of a launch that also adds VS split-K slices (sixteen slices need
+// more registers than five waves per SIMD leave)
+template <int R, int P, int VS>
+constexpr int exp_waves_per_simd() {
+  return (VS > 4 && ExpCfg<R, P>::WAVES_PER_SIMD > 4) ? 4 : ExpCfg<R, P>::WAVES_PER_SIMD;
+}
 
 // The B operand of one run for a wave's CB column blocks.  The blocks come in pairs whose
 // 16 columns are interleaved in groups of 4: block 2p + h, lane (l16, kq) takes column
@@ -820,8 +835,8 @@ __device__ inline void exp_load_b(gptr<const uint16_t> B, int wc, int l16, int k
 
 // VS: v comes as up to VS split-K slices (vks of them, vslice floats apart) that are added
 // here in slice order; VS == 1: v is final.
-template <int DT, int R, int VS>
-__global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_kernel(
+template <int DT, int R, int VS, int P>
+__global__ __launch_bounds__(256, (exp_waves_per_simd<R, P, VS>())) void expand_mfma_kernel(
     uint16_t* __restrict__ y, int64_t ld_y, const float* __restrict__ v, int64_t vslice, int32_t vks,
     const uint16_t* const* __restrict__ B_ptrs, const int32_t* __restrict__ seg_starts,
     int32_t S_host, const int32_t* __restrict__ perm, int32_t n, int32_t h_out, float scale,
@@ -829,7 +844,7 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
   const int S = meta ? meta[0] : S_host;
   if (meta && meta[2] < kLongMin) return;  // no long segment at all
   using E = Elem<DT>;
-  using C = ExpCfg<R>;
+  using C = ExpCfg<R, P>;
   constexpr int TR = C::TR, TRP = C::TRP, TC = C::TC, RB = C::RB, CB = C::CB;
   constexpr int KT = 2 * R;          // k of the hi/lo product
   constexpr int NK = KT / 32;        // MFMA k-steps
@@ -896,15 +911,23 @@ __global__ __launch_bounds__(256, ExpCfg<R>::WAVES_PER_SIMD) void expand_mfma_ke
         const int idx = tid + 256 * u;
         t[k][u] = (k < vks && g0 + idx / R < g1) ? v[k * vslice + static_cast<int64_t>(g0) * R + idx] : 0.f;
       }
-    // the slices' fixed order (sum_slices): (s0 + s1) + (s2 + s3), then + 0 (slices past
-    // vks are zeros)
-    static_assert(VS == 1 || VS == 4, "slice sum order");
+    // the slices' fixed order (sum_slices): partial sums p_q over slices q, q + 4, ...,
+    // then (p0 + p1) + (p2 + p3), then + 0 (slices past vks are zeros)
+    static_assert(VS == 1 || VS % 4 == 0, "slice sum order");
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-      if constexpr (VS == 1)
+      if constexpr (VS == 1) {
         vv[u] = t[0][u];
-      else
-        vv[u] = ((t[0][u] + t[1][u]) + (t[2][u] + t[3][u])) + 0.f;
+      } else {
+        float pq[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          pq[q] = t[q][u];
+#pragma unroll
+          for (int k = q + 4; k < VS; k += 4) pq[q] += t[k][u];
+        }
+        vv[u] = ((pq[0] + pq[1]) + (pq[2] + pq[3])) + 0.f;
+      }
     }
   }
   if (tile_long_segments_pre<TR, 256>(seg_starts, B_ptrs, S, g0, g1, sh, pre) == 0) return;  // uniform
@@ -1202,13 +1225,15 @@ hipError_t launch_expand_short(hipStream_t st, uint16_t* y, int64_t ld_y, const 
   return hipGetLastError();
 }
 
-// long segments read v as ks slices of vsrc (at most kExpandSlices, r <= 32) or final (ks 1)
-template <int DT, int R>
-hipError_t launch_expand_long(hipStream_t st, uint16_t* y, int64_t ld_y, const float* vsrc,
-                              int64_t slice, int ks, const Tables& T, int32_t h_out,
-                              float scale) {
-  const int tiles = (T.n + ExpCfg<R>::TR - 1) / ExpCfg<R>::TR;
-  const int strips = (h_out + ExpCfg<R>::TC - 1) / ExpCfg<R>::TC;
+// long segments read v as ks slices of vsrc (at most kExpandSlices<R, P>, r <= 32) or
+// final (ks 1); tiles of P passes of 32 rows
+template <int DT, int R, int P>
+hipError_t launch_expand_tiles(hipStream_t st, uint16_t* y, int64_t ld_y, const float* vsrc,
+                               int64_t slice, int ks, const Tables& T, int32_t h_out,
+                               float scale) {
+  using C = ExpCfg<R, P>;
+  const int tiles = (T.n + C::TR - 1) / C::TR;
+  const int strips = (h_out + C::TC - 1) / C::TC;
   const int xs = expand_strip_groups(strips, tiles);
   // each XCD takes at most ceil(strips / xs) strips of ceil(tiles / xt) tiles: pad the
   // grid to 8 equal shares
@@ -1218,19 +1243,40 @@ hipError_t launch_expand_long(hipStream_t st, uint16_t* y, int64_t ld_y, const f
   const dim3 grid(static_cast<unsigned>(share * kXcds));
   if (ks > 1) {
     if constexpr (R <= 32) {
-      if (ks > kExpandSlices) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((expand_mfma_kernel<DT, R, kExpandSlices>), grid, dim3(256), 0, st, y,
-                         ld_y, vsrc, slice, ks, T.ptrs, T.seg_starts, T.S, T.perm, T.n, h_out,
+      if (ks > kExpandSlices<R, P>) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((expand_mfma_kernel<DT, R, kExpandSlices<R, P>, P>), grid, dim3(256), 0, st,
+                         y, ld_y, vsrc, slice, ks, T.ptrs, T.seg_starts, T.S, T.perm, T.n, h_out,
                          scale, tiles, strips, xs, T.meta);
     } else {
       return hipErrorInvalidValue;  // r = 64: reduce_v_kernel runs first
     }
   } else {
-    hipLaunchKernelGGL((expand_mfma_kernel<DT, R, 1>), grid, dim3(256), 0, st, y, ld_y, vsrc,
+    hipLaunchKernelGGL((expand_mfma_kernel<DT, R, 1, P>), grid, dim3(256), 0, st, y, ld_y, vsrc,
                        slice, 1, T.ptrs, T.seg_starts, T.S, T.perm, T.n, h_out, scale, tiles,
                        strips, xs, T.meta);
   }
   return hipGetLastError();
+}
+
+// Two-pass tiles (B read once for 64 rows) unless they would leave CUs without a tile:
+// then one-pass tiles of 32 rows, twice as many (narrow outputs such as the 70B k/v
+// projections, h_out = 1024: 132 two-pass tiles for 256 CUs).
+constexpr int kCus = 256;
+
+template <int R>
+bool expand_one_pass(int32_t n, int32_t h_out) {
+  using C2 = ExpCfg<R, 2>;
+  const int64_t tiles2 = (n + C2::TR - 1) / C2::TR, strips = (h_out + C2::TC - 1) / C2::TC;
+  return tiles2 * strips < kCus;
+}
+
+template <int DT, int R>
+hipError_t launch_expand_long(hipStream_t st, uint16_t* y, int64_t ld_y, const float* vsrc,
+                              int64_t slice, int ks, const Tables& T, int32_t h_out,
+                              float scale) {
+  if (expand_one_pass<R>(T.n, h_out))
+    return launch_expand_tiles<DT, R, 1>(st, y, ld_y, vsrc, slice, ks, T, h_out, scale);
+  return launch_expand_tiles<DT, R, 2>(st, y, ld_y, vsrc, slice, ks, T, h_out, scale);
 }
 
 // v of every row whose slice count (rowks) is nonzero and whose kind `which` selects,
@@ -1249,8 +1295,11 @@ hipError_t launch_reduce(hipStream_t st, float* v, const Tables& T, const WsLayo
 // whether the long chain's slices need a reduce pass before its expand: a few slices are
 // added by the MFMA expand itself (r <= 32), more are summed once per row
 template <int R>
-bool long_needs_reduce(int ksl) {
-  return ksl > 1 && (ksl > kExpandSlices || R > 32);
+bool long_needs_reduce(int ksl, int32_t n, int32_t h_out) {
+  if (ksl <= 1) return false;
+  if (R > 32) return true;
+  const int most = expand_one_pass<R>(n, h_out) ? kExpandSlices<R, 1> : kExpandSlices<R, 2>;
+  return ksl > most;
 }
 
 template <int DT, int R>
@@ -1429,7 +1478,7 @@ hipError_t run_long_tail(hipStream_t st, uint16_t* y, int64_t ld_y, const Tables
                          char* ws, const Plan& P) {
   float* v_long = reinterpret_cast<float*>(ws + L.v_off);
   const float* part = reinterpret_cast<const float*>(ws + L.part_off);
-  if (long_needs_reduce<R>(P.ksl)) {
+  if (long_needs_reduce<R>(P.ksl, TA.n, h_out)) {
     const hipError_t e = launch_reduce<R>(st, v_long, TA, L, ws, kReduceLong);
     if (e != hipSuccess) return e;
     return launch_expand_long<DT, R>(st, y, ld_y, v_long, 0, 1, TB, h_out, scale);
@@ -1509,7 +1558,7 @@ hipError_t run_lora_add(hipStream_t st, uint16_t* y, int64_t ld_y, const uint16_
   if ((e = launch_shrink_short<DT, R>(st, x, ld_x, TA, h_in, L, ws, P)) != hipSuccess) return e;
   if ((e = launch_shrink_long<DT, R>(st, x, ld_x, TA, h_in, L, ws, v_long, P)) != hipSuccess)
     return e;
-  if (long_needs_reduce<R>(P.ksl) || P.ksg > 16) {
+  if (long_needs_reduce<R>(P.ksl, TA.n, h_out) || P.ksg > 16) {
     if ((e = launch_reduce<R>(st, v_long, TA, L, ws, kReduceAll)) != hipSuccess) return e;
     if ((e = launch_expand_short<DT, R>(st, y, ld_y, v_long, 0, 1, TB, h_out, scale)) != hipSuccess)
       return e;
