@@ -1263,20 +1263,43 @@ hipError_t launch_expand_tiles(hipStream_t st, uint16_t* y, int64_t ld_y, const 
 // projections, h_out = 1024: 132 two-pass tiles for 256 CUs).
 constexpr int kCus = 256;
 
+// at r = 32 four passes with four slices would spill registers
+template <int R>
+constexpr int kExpandMaxPasses = (R == 32) ? 3 : 4;
+
+// Passes per tile: one when two-pass tiles would leave CUs without a tile; else the
+// fewest passes (2 to 4) whose tiles all fit on the GPU at once, so that no tail round of
+// tiles runs after the others (13B gate/up: 1728 two-pass tiles for 1280 resident
+// workgroups, 1188 three-pass tiles); two when no count fits.
+template <int R>
+int expand_passes(int32_t n, int32_t h_out) {
+  const int64_t strips = (h_out + ExpCfg<R, 2>::TC - 1) / ExpCfg<R, 2>::TC;
+  auto tiles = [&](int p) { return (n + 32 * p - 1) / (32 * p) * strips; };
+  if (tiles(2) < kCus) return 1;
+  const int64_t resident = static_cast<int64_t>(kCus) * ExpCfg<R, 2>::WAVES_PER_SIMD;
+  for (int p = 2; p <= kExpandMaxPasses<R>; ++p)
+    if (tiles(p) <= resident) return p;
+  return 2;
+}
+
 template <int R>
 bool expand_one_pass(int32_t n, int32_t h_out) {
-  using C2 = ExpCfg<R, 2>;
-  const int64_t tiles2 = (n + C2::TR - 1) / C2::TR, strips = (h_out + C2::TC - 1) / C2::TC;
-  return tiles2 * strips < kCus;
+  return expand_passes<R>(n, h_out) == 1;
 }
 
 template <int DT, int R>
 hipError_t launch_expand_long(hipStream_t st, uint16_t* y, int64_t ld_y, const float* vsrc,
                               int64_t slice, int ks, const Tables& T, int32_t h_out,
                               float scale) {
-  if (expand_one_pass<R>(T.n, h_out))
-    return launch_expand_tiles<DT, R, 1>(st, y, ld_y, vsrc, slice, ks, T, h_out, scale);
-  return launch_expand_tiles<DT, R, 2>(st, y, ld_y, vsrc, slice, ks, T, h_out, scale);
+  switch (expand_passes<R>(T.n, h_out)) {
+    case 1: return launch_expand_tiles<DT, R, 1>(st, y, ld_y, vsrc, slice, ks, T, h_out, scale);
+    case 3: return launch_expand_tiles<DT, R, 3>(st, y, ld_y, vsrc, slice, ks, T, h_out, scale);
+    case 4:
+      if constexpr (kExpandMaxPasses<R> >= 4)
+        return launch_expand_tiles<DT, R, 4>(st, y, ld_y, vsrc, slice, ks, T, h_out, scale);
+      return hipErrorInvalidValue;
+    default: return launch_expand_tiles<DT, R, 2>(st, y, ld_y, vsrc, slice, ks, T, h_out, scale);
+  }
 }
 
 // v of every row whose slice count (rowks) is nonzero and whose kind `which` selects,

@@ -47,8 +47,15 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16/fp16 MFMA, AMD published figure
 ROTATION_BYTES = 1 << 30       # operand slots cycled per pass (> 2x the 256 MB MALL)
 FLUSH_BYTES = 1 << 30          # read before every timed replay (4x the 256 MB MALL)
-KERNEL_SRCS = [os.path.join(ROOT, "adapter_gemv_amd", "csrc", f)
+_CSRC = os.path.join(ROOT, "adapter_gemv_amd", "csrc")
+KERNEL_SRCS = [os.path.join(_CSRC, f)
                for f in ("sgmv_checks.h", "sgmv_device.h", "sgmv_kernels.hip", "sgmv_decode.hip")]
+# the sources each kernel's code comes from (a counter summary stays valid while they do)
+KERNEL_SRCS_OF = {
+    "lora_add_pool_kernel": ("sgmv_checks.h", "sgmv_device.h", "sgmv_decode.hip"),
+    "lora_add_ids_kernel": ("sgmv_checks.h", "sgmv_device.h", "sgmv_decode.hip"),
+    "sgmv_lora_add": ("sgmv_checks.h", "sgmv_device.h", "sgmv_kernels.hip"),
+}
 
 
 def workload_problem(name: str):
@@ -78,9 +85,12 @@ def algorithmic_flops(p) -> int:
     return 2 * p.n * p.r * (p.h_in + p.h_out)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str = "") -> str:
+    """First 16 hex digits of the SHA-256 of the kernel sources: all of them, or those that
+    `kernel` (a key of KERNEL_SRCS_OF) is built from."""
+    paths = [os.path.join(_CSRC, f) for f in KERNEL_SRCS_OF[kernel]] if kernel else KERNEL_SRCS
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
+    for path in paths:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -455,9 +465,9 @@ def load_traffic(workload: str, kernel: str):
                 k, v = line.split(":", 1)
                 rec[k.strip()] = v.split()[0] if v.split() else ""
     src = rec.get("kernel_source_sha256_16")
-    if src != kernel_source_hash():
+    if src != kernel_source_hash(kernel):
         return None, (f"{rel} was taken on kernel source {src}, not this build's "
-                      f"{kernel_source_hash()}")
+                      f"{kernel_source_hash(kernel)} ({', '.join(KERNEL_SRCS_OF[kernel])})")
     return int(float(rec["hbm_bytes_per_call"])), (
         f"from {rel}: FETCH_SIZE + WRITE_SIZE per call from two rocprofv3 --pmc runs, scaled "
         f"by a plain copy of known size; taken on kernel source {src}, the same as this "
@@ -1177,6 +1187,8 @@ def main(argv=None) -> int:
         "parity": parity,
         "workspace_flag_after": flag,
         "kernel_source_sha256_16": kernel_source_hash(),
+        "kernel_source_sha256_16_by_path": {k: kernel_source_hash(k) for k in
+                                            ("lora_add_ids_kernel", "sgmv_lora_add")},
     }
     if m["warm_s"] is not None:
         out["warm"] = {"us_per_call": round(m["warm_s"] * 1e6, 3),
