@@ -559,15 +559,32 @@ struct ShrLdsCfg {
   static constexpr int XPW = RBW * UN;  // x blocks per wave and stage
   static constexpr int LPS = 1 + XPW;   // 1 KB loads per wave and stage
   static constexpr int D = D_;          // stage buffers
+  // Row-run blocks (r = 16, 64-row tiles): a block holds 4 rows x 128 k (256 contiguous
+  // bytes of each row) instead of 16 rows x 32 k (64 bytes of each), which HBM serves
+  // about 1.5 times faster on MI355X; the MFMA reads them back through the slot map below.
+  static constexpr bool RUNS = UN == 4 && RBW == 1;
+  static constexpr int SLOTS = RUNS ? 65 : 64;  // 16-byte slots per block (one pad slot)
   static_assert(NB * UN == 4 && RBW >= 1 && MT <= 256, "tile shape");
   static_assert(D >= 3 && D <= 8 && (D - 2) * LPS < 64, "ring depth");
 };
 
 template <class C>
 struct ShrStage {
-  uint4 a[4][64];          // A block j: k step j / NB, columns 16 * (j % NB) ..
-  uint4 x[4][C::XPW][64];  // wave w's x block i: k step i / RBW, rows 16 * (i % RBW) ..
+  // A block j: k step j / NB, columns 16 * (j % NB) ..; row-run blocks: A rows 4j .. 4j + 3
+  uint4 a[4][C::SLOTS];
+  // wave w's x block i: k step i / RBW, rows 16 * (i % RBW) ..; row-run blocks: the wave's
+  // rows 4i .. 4i + 3
+  uint4 x[4][C::XPW][C::SLOTS];
 };
+
+// Row-run block layout: row j (0..3) of a block, 16-byte piece p (0..15, k = 8p .. 8p + 7
+// of the stage) sits in slot 16j + ((p + 4j) mod 16).  The loading lane of a slot is the
+// slot itself, so every aligned group of four lanes fetches 64 contiguous bytes.  The
+// MFMA lanes that read one 16-row k step at a time (rows 4i + j of blocks i) then hit 16
+// different 16-byte bank groups: block i starts i pad slots further on (65-slot blocks)
+// and the rotation by 4j separates the rows of a block.
+__device__ inline int run_slot(int j, int p) { return 16 * j + ((p + 4 * j) & 15); }
+__device__ inline int run_piece(int slot) { return ((slot & 15) - 4 * (slot >> 4)) & 15; }
 
 // wait until at most N vector-memory loads of this wave are in flight (gfx9 s_waitcnt:
 // vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima)
@@ -677,27 +694,60 @@ __global__ __launch_bounds__(256) void shrink_lds_kernel(
     }
     const gptr<const uint16_t> ar =
         global_ptr(sh.ptr[sg]) + static_cast<int64_t>(anb * 16 + mrow) * h_in;
+    // row-run loads: this lane fetches row 4i + lane / 16 of the wave's rows (block i) and
+    // piece run_piece(lane) of the stage; A row 4w + lane / 16 for the wave's A block
+    [[maybe_unused]] gptr<const uint16_t> xrun[4];
+    [[maybe_unused]] gptr<const uint16_t> arun = nullptr;
+    [[maybe_unused]] const int kpiece = 8 * run_piece(lane);
+    if constexpr (C::RUNS) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int qr = qw + 4 * i + (lane >> 4);
+        xrun[i] = global_ptr(x) + static_cast<int64_t>(s_prow[sh.rseg[qr] == sg ? qr : 0]) * ld_x;
+      }
+      arun = global_ptr(sh.ptr[sg]) + static_cast<int64_t>(4 * w + (lane >> 4)) * h_in;
+    }
     auto issue = [&](auto J, int s) {
       ShrStage<C>& st = buf(J);
-      const int k0 = k_lo + s * STAGE + 8 * kq;
-      const int ka = k0 + 32 * au;
-      load_to_lds(ar + (ka < k_hi ? ka : k_last), &st.a[w][0]);
-#pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        const int kk = k0 + 32 * u;
+      if constexpr (C::RUNS) {
+        const int kk = k_lo + s * STAGE + kpiece;
         const int off = kk < k_hi ? kk : k_last;
+        load_to_lds(arun + off, &st.a[w][0]);
 #pragma unroll
-        for (int rb = 0; rb < RBW; ++rb) load_to_lds(xr[rb] + off, &st.x[w][u * RBW + rb][0]);
+        for (int i = 0; i < 4; ++i) load_to_lds(xrun[i] + off, &st.x[w][i][0]);
+      } else {
+        const int k0 = k_lo + s * STAGE + 8 * kq;
+        const int ka = k0 + 32 * au;
+        load_to_lds(ar + (ka < k_hi ? ka : k_last), &st.a[w][0]);
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+          const int kk = k0 + 32 * u;
+          const int off = kk < k_hi ? kk : k_last;
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb) load_to_lds(xr[rb] + off, &st.x[w][u * RBW + rb][0]);
+        }
       }
     };
     auto compute = [&](auto J, int s) {
       const ShrStage<C>& st = buf(J);
       const int k0 = k_lo + s * STAGE + 8 * kq;
       uint4 av[4], xv[XPW];
+      if constexpr (C::RUNS) {
+        // k step u: MFMA lane (mrow, kq) takes piece 4u + kq of row mrow (block mrow / 4)
+        // for x and of A row mrow for the adapter
+        const int i = mrow >> 2, j = mrow & 3;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) av[j] = st.a[j][lane];
+        for (int u = 0; u < 4; ++u) {
+          const int slot = run_slot(j, 4 * u + kq);
+          av[u] = st.a[i][slot];
+          xv[u] = st.x[w][i][slot];
+        }
+      } else {
 #pragma unroll
-      for (int i = 0; i < XPW; ++i) xv[i] = st.x[w][i][lane];
+        for (int j = 0; j < 4; ++j) av[j] = st.a[j][lane];
+#pragma unroll
+        for (int i = 0; i < XPW; ++i) xv[i] = st.x[w][i][lane];
+      }
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
         const bool in = k0 + 32 * u < k_hi;

@@ -397,9 +397,44 @@ def queued_time(body, count: int, flush=None) -> float:
     return e0.elapsed_time(e1) * 1e-3 / count
 
 
+def captured_call_time(rig) -> bool:
+    """Whether the call's duration is taken from a graph replay: the device-table path
+    (device ids, n > 64), whose captured calls overlap their two chains."""
+    from adapter_gemv_amd import sgmv
+    return rig.pool_path and not rig.host_ids and rig.p.n > sgmv.DECODE_MAX_TOKENS
+
+
+def graph_call_time(rig, slot: int, count: int) -> float:
+    """Average duration of `count` captured calls on one slot (warm caches), from HIP
+    events around a replay queued behind a spin kernel."""
+    import torch
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        rig.step(slot)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(count):
+            rig.step(slot)
+    g.replay()
+    gpu_hold()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e-3 / count
+
+
 def warm_call_time(rig, steps: int, use_graph: bool) -> float:
     """The SGMV call with warm caches: every call on the same slot (slot 1, not the
     parity slot), so its operands stay in the L2s and the Infinity Cache."""
+    if use_graph and captured_call_time(rig):
+        return graph_call_time(rig, 1, min(steps, 500))
     if use_graph:
         return queued_time(lambda k: rig.step(1), steps)
     return kernel_pass(rig, 1, min(steps, 500), fixed_slot=1)
@@ -515,18 +550,29 @@ def measure(p, device, steps: int, warmup: int, eager: bool = False, force_table
                 rig.step(base + k)
         graph.replay()                     # untimed: uploads the graph
         torch.cuda.synchronize()
-        # The kernel's duration: the K calls launched one after another on the stream,
-        # queued behind a cache flush and a spin kernel long enough for the host to
-        # enqueue them all, so that the GPU runs them back to back and the HIP events
-        # around them see no launch gap (a graph launch adds about 12 us of its own per
-        # replay on this GPU, whatever it holds).
-        flush_caches(device, wait=False)
-        gpu_hold(100.0 + 40.0 * steps, sync=False)
         k_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-        k_ev[0].record(stream)
-        for k in range(steps):
-            rig.step(base + k)
-        k_ev[1].record(stream)
+        if captured_call_time(rig):
+            # Device tables (n > 64): a captured call runs its short- and long-segment
+            # chains side by side, an eager one runs them one after the other, so the
+            # call's duration is taken from the graph: HIP events around a replay queued
+            # behind a cache flush (the replay's fixed cost, about 12 us on this GPU, is
+            # spread over the K calls).
+            flush_caches(device, wait=False)
+            k_ev[0].record(stream)
+            graph.replay()
+            k_ev[1].record(stream)
+        else:
+            # One launch per call: the K calls launched one after another on the stream,
+            # queued behind a cache flush and a spin kernel long enough for the host to
+            # enqueue them all, so that the GPU runs them back to back and the HIP events
+            # around them see no launch gap (a graph launch adds about 12 us of its own
+            # per replay on this GPU, whatever it holds).
+            flush_caches(device, wait=False)
+            gpu_hold(100.0 + 40.0 * steps, sync=False)
+            k_ev[0].record(stream)
+            for k in range(steps):
+                rig.step(base + k)
+            k_ev[1].record(stream)
         torch.cuda.synchronize()
         kernel_s = k_ev[0].elapsed_time(k_ev[1]) * 1e-3 / steps
         # the K steps' wall time: host clock (and HIP events) around a replay of the graph
@@ -553,7 +599,10 @@ def measure(p, device, steps: int, warmup: int, eager: bool = False, force_table
     gpu_step = t_ev[0].elapsed_time(t_ev[1]) * 1e-3 / steps
     if use_graph:
         call_s = kernel_s
-        call_how = ("HIP events around the K calls launched one after another, queued behind "
+        call_how = ("HIP events around one replay of the K captured calls (short and long "
+                    "chains side by side), queued behind a cache flush, / K"
+                    if captured_call_time(rig) else
+                    "HIP events around the K calls launched one after another, queued behind "
                     "a cache flush and a spin kernel (no launch gap), / K")
     else:
         call_s = kernel_pass(rig, base + steps, min(steps, 500))
