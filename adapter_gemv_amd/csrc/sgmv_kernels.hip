@@ -392,7 +392,7 @@ struct ShrCfg {
 inline bool shrink_lds_long_rows(int32_t h_in, bool has_short) {
   return h_in > 16384 || (has_short && h_in > 6144);
 }
-template <int R> constexpr int kLdsD = (R == 16) ? 3 : 6;  // stage buffers
+template <int R> constexpr int kLdsD = (R == 16) ? 3 : 4;  // stage buffers
 constexpr int kLdsMT = 64;                                  // rows per tile
 constexpr int kLdsWgs = 512;                                // workgroup target
 // Loads of one stage.  They are unconditional (out-of-range k reads offset 0 of the same
@@ -539,52 +539,54 @@ __global__ __launch_bounds__(256, ShrCfg<R>::WAVES_PER_SIMD) void shrink_mfma_ke
 
 // Shrink on MFMA with the operands staged in LDS by direct global-to-LDS loads.  Same
 // product and outputs as shrink_mfma_kernel, organised to keep many bytes in flight at a
-// small register cost: every 1 KB operand block (64 lanes x 16 bytes, fetched in the
-// MFMA's lane order) goes straight from global memory into a ring of D stage buffers, so
-// D - 1 stages are in flight while one is multiplied.  The four waves split the tile's
-// rows (each owns MT / 4 rows over the whole chunk) and share the stage's A blocks, so A
-// is fetched once per tile and chunk for all MT rows, and no cross-wave sum is needed.  A
-// stage covers k = 32 * UN with NB * UN = 4 A blocks, one fetched by each wave.  A wave
-// waits for its own loads of a stage (vmcnt), then a barrier makes every wave's loads
-// visible; the same barrier tells each wave that all waves have finished reading the
-// buffer it refills next.  The stage buffers are separate LDS variables addressed with
-// compile-time indices, so that the compiler can tell which loads a read depends on.
+// small register cost: operands go straight from global memory into a ring of D stage
+// buffers, so D - 1 stages are in flight while one is multiplied.  Tiles are 64 rows; the
+// four waves split them (16 rows each, over the whole chunk) and share the stage's A
+// blocks, so A is fetched once per tile and chunk for all 64 rows and no cross-wave sum is
+// needed.  A stage covers STAGE values of k (128 at r = 16, 64 at r = 64), and every load
+// instruction fills one block of RPB rows x STAGE k: 4 rows x 256 contiguous bytes at
+// r = 16, 8 rows x 128 bytes at r = 64.  HBM serves such row runs about 1.5 times faster
+// on MI355X than 16 rows x 64 bytes, the MFMA operand's own shape (a read-only probe of
+// the 70B down projection's x: 117 MB in 28 instead of 35 us); the MFMA lanes read the
+// blocks back through a slot map (run_slot).  A wave waits for its own loads of a stage
+// (vmcnt), then a barrier makes every wave's loads visible; the same barrier tells each
+// wave that all waves have finished reading the buffer it refills next.  The stage buffers
+// are separate LDS variables addressed with compile-time indices, so that the compiler can
+// tell which loads a read depends on.
 template <int R, int MT_, int D_>
 struct ShrLdsCfg {
-  static constexpr int NB = R / 16;     // column blocks of v
-  static constexpr int MT = MT_;        // rows per tile
-  static constexpr int RBW = MT / 64;   // 16-row blocks per wave
-  static constexpr int UN = 4 / NB;     // k steps of 32 per stage
-  static constexpr int STAGE = 32 * UN;
-  static constexpr int XPW = RBW * UN;  // x blocks per wave and stage
-  static constexpr int LPS = 1 + XPW;   // 1 KB loads per wave and stage
-  static constexpr int D = D_;          // stage buffers
-  // Row-run blocks (r = 16, 64-row tiles): a block holds 4 rows x 128 k (256 contiguous
-  // bytes of each row) instead of 16 rows x 32 k (64 bytes of each), which HBM serves
-  // about 1.5 times faster on MI355X; the MFMA reads them back through the slot map below.
-  static constexpr bool RUNS = UN == 4 && RBW == 1;
-  static constexpr int SLOTS = RUNS ? 65 : 64;  // 16-byte slots per block (one pad slot)
-  static_assert(NB * UN == 4 && RBW >= 1 && MT <= 256, "tile shape");
+  static_assert(R == 16 || R == 64, "ranks of the LDS-staged shrink");
+  static constexpr int NB = R / 16;                  // column blocks of v
+  static constexpr int MT = MT_;                     // rows per tile
+  static constexpr int STAGE = R == 16 ? 128 : 64;   // k per stage
+  static constexpr int UN = STAGE / 32;              // MFMA k steps per stage
+  static constexpr int PPR = STAGE / 8;              // 16-byte pieces per row and stage
+  static constexpr int RPB = 64 / PPR;               // rows per block (one load instruction)
+  static constexpr int XB = 16 / RPB;                // x blocks per wave and stage
+  static constexpr int AB = R / RPB / 4;             // A blocks per wave and stage
+  static constexpr int LPS = XB + AB;                // loads per wave and stage
+  static constexpr int PAD = 16 / XB;                // pad slots after each block
+  static constexpr int SLOTS = 64 + PAD;             // 16-byte slots per block
+  static constexpr int D = D_;                       // stage buffers
+  static_assert(MT == 64, "64-row tiles");
   static_assert(D >= 3 && D <= 8 && (D - 2) * LPS < 64, "ring depth");
 };
-
 template <class C>
 struct ShrStage {
-  // A block j: k step j / NB, columns 16 * (j % NB) ..; row-run blocks: A rows 4j .. 4j + 3
-  uint4 a[4][C::SLOTS];
-  // wave w's x block i: k step i / RBW, rows 16 * (i % RBW) ..; row-run blocks: the wave's
-  // rows 4i .. 4i + 3
-  uint4 x[4][C::XPW][C::SLOTS];
+  uint4 a[4 * C::AB][C::SLOTS];  // block b: A rows RPB * b .. RPB * b + RPB - 1
+  uint4 x[4][C::XB * C::SLOTS];  // wave w's block i (tile rows 16w + RPB * i ..) at [w][i * SLOTS]
 };
 
-// Row-run block layout: row j (0..3) of a block, 16-byte piece p (0..15, k = 8p .. 8p + 7
-// of the stage) sits in slot 16j + ((p + 4j) mod 16).  The loading lane of a slot is the
-// slot itself, so every aligned group of four lanes fetches 64 contiguous bytes.  The
-// MFMA lanes that read one 16-row k step at a time (rows 4i + j of blocks i) then hit 16
-// different 16-byte bank groups: block i starts i pad slots further on (65-slot blocks)
-// and the rotation by 4j separates the rows of a block.
-__device__ inline int run_slot(int j, int p) { return 16 * j + ((p + 4 * j) & 15); }
-__device__ inline int run_piece(int slot) { return ((slot & 15) - 4 * (slot >> 4)) & 15; }
+// Block layout: row j (0 .. RPB - 1) of a block, 16-byte piece p (k = 8p .. 8p + 7 of the
+// stage; 0 .. PPR - 1) sits in slot PPR * j + (p + j) mod PPR, and the lane that loads it
+// is the slot itself.  The MFMA lanes reading one k step (16 rows, one piece each, from
+// 16 / RPB consecutive blocks) then meet no bank conflict whether the LDS serves 16 lanes
+// over 64 banks or 8 lanes over 32 banks at a time: the rotation by j separates the rows
+// of a block, and the PAD slots after each block (16 / XB) separate the blocks.
+template <int PPR>
+__device__ inline int run_slot(int j, int p) { return PPR * j + ((p + j) & (PPR - 1)); }
+template <int PPR>
+__device__ inline int run_piece(int slot) { return ((slot & (PPR - 1)) - slot / PPR) & (PPR - 1); }
 
 // wait until at most N vector-memory loads of this wave are in flight (gfx9 s_waitcnt:
 // vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima)
@@ -602,10 +604,13 @@ __device__ inline void load_to_lds(gptr<const uint16_t> src, uint4* dst) {
   __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)dst, 16, 0, 0);
 }
 
-// workgroup barrier with no memory fence (so no wait for the loads in flight); the
-// signal fences keep the compiler from moving LDS accesses across it
+// workgroup barrier that does not wait for the global loads in flight: it waits only for
+// this wave's LDS reads (lgkmcnt 0), so that a wave past the barrier may refill a stage
+// buffer that every wave has finished reading, not merely issued its reads of; the signal
+// fences keep the compiler from moving LDS accesses across it
 __device__ inline void barrier_no_fence() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0) only
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
@@ -626,8 +631,8 @@ __global__ __launch_bounds__(256) void shrink_lds_kernel(
     float* __restrict__ v_out, int32_t* __restrict__ rowks, int32_t rk_short,
     int32_t* __restrict__ bad_flag, const int32_t* __restrict__ meta) {
   using C = ShrLdsCfg<R, MT, D>;
-  constexpr int NB = C::NB, RBW = C::RBW, UN = C::UN, STAGE = C::STAGE, XPW = C::XPW;
-  constexpr int LPS = C::LPS;
+  constexpr int NB = C::NB, UN = C::UN, STAGE = C::STAGE, PPR = C::PPR, RPB = C::RPB;
+  constexpr int XB = C::XB, AB = C::AB, LPS = C::LPS;
   const int S = meta ? meta[0] : S_host;
   if (meta && meta[2] < kLongMin) return;  // no long segment at all
   __shared__ TileSegs<MT> sh;
@@ -673,91 +678,62 @@ __global__ __launch_bounds__(256) void shrink_lds_kernel(
   // 16 bytes of the row again (just fetched, so a cache hit) and multiplies zeros
   const int nst = ((k_hi - k_lo + STAGE - 1) / STAGE + D - 1) / D * D;
   const int k_last = k_hi - 8;
-  const int qw = w * 16 * RBW;  // this wave's first row in the tile
-  const int au = w / NB, anb = w % NB;  // the A block this wave fetches
+  const int qw = 16 * w;  // this wave's first row in the tile
+  // loading lane: row lane / PPR of a block, piece run_piece(lane) of the stage
+  const int lrow = lane / PPR;
+  const int kpiece = 8 * run_piece<PPR>(lane);
+  // MFMA lane (mrow, kq): row mrow of the wave's rows (block mrow / RPB) for x, A row
+  // 16 nb + mrow for column block nb; piece 4u + kq in k step u
+  const int bi = mrow / RPB, bj = mrow % RPB;
 
-  f32x4_t acc[RBW][NB];
+  f32x4_t acc[NB];
 #pragma unroll
-  for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   int q = 0;
   for (int sg; (sg = next_run(sh, q)) >= 0;) {
     // rows outside the run fetch row r0 of the tile (it exists) and are zeroed below
-    gptr<const uint16_t> xr[RBW];
-    bool xin[RBW];
+    const bool xin = sh.rseg[qw + mrow] == sg;
+    gptr<const uint16_t> xrun[XB], arun[AB];
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) {
-      const int qr = qw + 16 * rb + mrow;
-      xin[rb] = sh.rseg[qr] == sg;
-      xr[rb] = global_ptr(x) + static_cast<int64_t>(s_prow[xin[rb] ? qr : 0]) * ld_x;
+    for (int i = 0; i < XB; ++i) {
+      const int qr = qw + RPB * i + lrow;
+      xrun[i] = global_ptr(x) + static_cast<int64_t>(s_prow[sh.rseg[qr] == sg ? qr : 0]) * ld_x;
     }
-    const gptr<const uint16_t> ar =
-        global_ptr(sh.ptr[sg]) + static_cast<int64_t>(anb * 16 + mrow) * h_in;
-    // row-run loads: this lane fetches row 4i + lane / 16 of the wave's rows (block i) and
-    // piece run_piece(lane) of the stage; A row 4w + lane / 16 for the wave's A block
-    [[maybe_unused]] gptr<const uint16_t> xrun[4];
-    [[maybe_unused]] gptr<const uint16_t> arun = nullptr;
-    [[maybe_unused]] const int kpiece = 8 * run_piece(lane);
-    if constexpr (C::RUNS) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qr = qw + 4 * i + (lane >> 4);
-        xrun[i] = global_ptr(x) + static_cast<int64_t>(s_prow[sh.rseg[qr] == sg ? qr : 0]) * ld_x;
-      }
-      arun = global_ptr(sh.ptr[sg]) + static_cast<int64_t>(4 * w + (lane >> 4)) * h_in;
-    }
+    for (int t = 0; t < AB; ++t)
+      arun[t] = global_ptr(sh.ptr[sg]) + static_cast<int64_t>(RPB * (AB * w + t) + lrow) * h_in;
     auto issue = [&](auto J, int s) {
       ShrStage<C>& st = buf(J);
-      if constexpr (C::RUNS) {
-        const int kk = k_lo + s * STAGE + kpiece;
-        const int off = kk < k_hi ? kk : k_last;
-        load_to_lds(arun + off, &st.a[w][0]);
+      const int kk = k_lo + s * STAGE + kpiece;
+      const int off = kk < k_hi ? kk : k_last;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) load_to_lds(xrun[i] + off, &st.x[w][i][0]);
-      } else {
-        const int k0 = k_lo + s * STAGE + 8 * kq;
-        const int ka = k0 + 32 * au;
-        load_to_lds(ar + (ka < k_hi ? ka : k_last), &st.a[w][0]);
+      for (int t = 0; t < AB; ++t) load_to_lds(arun[t] + off, &st.a[AB * w + t][0]);
 #pragma unroll
-        for (int u = 0; u < UN; ++u) {
-          const int kk = k0 + 32 * u;
-          const int off = kk < k_hi ? kk : k_last;
-#pragma unroll
-          for (int rb = 0; rb < RBW; ++rb) load_to_lds(xr[rb] + off, &st.x[w][u * RBW + rb][0]);
-        }
-      }
+      for (int i = 0; i < XB; ++i) load_to_lds(xrun[i] + off, &st.x[w][i * C::SLOTS]);
     };
     auto compute = [&](auto J, int s) {
       const ShrStage<C>& st = buf(J);
       const int k0 = k_lo + s * STAGE + 8 * kq;
-      uint4 av[4], xv[XPW];
-      if constexpr (C::RUNS) {
-        // k step u: MFMA lane (mrow, kq) takes piece 4u + kq of row mrow (block mrow / 4)
-        // for x and of A row mrow for the adapter
-        const int i = mrow >> 2, j = mrow & 3;
+      // every operand is read unconditionally and masked afterwards: a read under a branch
+      // made the compiler wait for every load in flight first
+      uint4 xv[UN], av[UN][NB];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int slot = run_slot(j, 4 * u + kq);
-          av[u] = st.a[i][slot];
-          xv[u] = st.x[w][i][slot];
-        }
-      } else {
+      for (int u = 0; u < UN; ++u) {
+        const int slot = run_slot<PPR>(bj, 4 * u + kq);
+        // (the bound is never reached; without it the compiler cannot tell this read from
+        // the global-to-LDS loads in flight into the other stage buffers and waits for all
+        // of them first)
+        xv[u] = st.x[w][min(bi * C::SLOTS + slot, XB * C::SLOTS - 1)];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) av[j] = st.a[j][lane];
-#pragma unroll
-        for (int i = 0; i < XPW; ++i) xv[i] = st.x[w][i][lane];
+        for (int nb = 0; nb < NB; ++nb) av[u][nb] = st.a[16 * nb / RPB + bi][slot];
       }
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
         const bool in = k0 + 32 * u < k_hi;
+        const uint4 xa = (in && xin) ? xv[u] : zero4();
 #pragma unroll
-        for (int rb = 0; rb < RBW; ++rb) {
-          const uint4 xa = (in && xin[rb]) ? xv[u * RBW + rb] : zero4();
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            acc[rb][nb] = Elem<DT>::mfma(xa, in ? av[u * NB + nb] : zero4(), acc[rb][nb]);
-        }
+        for (int nb = 0; nb < NB; ++nb)
+          acc[nb] = Elem<DT>::mfma(xa, in ? av[u][nb] : zero4(), acc[nb]);
       }
     };
     auto step = [&](auto J, int s) {
@@ -775,22 +751,20 @@ __global__ __launch_bounds__(256) void shrink_lds_kernel(
     static_for<1, D>([&](auto J) { compute(J, s + J); });
     barrier_no_fence();  // the next run refills the buffers
   }
-  // rows qw + 16rb + 4(lane/16) + c, column nb*16 + lane%16
+  // rows qw + 4(lane/16) + c, column nb*16 + lane%16
 #pragma unroll
-  for (int rb = 0; rb < RBW; ++rb)
+  for (int c = 0; c < 4; ++c) {
+    const int qr = qw + 4 * kq + c;
+    if (sh.rseg[qr] < 0) continue;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int qr = qw + 16 * rb + 4 * kq + c;
-      if (sh.rseg[qr] < 0) continue;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int64_t o = static_cast<int64_t>(r0 + qr) * R + nb * 16 + mrow;
-        if (ks == 1)
-          v_out[o] = acc[rb][nb][c];
-        else
-          part[kc * slice + o] = acc[rb][nb][c];
-      }
+    for (int nb = 0; nb < NB; ++nb) {
+      const int64_t o = static_cast<int64_t>(r0 + qr) * R + nb * 16 + mrow;
+      if (ks == 1)
+        v_out[o] = acc[nb][c];
+      else
+        part[kc * slice + o] = acc[nb][c];
     }
+  }
 }
 
 // Expand on MFMA 16x16x32 for a tile of TR sorted rows and TC columns, computed
@@ -1204,11 +1178,9 @@ Plan make_plan(const Tables& T, int32_t h_in, const WsLayout& L) {
     P.lds = R == 16 && shrink_lds_long_rows(h_in, !T.meta && !T.in_group && T.use_gemv());
   }
   if (P.lds) {
-    // Chunks are whole multiples of D stages.  For the 70B batch this gives 15 chunks, not
-    // a multiple of 8, so each XCD's L2 sees every chunk of A: at r = 64 the L2s miss on A
-    // again (down projection: 175 instead of 127 MB fetched per call), but those misses are
-    // served by the Infinity Cache, and 16 chunks of 64-k multiples, padded to whole ring
-    // turns, measured 5 % slower on MI355X (down 114 vs 119 us per call).
+    // Chunks are whole multiples of D stages (384 k at r = 16, 256 at r = 64): for the 70B
+    // batch 11 chunks at r = 16 and 16 at r = 64, which are XCD-owned (each XCD's L2 then
+    // holds an eighth of A).
     if constexpr (R != 32) {
       using C = ShrLdsCfg<R, kLdsMT, kLdsD<R>>;
       split_k(T.n, h_in, L.ks_max, kLdsMT, kLdsWgs, C::STAGE * kLdsD<R>, &P.kcm, &P.ksl);
