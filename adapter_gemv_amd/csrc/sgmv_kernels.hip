@@ -392,9 +392,9 @@ struct ShrCfg {
 inline bool shrink_lds_long_rows(int32_t h_in, bool has_short) {
   return h_in > 16384 || (has_short && h_in > 6144);
 }
-template <int R> constexpr int kLdsD = (R == 16) ? 3 : 4;  // stage buffers
+template <int R> constexpr int kLdsD = 3;  // stage buffers (four at r = 64: 4-9 % slower)
 constexpr int kLdsMT = 64;                                  // rows per tile
-constexpr int kLdsWgs = 512;                                // workgroup target
+constexpr int kLdsWgs = 512;  // workgroups resident at once (two per CU, for their LDS)
 // Loads of one stage.  They are unconditional (out-of-range k reads offset 0 of the same
 // row, rows outside the current run read a row that exists) so that the compiler can count
 // them exactly and keep the next stage in flight; shr_mul zeroes what does not belong.
@@ -1112,15 +1112,21 @@ static_assert(GemvCfg<16>::KC == 512 && GemvCfg<32>::KC == 256 && GemvCfg<64>::K
 // of 8 chunks where there are 8 or more before the rounding (XCD-owned chunks), and no
 // more slices than the workspace holds
 inline void split_k(int32_t n, int32_t h_in, int ks_cap, int mt, int target, int granule,
-                    int* kcm, int* ks) {
+                    int* kcm, int* ks, bool resident = false) {
   const int tiles = (n + mt - 1) / mt;
   int k = (target + tiles - 1) / tiles;
   k = min(k, max(1, h_in / 256));
   k = max(1, min(k, ks_cap));
   if (k >= 8) k -= k % 8;
-  const int c = ((h_in + k - 1) / k + granule - 1) / granule * granule;
-  *kcm = c;
-  *ks = (h_in + c - 1) / c;
+  for (;;) {
+    const int c = ((h_in + k - 1) / k + granule - 1) / granule * granule;
+    *kcm = c;
+    *ks = (h_in + c - 1) / c;
+    // resident: every workgroup must fit on the GPU at once (target is that count), or
+    // the last ones start only when others end and the kernel takes one of them longer
+    if (!resident || k == 1 || static_cast<int64_t>(tiles) * *ks <= target) return;
+    --k;
+  }
 }
 
 template <class C>
@@ -1183,7 +1189,7 @@ Plan make_plan(const Tables& T, int32_t h_in, const WsLayout& L) {
     // holds an eighth of A).
     if constexpr (R != 32) {
       using C = ShrLdsCfg<R, kLdsMT, kLdsD<R>>;
-      split_k(T.n, h_in, L.ks_max, kLdsMT, kLdsWgs, C::STAGE * kLdsD<R>, &P.kcm, &P.ksl);
+      split_k(T.n, h_in, L.ks_max, kLdsMT, kLdsWgs, C::STAGE * kLdsD<R>, &P.kcm, &P.ksl, true);
     }
   } else {
     if constexpr (R != 64) mfma_split<ShrCfg<R>>(T.n, h_in, L.ks_max, &P.kcm, &P.ksl);
