@@ -28,6 +28,7 @@ oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -575,19 +576,31 @@ def measure(p, device, steps: int, warmup: int, eager: bool = False, force_table
             k_ev[1].record(stream)
         torch.cuda.synchronize()
         kernel_s = k_ev[0].elapsed_time(k_ev[1]) * 1e-3 / steps
-        # the K steps' wall time: host clock (and HIP events) around a replay of the graph
-        # after a cache flush
+        # the K steps' wall time: host clock around a replay of the graph after a cache
+        # flush; the GPU time of the replay (HIP events) from a second replay after another
+        # flush, so that recording the events is not in the wall time.  Two untimed
+        # replays first (warm-up: the first replays of a graph launch more slowly; the
+        # flush then evicts what they cached)
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
         flush_caches(device)
+        gc.disable()    # no collector pass inside the timed region
         t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        gc.enable()
+        flush_caches(device)
         t_ev[0].record(stream)
         graph.replay()
         t_ev[1].record(stream)
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
         del graph
     else:
         torch.cuda.synchronize()
         flush_caches(device)
+        gc.disable()
         t0 = time.perf_counter()
         t_ev[0].record(stream)
         for k in range(steps):
@@ -595,6 +608,7 @@ def measure(p, device, steps: int, warmup: int, eager: bool = False, force_table
         t_ev[1].record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        gc.enable()
     wall = (t1 - t0) / steps
     gpu_step = t_ev[0].elapsed_time(t_ev[1]) * 1e-3 / steps
     if use_graph:
