@@ -549,10 +549,10 @@ __global__ __launch_bounds__(256, ShrCfg<R>::WAVES_PER_SIMD) void shrink_mfma_ke
 // on MI355X than 16 rows x 64 bytes, the MFMA operand's own shape (a read-only probe of
 // the 70B down projection's x: 117 MB in 28 instead of 35 us); the MFMA lanes read the
 // blocks back through a slot map (run_slot).  A wave waits for its own loads of a stage
-// (vmcnt), then a barrier makes every wave's loads visible; the same barrier tells each
-// wave that all waves have finished reading the buffer it refills next.  The stage buffers
-// are separate LDS variables addressed with compile-time indices, so that the compiler can
-// tell which loads a read depends on.
+// (vmcnt) and its own LDS reads (lgkmcnt), then a barrier makes every wave's loads visible
+// and tells each wave that all waves have finished reading the buffer it refills next.
+// The stage buffers are separate LDS variables addressed with compile-time indices, so
+// that the compiler can tell which loads a read depends on.
 template <int R, int MT_, int D_>
 struct ShrLdsCfg {
   static_assert(R == 16 || R == 64, "ranks of the LDS-staged shrink");

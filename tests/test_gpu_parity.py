@@ -113,6 +113,8 @@ EXACT_CASES = [
     # r = 16, short and long segments, 6144 < h_in <= 16384: the LDS-staged shrink with a
     # reduce pass, ragged last tile
     ("lds_r16_mixed", 150, 8200, 1032, 16, 12, "mixed"),
+    # long segments only, 1100 rows (a ragged last tile of three-pass expand tiles)
+    ("long_1100", 1100, 1032, 1048, 16, 3, "blocks"),
 ]
 
 
