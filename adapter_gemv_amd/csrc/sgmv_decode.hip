@@ -42,6 +42,42 @@ constexpr int kItemsPerWg = 1;           // work items per workgroup (one per wa
                                          // workgroups spread the loads over more CUs
 constexpr uint32_t kNoKey = 0xffffffffu;
 
+// v of lane (lane ^ S), S in {1, 2, 4}: DPP quad permutations for 1 and 2, a swizzle
+// (and-mask 31, xor-mask 4) for 4
+template <int S>
+__device__ inline uint32_t xor_lane(uint32_t v) {
+  if constexpr (S == 1) return __builtin_amdgcn_mov_dpp(v, 0xb1, 0xf, 0xf, true);  // [1,0,3,2]
+  if constexpr (S == 2) return __builtin_amdgcn_mov_dpp(v, 0x4e, 0xf, 0xf, true);  // [2,3,0,1]
+  if constexpr (S == 4) return __builtin_amdgcn_ds_swizzle(v, 0x101f);
+}
+
+// an empty asm that takes v in a VGPR: everything that computes v is done before it
+__device__ inline void pin(float& v) { asm volatile("" : "+v"(v)); }
+
+// One stage of the transpose of B's words within groups of GC lanes.  bw holds the 16
+// loads of a lane, four words each (load u in bw[4u .. 4u+3]); lanes q and q ^ S swap
+// load GC*t + k (held by the lane whose bit S differs from k's) for every t and k.
+template <int GC, int S>
+__device__ inline void transpose_stage(uint32_t (&bw)[64], int q) {
+  if constexpr (S < GC) {
+    const bool hi = (q & S) != 0;
+#pragma unroll
+    for (int t = 0; t < 16 / GC; ++t)
+#pragma unroll
+      for (int k = 0; k < GC; ++k) {
+        if (k & S) continue;
+        const int lo_u = GC * t + k, hi_u = GC * t + (k | S);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          uint32_t& a = bw[4 * lo_u + d];
+          uint32_t& c = bw[4 * hi_u + d];
+          const uint32_t r = xor_lane<S>(hi ? a : c);
+          if (hi) a = r; else c = r;
+        }
+      }
+  }
+}
+
 // ------------------------------------------------------------------------------------
 // segment plan of one batch, computed by a single wavefront
 // ------------------------------------------------------------------------------------
@@ -542,6 +578,7 @@ struct PoolArgs {
   int64_t ld_y, ld_x, A_stride, B_stride;
   int32_t n, n_adapters, h_in, h_out;
   int32_t KS, NS;
+  int32_t b_delay;  // expand items: short sleeps before their B loads
   float scale;
   int32_t* ws_flag;
   int32_t* counters;
@@ -621,46 +658,104 @@ __device__ inline void shrink_item(const PoolArgs& p, const Leader& L, int blk, 
   SGMV_STAMP(p, 4, true);
 }
 
-// expand item: one caller row r and columns [nc*64*CPL, (nc+1)*64*CPL); lane owns
-// CPL = pool_cpl(R) consecutive columns, i.e. CPL * R * 2 contiguous bytes of the stored
-// [h_out, r] B[a].  Keying expand items by row spreads an adapter with many rows over as
-// many wavefronts.  B and y are loaded (and B widened to float32) while the shrink runs.
+// expand item: one caller row r and the 64 * CPL columns from c0 = nc * 64 * CPL
+// (CPL = pool_cpl(R)), whose rows of the stored [h_out, r] B[a] are 16 KB of contiguous
+// memory.  Load instruction u reads 1 KB of it: lane l gets the 8 rank values 8q .. 8q+7
+// of column c0 + u * 64/GC + l / GC, where GC = R / 8 lanes share a column and
+// q = l % GC.  A transpose within each group of GC lanes (DPP) then leaves lane l with
+// every rank value of the columns of the loads u = GC*t + q, t < 16/GC, i.e. columns
+// c0 + 64t + q * 64/GC + l / GC, so that every load of B covers whole cache lines and
+// every y access 64 consecutive columns.  Keying expand items by row spreads an adapter
+// with many rows over as many wavefronts.  The y loads are issued first; the B loads wait
+// `p.b_delay` short sleeps (chosen on the host from the bytes the shrink items fetch), so
+// that A and x, which the partial sums wait for, reach the CUs before B competes with
+// them for HBM.  B is transposed and widened to float32 while the shrink runs.
 template <int DT, int R>
 __device__ inline void expand_item(const PoolArgs& p, const Leader& L, int r, int nc) {
   using E = Elem<DT>;
-  constexpr int CPL = pool_cpl(R);
-  constexpr int NV = CPL * R / 8;  // 16-byte loads of B per lane
-  constexpr int YW = CPL / 2;
-  constexpr int G = 64 / R;  // lanes per column j when reading the partial slices
+  constexpr int GC = R / 8;     // lanes per column of B in the loads
+  constexpr int G = 64 / R;     // lane groups when reading the partial sums
+  constexpr int NV = 16;        // 16-byte loads of B per lane: 16 KB per item
+  constexpr int CPI = 64 / GC;  // columns per load instruction
+  constexpr int NT = 16 / GC;   // columns per lane
+  static_assert(NV * 64 * 8 == 64 * pool_cpl(R) * R, "an item covers 16 KB of B");
   const int lane = threadIdx.x & 63;
-  const int c0 = (nc * 64 + lane) * CPL;
-  const bool cin = c0 < p.h_out;
-  const int cl = cin ? c0 : 0;  // lanes past h_out load column 0 and store nothing
+  const int q = lane % GC, m = lane / GC;
+  const int c0 = nc * 64 * pool_cpl(R);
+  const int cq = c0 + q * CPI + m;  // the lane's column for t = 0; + 64t for t
 
-  // unconditional loads keep the compiler's wait counts exact
-  uint4 b[NV];
-  const gptr<const uint16_t> Bblk =
-      global_ptr(p.B) + static_cast<int64_t>(L.a) * p.B_stride + static_cast<int64_t>(cl) * R;
+  // unconditional loads keep the compiler's wait counts exact: columns past h_out read
+  // column 0 and store nothing
+  const gptr<uint16_t> yrow = global_ptr(p.y) + static_cast<int64_t>(r) * p.ld_y;
+  uint32_t yv[NT];
 #pragma unroll
-  for (int v = 0; v < NV; ++v) b[v] = ld16(Bblk + 8 * v);
-  uint32_t yv[YW];
-  const gptr<uint16_t> yrow = global_ptr(p.y) + static_cast<int64_t>(r) * p.ld_y + cl;
-  load_words<YW>(yrow, yv);
-  asm volatile("" ::: "memory");  // keep the B and y loads ahead of the polling below
-  float bf[CPL * R];
+  for (int t = 0; t < NT; ++t) {
+    const int c = cq + 64 * t;
+    yv[t] = *(yrow + (c < p.h_out ? c : 0));
+  }
+  asm volatile("" ::: "memory");  // keep the y loads ahead of the delay
+  for (int i = 0; i < p.b_delay; ++i) __builtin_amdgcn_s_sleep(1);
+  const gptr<const uint16_t> Bad = global_ptr(p.B) + static_cast<int64_t>(L.a) * p.B_stride + 8 * q;
+  uint32_t bw[4 * NV];
 #pragma unroll
-  for (int e = 0; e < CPL * R; ++e) bf[e] = elem<DT>(b[e >> 3], e & 7);
-  SGMV_STAMP(p, 2, true);
+  for (int u = 0; u < NV; ++u) {
+    const int c = c0 + u * CPI + m;
+    const u32x4_t v = *(gptr<const u32x4_t>)(Bad + static_cast<int64_t>(c < p.h_out ? c : 0) * R);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) bw[4 * u + d] = v[d];
+  }
+  asm volatile("" ::: "memory");  // keep the B loads ahead of the polling below
 
-  // v[r, j]: lane (j = lane % R, g = lane / R) takes slices g, g+G, ... of column j in
-  // batches of 8, polls each batch until every tag is present and adds it in order; the
-  // G lane groups are then combined by a fixed butterfly, so every lane ends with the
-  // same sum
+  // v[r, j]: lane (j = lane % R, g = lane / R) takes slices g, g+G, ... of column j,
+  // polls them until every tag is present and adds them in order; the G lane groups are
+  // then combined by a fixed butterfly, so every lane ends with the same sum.  The first
+  // two slices of each group are loaded before B is transposed (their loads go out right
+  // after B's and return behind them), the rest in batches of 8.
   const int64_t slice = pool_slice(R);
   const uint64_t* src = p.part + static_cast<int64_t>(r) * pool_part_row(R) + (lane % R);
   const int g = lane / R;
+  uint64_t w0[2];
+  auto load_first = [&]() {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {  // unconditional: slices past KS read slice KS - 1
+      const int k = g + u * G;
+      w0[u] = load_partial(src + (k < p.KS ? k : p.KS - 1) * slice);
+    }
+  };
+  load_first();
+  // the transpose takes b from here on: after the poll's loads have been issued
+#pragma unroll
+  for (int i = 0; i < 4 * NV; ++i) asm volatile("" : "+v"(bw[i])::"memory");
+  transpose_stage<GC, 1>(bw, q);
+  transpose_stage<GC, 2>(bw, q);
+  transpose_stage<GC, 4>(bw, q);
+  // bf[t * R + j] = B[column of t, j], pinned in registers here so that none of this
+  // work is left for after the poll
+  float bf[NT * R];
+#pragma unroll
+  for (int e = 0; e < NT * R; ++e) {
+    bf[e] = (e & 1) ? E::hi(bw[e >> 1]) : E::lo(bw[e >> 1]);
+    pin(bf[e]);
+  }
+  SGMV_STAMP(p, 2, true);
+
   float acc = 0.f;
-  for (int k0 = 0; k0 < p.KS; k0 += 8 * G) {
+  for (int spins = 0;; ++spins) {
+    bool ready = true;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) ready = ready && (g + u * G >= p.KS || (w0[u] >> 32) != 0);
+    if (__ballot(!ready) == 0) break;
+    if (spins >= kSpinLimit) {
+      if (lane == 0) raise_flag(p.ws_flag, kFlagWaitTimeout);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    load_first();
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    acc += (g + u * G < p.KS) ? __uint_as_float(static_cast<uint32_t>(w0[u])) : 0.f;
+  for (int k0 = 2 * G; k0 < p.KS; k0 += 8 * G) {
     uint64_t w[8];
     for (int spins = 0;; ++spins) {
 #pragma unroll
@@ -694,22 +789,24 @@ __device__ inline void expand_item(const PoolArgs& p, const Leader& L, int r, in
 #pragma unroll
   for (int jj = 0; jj < R; ++jj)
     vj[jj] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), jj));
-
-  if (cin) {
-    float out[CPL];
+  float out[NT];
 #pragma unroll
-    for (int cc = 0; cc < CPL; ++cc) out[cc] = 0.f;
+  for (int t = 0; t < NT; ++t) out[t] = 0.f;
 #pragma unroll
-    for (int jj = 0; jj < R; ++jj)
+  for (int jj = 0; jj < R; ++jj)
 #pragma unroll
-      for (int cc = 0; cc < CPL; ++cc) out[cc] = fmaf(vj[jj], bf[cc * R + jj], out[cc]);
-    uint32_t packed[YW];
+    for (int t = 0; t < NT; ++t) out[t] = fmaf(vj[jj], bf[t * R + jj], out[t]);
+  uint16_t yo[NT];
 #pragma unroll
-    for (int q = 0; q < YW; ++q) {
-      const float y0 = E::lo(yv[q]), y1 = E::hi(yv[q]);
-      packed[q] = E::pack(fmaf(p.scale, out[2 * q], y0), fmaf(p.scale, out[2 * q + 1], y1));
-    }
-    store_words<YW>(yrow, packed);
+  for (int t = 0; t < NT; ++t)
+    yo[t] = static_cast<uint16_t>(E::pack(fmaf(p.scale, out[t], E::lo(yv[t])), 0.f));
+  if (c0 + 64 * pool_cpl(R) <= p.h_out) {  // the whole item inside y: no per-column test
+#pragma unroll
+    for (int t = 0; t < NT; ++t) *(yrow + cq + 64 * t) = yo[t];
+  } else {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      if (cq + 64 * t < p.h_out) *(yrow + cq + 64 * t) = yo[t];
   }
   SGMV_STAMP(p, 4, false);
   SGMV_STAMP(p, 5, true);
@@ -891,6 +988,17 @@ uint64_t* next_stamps(int grid) {
 uint64_t* next_stamps(int) { return nullptr; }
 #endif
 
+// Short sleeps (64 clocks each) before an expand item loads B: about the time HBM takes
+// to deliver what the shrink items fetch (the distinct adapters' A and the rows of x),
+// kDelayPerMiB per MiB (tuned on MI355X), at most kDelayMax.
+constexpr double kDelayPerMiB = 5.0;
+constexpr int kDelayMax = 160;
+int32_t b_delay(int distinct, int n, int h_in, int r) {
+  const double mib = 2.0 * h_in * (static_cast<double>(distinct) * r + n) / (1 << 20);
+  const double d = kDelayPerMiB * mib;
+  return static_cast<int32_t>(d < kDelayMax ? d + 0.5 : kDelayMax);
+}
+
 // Arguments of the one-launch kernels (n <= 64).
 PoolArgs pool_args(void* y, int64_t ld_y, const void* x, int64_t ld_x, const int32_t* adapter_ids,
                    int32_t n, const void* A_pool, int64_t A_stride, const void* B_pool,
@@ -913,6 +1021,7 @@ PoolArgs pool_args(void* y, int64_t ld_y, const void* x, int64_t ld_x, const int
   p.KS = (h_in + pool_kc(r) - 1) / pool_kc(r);
   const int cols = 64 * pool_cpl(r);
   p.NS = (h_out + cols - 1) / cols;  // 64 lanes x pool_cpl(r) columns per item
+  p.b_delay = 0;
   p.scale = scale;
   char* ws = static_cast<char*>(workspace);
   p.ws_flag = reinterpret_cast<int32_t*>(ws);
@@ -966,9 +1075,9 @@ extern "C" int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, in
         h_in, h_out, scale, workspace));
   }
 
-  const PoolArgs p = pool_args(y, ld_y, x, ld_x, adapter_ids, n, A_pool, A_stride, B_pool,
-                               B_stride, n_adapters, h_in, h_out, r, scale, workspace,
-                               workspace_bytes);
+  PoolArgs p = pool_args(y, ld_y, x, ld_x, adapter_ids, n, A_pool, A_stride, B_pool, B_stride,
+                         n_adapters, h_in, h_out, r, scale, workspace, workspace_bytes);
+  p.b_delay = b_delay(n < n_adapters ? n : n_adapters, n, h_in, r);  // ids unknown here
   hipError_t e;
   if (dtype == SGMV_F16) {
     e = (r == 16) ? launch_pool<SGMV_F16, 16>(stream, p)
@@ -982,16 +1091,33 @@ extern "C" int sgmv_lora_add_pool(hipStream_t stream, int32_t dtype, void* y, in
 
 namespace {
 
+// Number of distinct values among ids[0 .. n), n <= 64 (open addressing in a table of 128).
+int distinct_ids(const int32_t* ids, int32_t n) {
+  uint32_t tab[128] = {};  // id + 1, 0 = empty
+  int count = 0;
+  for (int i = 0; i < n; ++i) {
+    const uint32_t key = static_cast<uint32_t>(ids[i]) + 1u;
+    uint32_t h = (key * 2654435761u) >> 25;
+    while (tab[h] != 0 && tab[h] != key) h = (h + 1) & 127u;
+    if (tab[h] == 0) {
+      tab[h] = key;
+      ++count;
+    }
+  }
+  return count;
+}
+
 // The one-launch kernel with host ids on a workspace that the caller's checks accepted.
 int run_host_ids(hipStream_t stream, int32_t dtype, void* y, int64_t ld_y, const void* x,
                  int64_t ld_x, const int32_t* adapter_ids, int32_t n, const void* A_pool,
                  int64_t A_stride, const void* B_pool, int64_t B_stride, int32_t n_adapters,
                  int32_t h_in, int32_t h_out, int32_t r, float scale, void* workspace,
                  size_t workspace_bytes) {
-  const PoolArgs p = pool_args(y, ld_y, x, ld_x, nullptr, n, A_pool, A_stride, B_pool, B_stride,
-                               n_adapters, h_in, h_out, r, scale, workspace, workspace_bytes);
+  PoolArgs p = pool_args(y, ld_y, x, ld_x, nullptr, n, A_pool, A_stride, B_pool, B_stride,
+                         n_adapters, h_in, h_out, r, scale, workspace, workspace_bytes);
   PoolIds ids;
   for (int i = 0; i < kPoolMaxN; ++i) ids.id[i] = i < n ? adapter_ids[i] : -1;
+  p.b_delay = b_delay(distinct_ids(adapter_ids, n), n, h_in, r);
   hipError_t e;
   if (dtype == SGMV_F16) {
     e = (r == 16) ? launch_ids<SGMV_F16, 16>(stream, p, ids)
