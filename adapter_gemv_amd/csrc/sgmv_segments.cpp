@@ -1,9 +1,10 @@
 // Host side of libsgmv that needs no GPU: status strings and the segment-metadata
 // builder.  The builder is the "sort the batch by adapter" step of the Punica paper
-// summary (research.elamur.ai, "Interesting ideas", I2): a stable counting sort of
-// the caller's rows by adapter id, so that every adapter's rows form one contiguous
+// summary (research.elamur.ai, "Interesting ideas", I2): a stable sort of the caller's
+// rows by adapter id, so that every adapter's rows form one contiguous
 // segment, followed by the per-segment adapter pointer table that lets one launch
 // gather each segment's own A and B.
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <vector>
@@ -35,27 +36,49 @@ extern "C" int sgmv_build_segments(const int32_t* adapter_ids, int32_t n, int32_
   if (n < 0 || n_adapters <= 0) return SGMV_ERR_SHAPE;
   if (!seg_starts || !n_segments || (n > 0 && (!adapter_ids || !perm || !seg_adapter)))
     return SGMV_ERR_NULL;
-  for (int32_t t = 0; t < n; ++t)
-    if (adapter_ids[t] < 0 || adapter_ids[t] >= n_adapters) return SGMV_ERR_ADAPTER_ID;
 
-  // counts per adapter, then an exclusive prefix sum gives each adapter's first slot
-  std::vector<int32_t> slot(static_cast<size_t>(n_adapters) + 1, 0);
-  for (int32_t t = 0; t < n; ++t) ++slot[adapter_ids[t] + 1];
-  int32_t S = 0, lo = n, hi = 0;
-  for (int32_t a = 0; a < n_adapters; ++a) {
-    const int32_t cnt = slot[a + 1];
-    if (cnt > 0) {
-      seg_starts[S] = slot[a];
-      seg_adapter[S] = a;
-      ++S;
-      if (cnt < lo) lo = cnt;
-      if (cnt > hi) hi = cnt;
-    }
-    slot[a + 1] += slot[a];
+  // Runs of equal ids in caller order (a request's rows are usually contiguous), so that
+  // the work below is per run and per distinct id, not per row or per pool entry.
+  struct Run {
+    int32_t id, row0, len;
+  };
+  std::vector<Run> runs;
+  for (int32_t t = 0; t < n;) {
+    const int32_t a = adapter_ids[t];
+    if (a < 0 || a >= n_adapters) return SGMV_ERR_ADAPTER_ID;
+    int32_t u = t + 1;
+    while (u < n && adapter_ids[u] == a) ++u;
+    runs.push_back({a, t, u - t});
+    t = u;
+  }
+  // one segment per distinct id, in increasing id order
+  std::vector<int32_t> ids(runs.size());
+  for (size_t i = 0; i < runs.size(); ++i) ids[i] = runs[i].id;
+  std::sort(ids.begin(), ids.end());
+  ids.erase(std::unique(ids.begin(), ids.end()), ids.end());
+  const int32_t S = static_cast<int32_t>(ids.size());
+  std::vector<int32_t> seg_of(runs.size()), next(static_cast<size_t>(S) + 1, 0);
+  for (size_t i = 0; i < runs.size(); ++i) {
+    seg_of[i] = static_cast<int32_t>(std::lower_bound(ids.begin(), ids.end(), runs[i].id) - ids.begin());
+    next[seg_of[i] + 1] += runs[i].len;
+  }
+  int32_t lo = n, hi = 0;
+  for (int32_t s = 0; s < S; ++s) {
+    const int32_t cnt = next[s + 1];
+    if (cnt < lo) lo = cnt;
+    if (cnt > hi) hi = cnt;
+    next[s + 1] += next[s];  // next[s] = first sorted position of segment s
+    seg_starts[s] = next[s];
+    seg_adapter[s] = ids[s];
   }
   seg_starts[S] = n;
-  // scatter in caller order: rows of one adapter keep their relative order (stable)
-  for (int32_t t = 0; t < n; ++t) perm[slot[adapter_ids[t]]++] = t;
+  // scatter the runs in caller order: the rows of one adapter keep their relative order
+  // (a stable sort)
+  for (size_t i = 0; i < runs.size(); ++i) {
+    int32_t* dst = perm + next[seg_of[i]];
+    for (int32_t v = 0; v < runs[i].len; ++v) dst[v] = runs[i].row0 + v;
+    next[seg_of[i]] += runs[i].len;
+  }
 
   *n_segments = S;
   if (min_seg_len) *min_seg_len = (n > 0) ? lo : 0;

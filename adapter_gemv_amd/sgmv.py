@@ -55,23 +55,24 @@ class SegmentTable:
 
 
 def sgmv_build_segments(adapter_ids, n_adapters: int) -> SegmentTable:
-    ids = np.ascontiguousarray(np.asarray(adapter_ids), dtype=np.int32)
+    ids = np.ascontiguousarray(adapter_ids, dtype=np.int32)
     n = int(ids.shape[0])
-    perm = np.zeros(n, np.int32)
-    starts = np.zeros(n + 1, np.int32)
-    seg_ad = np.zeros(max(n, 1), np.int32)
-    S, lo, hi = (np.zeros(1, np.int32) for _ in range(3))
-    st = _lib.lib().sgmv_build_segments(_ptr(ids), n, int(n_adapters), _ptr(perm), _ptr(starts),
-                                        _ptr(seg_ad), _ptr(S), _ptr(lo), _ptr(hi))
+    # perm [n] | seg_starts [n+1] | seg_adapter [n] | n_segments, min, max: one buffer, so
+    # that numpy's (slow) ctypes address is taken once
+    buf = np.empty(3 * n + 4, np.int32)
+    a = buf.ctypes.data
+    st = _lib.lib().sgmv_build_segments(_ptr(ids), n, int(n_adapters), a, a + 4 * n,
+                                        a + 4 * (2 * n + 1), a + 4 * (3 * n + 1),
+                                        a + 4 * (3 * n + 2), a + 4 * (3 * n + 3))
     check(st, "sgmv_build_segments")
-    s = int(S[0])
-    return SegmentTable(perm, starts[: s + 1].copy(), seg_ad[:s].copy(), s, int(lo[0]), int(hi[0]))
+    s, lo, hi = (int(v) for v in buf[3 * n + 1:])
+    return SegmentTable(buf[:n], buf[n: n + s + 1], buf[2 * n + 1: 2 * n + 1 + s], s, lo, hi)
 
 
 def sgmv_build_ptr_table(adapter_base, seg_adapter) -> np.ndarray:
-    base = np.ascontiguousarray(np.asarray(adapter_base), dtype=np.uint64)
-    seg_ad = np.ascontiguousarray(np.asarray(seg_adapter), dtype=np.int32)
-    out = np.zeros(max(seg_ad.shape[0], 1), np.uint64)
+    base = np.ascontiguousarray(adapter_base, dtype=np.uint64)
+    seg_ad = np.ascontiguousarray(seg_adapter, dtype=np.int32)
+    out = np.empty(max(seg_ad.shape[0], 1), np.uint64)
     st = _lib.lib().sgmv_build_ptr_table(_ptr(base), int(base.shape[0]), _ptr(seg_ad),
                                          int(seg_ad.shape[0]), _ptr(out))
     check(st, "sgmv_build_ptr_table")

@@ -52,6 +52,12 @@ def _ids_cases():
         ("distinct", rng.permutation(32).astype(np.int32), 32),
         ("sorted", np.repeat(np.arange(4), 512).astype(np.int32), 4),
         ("empty_adapters", rng.choice([0, 7, 63], 100).astype(np.int32), 64),
+        # an adapter's rows in several runs of caller rows, runs of other adapters between
+        ("runs_recurring", np.array([3] * 5 + [1] * 7 + [3] * 4 + [0] * 9 + [1] * 2 + [3],
+                                    np.int32), 4),
+        # a pool far larger than the batch: ids spread over 2^20 entries, in runs
+        ("large_pool", np.repeat(rng.integers(0, 1 << 20, 40), rng.integers(1, 20, 40)).astype(np.int32),
+         1 << 20),
     ]
     for k in range(20):
         P = int(rng.integers(1, 70))
