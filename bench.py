@@ -502,12 +502,12 @@ def load_traffic(workload: str, kernel: str):
                 rec[k.strip()] = v.split()[0] if v.split() else ""
     src = rec.get("kernel_source_sha256_16")
     if src != kernel_source_hash(kernel):
-        return None, (f"{rel} was taken on kernel source {src}, not this build's "
+        return None, (f"{rel} was taken on kernel source {src}, not the current sources' "
                       f"{kernel_source_hash(kernel)} ({', '.join(KERNEL_SRCS_OF[kernel])})")
     return int(float(rec["hbm_bytes_per_call"])), (
         f"from {rel}: FETCH_SIZE + WRITE_SIZE per call from two rocprofv3 --pmc runs, scaled "
-        f"by a plain copy of known size; taken on kernel source {src}, the same as this "
-        f"build; not measured in this run")
+        f"by a plain copy of known size; taken on kernel source {src}, the same as the "
+        f"current sources; not measured in this run")
 
 
 def measure(p, device, steps: int, warmup: int, eager: bool = False, force_table: bool = False,
