@@ -662,10 +662,11 @@ __device__ inline void shrink_item(const PoolArgs& p, const Leader& L, int blk, 
 // (CPL = pool_cpl(R)), whose rows of the stored [h_out, r] B[a] are 16 KB of contiguous
 // memory.  Load instruction u reads 1 KB of it: lane l gets the 8 rank values 8q .. 8q+7
 // of column c0 + u * 64/GC + l / GC, where GC = R / 8 lanes share a column and
-// q = l % GC.  A transpose within each group of GC lanes (DPP) then leaves lane l with
-// every rank value of the columns of the loads u = GC*t + q, t < 16/GC, i.e. columns
-// c0 + 64t + q * 64/GC + l / GC, so that every load of B covers whole cache lines and
-// every y access 64 consecutive columns.  Keying expand items by row spreads an adapter
+// q = l % GC.  A transpose within each group of GC lanes (DPP quad permutations, and a
+// swizzle for the third stage at r = 64) then leaves lane l with every rank value of the
+// columns of the loads u = GC*t + q, t < 16/GC, i.e. columns c0 + 64t + q * 64/GC + l / GC,
+// so that every load of B covers whole cache lines and every y access 64 consecutive
+// columns.  Keying expand items by row spreads an adapter
 // with many rows over as many wavefronts.  The y loads are issued first; the B loads wait
 // `p.b_delay` short sleeps (chosen on the host from the bytes the shrink items fetch), so
 // that A and x, which the partial sums wait for, reach the CUs before B competes with
@@ -723,7 +724,7 @@ __device__ inline void expand_item(const PoolArgs& p, const Leader& L, int r, in
     }
   };
   load_first();
-  // the transpose takes b from here on: after the poll's loads have been issued
+  // the transpose takes bw from here on: after the poll's loads have been issued
 #pragma unroll
   for (int i = 0; i < 4 * NV; ++i) asm volatile("" : "+v"(bw[i])::"memory");
   transpose_stage<GC, 1>(bw, q);
