@@ -504,6 +504,22 @@ def test_host_ids_ragged(torch_cuda, n, h_in, h_out, r):
                   f"host-id ragged n={n} {h_in}x{h_out} r={r}")
 
 
+@pytest.mark.parametrize("path", ["host ids", "device ids"])
+def test_decode_longest_b_delay(torch_cuda, path):
+    """64 tokens on 64 distinct adapters at r = 64, h_in = 4096: the shrink items fetch
+    32.5 MiB, so the expand items' wait before their loads of B is at its cap; a ragged
+    h_out (1032) leaves the last expand item 8 columns."""
+    _say(f"[decode longest B delay] {path}")
+    p = synth.random_problem((94,), n=64, h_in=4096, h_out=1032, r=64, n_adapters=64,
+                             dtype="f16", ids=np.random.default_rng(94).permutation(64).astype(np.int32),
+                             scale=0.5)
+    dp = _upload(p)
+    y = dp.lora_add_host_ids() if path == "host ids" else dp.lora_add_pool()
+    torch_cuda.cuda.synchronize()
+    _assert_close(oracle.decode(_storage(y, "f16"), "f16"), oracle.lora_add_problem(p),
+                  f"longest B delay, {path}")
+
+
 def test_host_ids_graph_replay_and_shared_workspace(torch_cuda):
     """Calls captured with different host ids replay with the ids they were captured with,
     every replay equal to eager; the workspace is shared with the device-id path and left
