@@ -623,6 +623,9 @@ __device__ inline void static_for(F&& f) {
   }
 }
 
+// above this h_in the LDS-staged shrink assigns (chunk, tile) pairs to XCDs chunk-major
+constexpr int kChunkMajorMinK = 16384;
+
 template <int DT, int R, int MT, int D>
 __global__ __launch_bounds__(256) void shrink_lds_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, const uint16_t* const* __restrict__ A_ptrs,
@@ -650,15 +653,28 @@ __global__ __launch_bounds__(256) void shrink_lds_kernel(
     else return b7;
   };
 
+  // Workgroup b runs on XCD b % 8.  With a multiple of 8 chunks, XCD x owns the chunks
+  // kc = x (mod 8) of every tile.  Otherwise, for h_in above kChunkMajorMinK (A of several
+  // MB per adapter), XCD x takes a contiguous eighth of the (chunk, tile) pairs in
+  // chunk-major order, so that its L2 fetches about ks / 8 + 1 chunks of A instead of all
+  // of them; at smaller h_in the pairs go tile-major (chunk-major cost 1-2 % there, for
+  // little A).
   const int b = blockIdx.x;
   int tile, kc;
   if (ks % kXcds == 0) {
     const int m = ks / kXcds, j = b / kXcds;
     tile = j / m;
     kc = b % kXcds + kXcds * (j % m);
-  } else {
+  } else if (h_in <= kChunkMajorMinK) {
     tile = b / ks;
     kc = b % ks;
+  } else {
+    const int tiles = static_cast<int>(gridDim.x) / ks;
+    const int pairs = tiles * ks;
+    const int xcd = b % kXcds, per = pairs / kXcds, rem = pairs % kXcds;
+    const int idx = xcd * per + min(xcd, rem) + b / kXcds;
+    kc = idx / tiles;
+    tile = idx % tiles;
   }
   const int r0 = tile * MT;
   const int r1 = min(n, r0 + MT);
