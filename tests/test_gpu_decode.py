@@ -563,3 +563,29 @@ def test_host_ids_graph_replay_and_shared_workspace(torch_cuda):
     ks = -(-p.h_in // (8192 // 16))
     tail = 8 * ks * 64 * 16 + 256
     assert int(ws[-tail:].view(torch.int32).abs().sum().item()) == 0
+
+
+@pytest.mark.parametrize("path", ["host ids", "device ids"])
+@pytest.mark.parametrize("n,h_out,r", [(40, 1032, 64), (33, 136, 16), (9, 776, 32)])
+def test_decode_padded_rows_keep_their_padding(torch_cuda, path, n, h_out, r):
+    """y rows wider than h_out (ld_y = h_out + 64), with an h_out that leaves the last
+    expand item a partial column range: the columns past h_out hold a sentinel that the
+    call must leave bit for bit, and y itself matches the oracle."""
+    torch = torch_cuda
+    _say(f"[decode padded rows] {path} n={n} h_out={h_out} r={r}")
+    p = synth.random_problem((95, n, h_out, r), n=n, h_in=520, h_out=h_out, r=r, n_adapters=11,
+                             dtype="f16", id_dist="zipf", zipf_s=1.1)
+    dp = _upload(p)
+    pad = 64
+    wide = torch.full((n, h_out + pad), -7.0, dtype=torch.float16, device=dp.x.device)
+    wide[:, :h_out] = dp.y0
+    y = wide[:, :h_out]
+    if path == "host ids":
+        dp.lora_add_host_ids(y=y)
+    else:
+        dp.lora_add_pool(y=y)
+    torch.cuda.synchronize()
+    tail = wide[:, h_out:].cpu().numpy()
+    assert np.all(tail == np.float16(-7.0)), f"{int((tail != np.float16(-7.0)).sum())} padding values changed"
+    _assert_close(oracle.decode(_storage(y, "f16"), "f16"), oracle.lora_add_problem(p),
+                  f"padded rows, {path}")
