@@ -184,4 +184,12 @@ __device__ inline float sum_slices(const float* __restrict__ src, int64_t stride
   return ks > 0 ? ((p[0] + p[1]) + (p[2] + p[3])) + 0.f : 0.f;
 }
 
+// Fourth word of a raw buffer resource on gfx950 (32-bit data format, no swizzle, no
+// stride): offsets are in bytes and accesses at or past num_records are dropped.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+// Cache-policy operand of the buffer-store builtins on gfx950: sc1, a device-scope store,
+// which the L2 writes through instead of keeping the line dirty until the write-back at
+// the kernel's end.
+constexpr int kStoreSc1 = 16;
+
 }  // namespace sgmv_dev
