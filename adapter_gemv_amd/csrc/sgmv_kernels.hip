@@ -883,7 +883,7 @@ __global__ __launch_bounds__(256, (exp_waves_per_simd<R, P, VS>())) void expand_
     uint16_t* __restrict__ y, int64_t ld_y, const float* __restrict__ v, int64_t vslice, int32_t vks,
     const uint16_t* const* __restrict__ B_ptrs, const int32_t* __restrict__ seg_starts,
     int32_t S_host, const int32_t* __restrict__ perm, int32_t n, int32_t h_out, float scale,
-    int32_t tiles, int32_t strips, int32_t xs, const int32_t* __restrict__ meta) {
+    int32_t tiles, int32_t strips, int32_t xs, int32_t ybuf, const int32_t* __restrict__ meta) {
   const int S = meta ? meta[0] : S_host;
   if (meta && meta[2] < kLongMin) return;  // no long segment at all
   using E = Elem<DT>;
@@ -1016,9 +1016,9 @@ __global__ __launch_bounds__(256, (exp_waves_per_simd<R, P, VS>())) void expand_
 
   // y is stored through a raw buffer resource over all of y with sc1 stores, which the L2
   // writes through, so the y lines are not left dirty for the write-back at the kernel's
-  // end (13B prefill calls 3-6 % faster); when y spans 4 GiB or more, past the 32-bit
-  // buffer offsets, the stores are plain global stores
-  const bool ybuf = (static_cast<int64_t>(n - 1) * ld_y + h_out) * 2 < (int64_t(1) << 32);
+  // end (13B prefill calls 3-6 % faster); ybuf (set on the host from the caller's whole
+  // y) is 0 when y spans 4 GiB or more, past the 32-bit buffer offsets, and the stores
+  // are then plain global stores
   const __amdgpu_buffer_rsrc_t yrs =
       __builtin_amdgcn_make_buffer_rsrc(static_cast<void*>(y), static_cast<short>(0), -1, kBufferRsrcWord3);
   int cur = sg;  // the run whose B is in bop
@@ -1205,6 +1205,14 @@ struct Tables {
   // the workspace's flag word, for host tables (kernels flag tables that contradict
   // min_len / max_len)
   int32_t* flag = nullptr;
+  // rows of the caller's y when they are more than n (a rank group's rows, addressed
+  // through perm, lie anywhere in the whole batch's y); 0: n
+  int32_t y_rows = 0;
+  // whether every byte offset into y fits the 32-bit offsets of a buffer resource
+  bool y_fits_buffer(int64_t ld_y, int32_t h_out) const {
+    const int64_t rows = y_rows > 0 ? y_rows : n;
+    return rows > 0 && ((rows - 1) * ld_y + h_out) * 2 < (int64_t(1) << 32);
+  }
   bool use_gemv() const { return meta || min_len < kLongMin; }
   bool use_long() const { return meta || max_len >= kLongMin; }
   // grid of a GEMV kernel with `per` items per segment: one workgroup per item with host
@@ -1326,19 +1334,20 @@ hipError_t launch_expand_tiles(hipStream_t st, uint16_t* y, int64_t ld_y, const 
                         ((strips + xs - 1) / xs);
   if (share * kXcds > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(share * kXcds));
+  const int32_t ybuf = T.y_fits_buffer(ld_y, h_out) ? 1 : 0;
   if (ks > 1) {
     if constexpr (R <= 32) {
       if (ks > kExpandSlices<R, P>) return hipErrorInvalidValue;
       hipLaunchKernelGGL((expand_mfma_kernel<DT, R, kExpandSlices<R, P>, P>), grid, dim3(256), 0, st,
                          y, ld_y, vsrc, slice, ks, T.ptrs, T.seg_starts, T.S, T.perm, T.n, h_out,
-                         scale, tiles, strips, xs, T.meta);
+                         scale, tiles, strips, xs, ybuf, T.meta);
     } else {
       return hipErrorInvalidValue;  // r = 64: reduce_v_kernel runs first
     }
   } else {
     hipLaunchKernelGGL((expand_mfma_kernel<DT, R, 1, P>), grid, dim3(256), 0, st, y, ld_y, vsrc,
                        slice, 1, T.ptrs, T.seg_starts, T.S, T.perm, T.n, h_out, scale, tiles,
-                       strips, xs, T.meta);
+                       strips, xs, ybuf, T.meta);
   }
   return hipGetLastError();
 }
@@ -1913,6 +1922,7 @@ extern "C" int sgmv_lora_add_ranked(hipStream_t stream, int32_t dtype, void* y, 
     Tables T{reinterpret_cast<const uint16_t* const*>(P) + G.seg0, seg_starts + G.starts0,
              perm + G.row0, G.n, G.n_segments, G.min_seg_len, G.max_seg_len, nullptr, true};
     T.flag = static_cast<int32_t*>(workspace);
+    T.y_rows = n;
     return T;
   };
   // The groups touch disjoint rows.  Under graph capture, with room for every group's
