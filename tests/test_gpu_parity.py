@@ -525,3 +525,33 @@ def test_segment_bounds_that_contradict_the_tables_are_flagged(torch_cuda, wrong
         == _lib.ERR_DEVICE
     assert int(f[0]) == _lib.FLAG_SEG_BOUNDS
     assert sgmv.workspace_flags(ws) == 0
+
+
+@pytest.mark.parametrize("path", ["table", "host ids"])
+def test_y_rows_past_4_gib(torch_cuda, path):
+    """y rows 2^27 elements apart, so that the last of 17 rows starts 4 GiB past y's first
+    byte, beyond 32-bit buffer offsets: the MFMA expand of the 16-row segment then writes y
+    with plain global stores, and the decode kernel's per-row buffers each start at their
+    row.  Every row against the oracle; the padding after row 0 keeps its sentinel."""
+    torch = torch_cuda
+    n, h_in, h_out, r = 17, 256, 264, 16
+    _say(f"[y past 4 GiB] {path} n={n} h_out={h_out} ld_y=2^27")
+    ids = np.array([0] * 16 + [1], dtype=np.int32)  # a 16-row segment and a 1-row segment
+    p = synth.random_problem((96,), n=n, h_in=h_in, h_out=h_out, r=r, n_adapters=2, dtype="f16",
+                             ids=ids)
+    dp = _upload(p)
+    wide = torch.empty((n, 1 << 27), dtype=torch.float16, device=dp.x.device)  # 4.25 GiB
+    y = wide[:, :h_out]
+    y.copy_(dp.y0)
+    wide[:, h_out:h_out + 64] = -7.0
+    if path == "table":
+        dp.lora_add(y=y)
+    else:
+        dp.lora_add_host_ids(y=y)
+    torch.cuda.synchronize()
+    pad = wide[:, h_out:h_out + 64].cpu().numpy()
+    got = _y_f64(y, "f16")
+    del wide, y
+    torch.cuda.empty_cache()
+    assert np.all(pad == np.float16(-7.0)), f"{int((pad != np.float16(-7.0)).sum())} padding values changed"
+    _assert_close(got, oracle.lora_add_problem(p), f"y past 4 GiB, {path}")
